@@ -1,0 +1,197 @@
+"""CPU oracle for attention over an NVFP4 KV cache.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check in
+``__graft_entry__`` and by the CPU-baseline leg of ``bench.py``.  The product
+path never imports it.  It wraps ``nvfp4_oracle.c`` (plain C, built with gcc)
+through ctypes and shares no code with the HIP library.
+
+Every function follows the release post of the gzenz/ninfer fork
+(prismix.dev), section "NVFP4 KV cache (from scratch)" and section "YaRN
+context extension"; the C source states, per function, what it computes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "nvfp4_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+HEAD_DIM = 128
+PAGE = 64
+BLOCK_BYTES = 9216
+
+
+def build() -> str:
+    """Compile the oracle with gcc (binary32 steps without contraction)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", LIB + ".tmp", SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32, i64, f64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_float
+        L.orc_e4m3_value.argtypes = [ctypes.c_int]
+        L.orc_e4m3_value.restype = f64
+        L.orc_e4m3_scale_code.argtypes = [f32]
+        L.orc_e4m3_scale_code.restype = ctypes.c_int
+        L.orc_e2m1_value.argtypes = [ctypes.c_int]
+        L.orc_e2m1_value.restype = f64
+        L.orc_e2m1_code.argtypes = [f32, f64]
+        L.orc_e2m1_code.restype = ctypes.c_int
+        L.orc_rope_table.argtypes = [f64, ctypes.c_int, f64, ctypes.c_int, P, P]
+        L.orc_rope_apply.argtypes = [P, ctypes.c_int, P, P]
+        L.orc_hadamard128.argtypes = [P]
+        L.orc_quant_row.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P]
+        L.orc_dequant_row.argtypes = [P, P, P]
+        L.orc_pool_bytes.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+        L.orc_pool_bytes.restype = ctypes.c_size_t
+        L.orc_pool_read_row.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
+                                        ctypes.c_int, P, P]
+        L.orc_append.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, P, P, P, P, P, P]
+        L.orc_decode_attention.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P,
+                                           P, ctypes.c_int, P, f64, P]
+        L.orc_reference_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, P, i32, P, P, P, P, P, f64, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# -- scalar codecs -----------------------------------------------------------
+def e4m3_value(code: int) -> float:
+    return lib().orc_e4m3_value(int(code))
+
+
+def e4m3_scale_code(amax: float) -> int:
+    return lib().orc_e4m3_scale_code(float(np.float32(amax)))
+
+
+def e2m1_value(nibble: int) -> float:
+    return lib().orc_e2m1_value(int(nibble))
+
+
+def e2m1_code(y: float, s: float) -> int:
+    return lib().orc_e2m1_code(float(np.float32(y)), float(s))
+
+
+# -- row operations ----------------------------------------------------------
+def rope_table(theta: float, rotary_dim: int, pos_scale: float, max_pos: int):
+    half = rotary_dim // 2
+    c = np.zeros((max_pos, max(half, 1)), np.float32)
+    s = np.zeros((max_pos, max(half, 1)), np.float32)
+    if half:
+        lib().orc_rope_table(theta, rotary_dim, pos_scale, max_pos, _p(c), _p(s))
+    return c[:, :half].copy(), s[:, :half].copy()
+
+
+def rope_apply(x: np.ndarray, rotary_dim: int, c_row: np.ndarray, s_row: np.ndarray):
+    x = _c(x, np.float32).copy()
+    lib().orc_rope_apply(_p(x), rotary_dim, _p(_c(c_row, np.float32)), _p(_c(s_row, np.float32)))
+    return x
+
+
+def hadamard128(x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float32).copy()
+    assert x.shape == (HEAD_DIM,)
+    lib().orc_hadamard128(_p(x))
+    return x
+
+
+def quant_row(x, rotary_dim=0, c_row=None, s_row=None, hadamard=False):
+    x = _c(x, np.float32)
+    codes = np.zeros(64, np.uint8)
+    scales = np.zeros(8, np.uint8)
+    cr = _c(c_row, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    sr = _c(s_row, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    lib().orc_quant_row(_p(x), rotary_dim, _p(cr), _p(sr), int(bool(hadamard)), _p(codes), _p(scales))
+    return codes, scales
+
+
+def dequant_row(codes, scales) -> np.ndarray:
+    out = np.zeros(HEAD_DIM, np.float64)
+    lib().orc_dequant_row(_p(_c(codes, np.uint8)), _p(_c(scales, np.uint8)), _p(out))
+    return out
+
+
+# -- pool --------------------------------------------------------------------
+def pool_bytes(num_layers: int, num_pages: int, num_kv_heads: int) -> int:
+    return lib().orc_pool_bytes(num_layers, num_pages, num_kv_heads)
+
+
+def pool_read_row(pool, num_pages, hkv, layer, slot, kvh, which):
+    codes = np.zeros(64, np.uint8)
+    scales = np.zeros(8, np.uint8)
+    lib().orc_pool_read_row(_p(pool), num_pages, hkv, layer, int(slot), kvh, which,
+                            _p(codes), _p(scales))
+    return codes, scales
+
+
+def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, positions,
+           cos_tab=None, sin_tab=None):
+    """Quantize and write n_tok tokens into `pool` (a writable uint8 array)."""
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    k = _c(k, np.float32)
+    v = _c(v, np.float32)
+    n_tok = k.shape[0]
+    slots = _c(slots, np.int64)
+    positions = _c(positions, np.int32)
+    ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    lib().orc_append(_p(pool), num_pages, hkv, rotary_dim, int(bool(hadamard)), layer, n_tok,
+                     _p(k), _p(v), _p(slots), _p(positions), _p(ct), _p(st))
+
+
+def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
+                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None):
+    """fp64 attention for every sequence and query head over the pool's bytes."""
+    q = _c(q, np.float32)
+    n_seq, hq, _ = q.shape
+    page_table = _c(page_table, np.int32)
+    out = np.zeros((n_seq, hq, HEAD_DIM), np.float64)
+    ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    lib().orc_decode_attention(_p(_c(pool, np.uint8)), num_pages, hkv, layer, rotary_dim,
+                               int(bool(hadamard)), n_seq, hq, _p(q), _p(_c(q_pos, np.int32)),
+                               _p(ct), _p(st), _p(page_table), page_table.shape[1],
+                               _p(_c(seq_lens, np.int32)), float(sm_scale), _p(out))
+    return out
+
+
+def reference_attention(q, q_pos, k, v, k_pos, rotary_dim, sm_scale, cos_tab=None, sin_tab=None):
+    """fp64 attention on unquantized rows for one sequence: q [hq][128], k/v [T][hkv][128]."""
+    q = _c(q, np.float32)
+    k = _c(k, np.float32)
+    v = _c(v, np.float32)
+    hq = q.shape[0]
+    T, hkv, _ = k.shape
+    out = np.zeros((hq, HEAD_DIM), np.float64)
+    ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
+    lib().orc_reference_attention(hkv, hq, T, rotary_dim, _p(q), int(q_pos), _p(k), _p(v),
+                                  _p(_c(k_pos, np.int32)), _p(ct), _p(st), float(sm_scale), _p(out))
+    return out
