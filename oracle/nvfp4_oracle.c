@@ -97,14 +97,16 @@ double orc_e2m1_value(int nibble)
 /* E2M1 code of element y in a block with scale s (an E4M3 value >= 0): the
  * magnitude whose multiple of s is nearest to |y|, ties to the even code,
  * saturating at 6; the sign bit is the sign bit of y.  A zero scale gives
- * magnitude 0.  Distances |(|y|) - v*s| are exact in double (|y| has 24
- * significant bits, v*s at most 6, and a decision between two neighbours
- * only arises when they are of similar size). */
+ * magnitude 0.  |y| >= 6 s takes the largest magnitude directly (it is the
+ * nearest); below that, the distances |(|y|) - v*s| that can decide are
+ * exact in double (|y| has 24 significant bits and is below 6 s, v*s has at
+ * most 6), and a |y| far below s is nearest to 0 by a wide margin. */
 int orc_e2m1_code(float y, double s)
 {
     int sign = signbit(y) ? 8 : 0;
     double a = fabs((double)y);
     if (s == 0.0) return sign;
+    if (a >= 6.0 * s) return sign | 7;
     int best = 0;
     double bestd = INFINITY;
     for (int c = 0; c < 8; ++c) {

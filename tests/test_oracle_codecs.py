@@ -126,6 +126,11 @@ def test_e2m1_tie_table():
     assert [oracle.e2m1_code(r, 1.0) for r in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] == \
         [0, 2, 2, 4, 4, 6, 6]
     assert oracle.e2m1_code(100.0, 1.0) == 7            # saturates at 6
+    # far beyond the grid every distance to v*s rounds to the same double;
+    # the nearest value is still 6*s
+    assert oracle.e2m1_code(1e35, 448.0) == 7
+    assert oracle.e2m1_code(-3e38, 2.0 ** -9) == 15
+    assert oracle.e2m1_code(6.0 * 448.0, 448.0) == 7
     assert oracle.e2m1_code(1.0, 0.0) == 0              # zero scale gives magnitude 0
     assert oracle.e2m1_code(-1.0, 0.0) == 8
     assert oracle.e2m1_code(-0.0, 1.0) == 8             # sign bit kept on zero
