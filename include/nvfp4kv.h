@@ -1,0 +1,169 @@
+/*
+ * nvfp4kv.h -- attention over a 4-bit NVFP4 KV cache on AMD Instinct MI355X
+ * (gfx950).  C ABI of libnvfp4kv.so.
+ *
+ * The method is the one described in the release post of the gzenz/ninfer
+ * fork (prismix.dev, news item 833001997676), section "NVFP4 KV cache (from
+ * scratch)":
+ *   - K and V are stored as NVFP4: 4-bit E2M1 elements, one E4M3 scale per
+ *     16 elements, scales kept row-major without swizzle (bullets 1 and 4);
+ *   - K and Q are rotated by a 128-point Hadamard transform before they are
+ *     quantized, V is not rotated (bullet 2);
+ *   - Q is quantized to NVFP4 as well; V is dequantized for the PV product
+ *     (bullet 1);
+ *   - the current token's K and V are quantized in place during decode,
+ *     without a separate quantization pass (bullet 3);
+ *   - 144 bytes per token per KV head (the "Result" line).
+ * RoPE follows section "YaRN context extension" of the same post: rotary on a
+ * leading part of the head (a quarter of it in the post's model), theta 1e7,
+ * longer contexts by linear scaling of the position.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *     owns every buffer (pool, inputs, outputs, workspace) and keeps it alive
+ *     until the work queued on `stream` has finished.  The library never
+ *     allocates or frees device memory, never synchronizes, and keeps no
+ *     device state.
+ *   - All work is queued on `stream` in call order.  Append a token before
+ *     the decode that must see it, on the same stream.
+ *   - Arguments are checked on the host before anything is queued.  A bad
+ *     argument returns a negative nvfp4kv_status and leaves a message for
+ *     nvfp4kv_last_error(); nothing is queued then.  Device-side contents
+ *     (slots, page ids, positions, sequence lengths) are trusted: values
+ *     outside the documented ranges give undefined results.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef NVFP4KV_H
+#define NVFP4KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NVFP4KV_OK = 0,
+    NVFP4KV_ERR_INVALID_ARG = -1, /* null pointer, size or index out of range */
+    NVFP4KV_ERR_UNSUPPORTED = -2, /* head_dim != 128, page_size != 64, ... */
+    NVFP4KV_ERR_WORKSPACE = -3,   /* workspace too small or misaligned */
+    NVFP4KV_ERR_HIP = -4          /* the HIP runtime reported an error */
+} nvfp4kv_status;
+
+typedef enum { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1 } nvfp4kv_dtype;
+
+/* Byte layout of the pool (device memory, caller-owned, 256-byte aligned).
+ * One block of 9216 bytes per (layer, page, kv head), blocks ordered
+ * [layer][page][kv_head].  A slot is page * 64 + t with t the token's place
+ * in its page.  Code byte j of a row holds elements 2j (low nibble) and 2j+1
+ * (high nibble).  Inside a block:
+ *   [   0, 4096) K codes, byte j of token t at (t/16)*1024 + (j/16)*256 + (t%16)*16 + j%16
+ *   [4096, 8192) V codes, byte j of token t at 4096 + (t/4)*256 + (j/4)*16 + (t%4)*4 + j%4
+ *   [8192, 8704) K scales, row-major: scale of block b (elements 16b..16b+15) of token t at 8192 + 8t + b
+ *   [8704, 9216) V scales, row-major: at 8704 + 8t + b
+ * The code tiling puts the 16 bytes that one lane of a 16x16x32 matrix
+ * instruction needs next to each other; the scales stay row-major as the
+ * release post specifies.  K rows are stored rotated (Hadamard domain). */
+typedef struct {
+    void* base;             /* device pointer to the pool */
+    int64_t num_pages;      /* pages per layer; page ids index [0, num_pages) */
+    int32_t num_layers;     /* >= 1 */
+    int32_t num_kv_heads;   /* >= 1 */
+    int32_t head_dim;       /* must be 128 */
+    int32_t page_size;      /* must be 64 */
+    int32_t rotary_dim;     /* RoPE dims at the head's start: 0..128, a multiple of 16 */
+    int32_t hadamard;       /* 1: rotate K and Q before quantizing; 0: do not */
+} nvfp4kv_pool;
+
+/* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144.
+ * Returns 0 if `p` is null or its sizes are invalid. */
+size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p);
+
+/* RoPE table on the HOST (section "YaRN context extension"): for position
+ * pos < max_pos and pair i < rotary_dim/2,
+ *   angle = (pos / pos_scale) * theta^(-(2 i)/rotary_dim)
+ * evaluated in double, cos and sin rounded once to float, written to host
+ * arrays cos_out/sin_out laid out [max_pos][rotary_dim/2].  pos_scale is the
+ * linear position-scaling factor (1 = none).  Copy the table to the device
+ * and pass it to nvfp4kv_append and nvfp4kv_decode_attn. */
+int nvfp4kv_rope_table(double theta, int32_t rotary_dim, double pos_scale, int32_t max_pos,
+                       float* cos_out, float* sin_out);
+
+/* Append n_tok tokens to one layer of the pool (bullets 1-4 of the NVFP4
+ * section): K rows get RoPE at positions[i], then the Hadamard rotation if
+ * the pool's `hadamard` is 1; V rows get neither.  Each row is quantized to
+ * NVFP4 (E4M3 scale nearest amax/6 per 16 elements, E2M1 codes rounded to
+ * nearest even) and written to slot slots[i], overwriting what was there.
+ *   k, v       [n_tok][num_kv_heads][128], dtype in_dtype (bf16 or f32)
+ *   slots      [n_tok] int64, page * 64 + offset, page < num_pages
+ *   positions  [n_tok] int32, < max_pos (read only when rotary_dim > 0)
+ *   rope_cos/rope_sin [max_pos][rotary_dim/2] float (may be null when
+ *              rotary_dim == 0)
+ * Two tokens with the same slot in one call race. */
+int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok,
+                   const void* k, const void* v, nvfp4kv_dtype in_dtype,
+                   const int64_t* slots, const int32_t* positions,
+                   const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                   hipStream_t stream);
+
+/* Workspace bytes nvfp4kv_decode_attn needs for this shape (split-K
+ * partials).  pages_per_split 0 selects the library's own split plan; the
+ * same value must be passed to nvfp4kv_decode_attn.  Returns 0 on invalid
+ * arguments. */
+size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
+                                      int64_t max_seq_len, int32_t pages_per_split);
+
+/* One decode step of attention for n_seq sequences (bullets 1-3 of the NVFP4
+ * section).  For sequence n and query head h (kv head h / (n_q_heads /
+ * num_kv_heads)): the query gets RoPE at q_positions[n] and the Hadamard
+ * rotation (when the pool has it), is quantized to NVFP4 and dequantized;
+ * scores against the dequantized cached K of tokens 0 .. seq_lens[n]-1 are
+ * scaled by sm_scale, softmax-normalized, and weight the dequantized V.
+ * Split-K: each (sequence, kv head, page range) is one work item writing
+ * partial results to the workspace; a second kernel combines them.
+ *   q           [n_seq][n_q_heads][128], dtype q_dtype, before RoPE
+ *   q_positions [n_seq] int32
+ *   page_table  [n_seq][page_table_stride] int32 page ids; token t of
+ *               sequence n sits in slot page_table[n][t/64]*64 + t%64
+ *   seq_lens    [n_seq] int32, 1 <= seq_lens[n] <= max_seq_len, counting the
+ *               token appended in this step
+ *   max_seq_len host value, sizes the grid
+ *   sm_scale    >= 0 (1/sqrt(128) for plain attention)
+ *   out         [n_seq][n_q_heads][128] float
+ *   workspace   at least nvfp4kv_decode_workspace_bytes(...) bytes, 256-byte
+ *               aligned; its contents on entry do not matter
+ *   pages_per_split 0 = automatic, else 1..4096
+ * n_q_heads / num_kv_heads must be an integer from 1 to 16. */
+int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
+                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                        const int32_t* page_table, int32_t page_table_stride,
+                        const int32_t* seq_lens, int64_t max_seq_len, float sm_scale,
+                        float* out, void* workspace, size_t workspace_bytes,
+                        int32_t pages_per_split, hipStream_t stream);
+
+/* Dequantize cached rows (element = E2M1 value * E4M3 scale, exact in f32 and
+ * bf16).  K comes back in the rotated domain unless `unrotate` is 1, which
+ * applies the Hadamard transform once more (it is its own inverse; the
+ * result then carries float rounding).
+ *   slots       [n_tok] int64
+ *   k_out/v_out [n_tok][num_kv_heads][128] of out_dtype; either may be null */
+int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const int64_t* slots,
+                    void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
+                    hipStream_t stream);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call on the same thread. */
+const char* nvfp4kv_last_error(void);
+
+/* Library version string, e.g. "nvfp4kv 0.1.0 gfx950". */
+const char* nvfp4kv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4KV_H */

@@ -1,0 +1,225 @@
+"""Python binding of libnvfp4kv (attention over an NVFP4 KV cache on MI355X).
+
+Argument marshalling only: every step of append, decode attention and
+dequantization runs in the HIP kernels of ``libnvfp4kv.so``.  PyTorch supplies
+device memory and the stream.  The functions carry the names of the C entry
+points declared in ``include/nvfp4kv.h`` and take torch tensors in place of
+pointers.  There is no CPU fallback: if the library cannot be loaded, import
+fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+HEAD_DIM, PAGE_SIZE, BLOCK_BYTES = 128, 64, 9216
+
+
+class NVFP4KVError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class _PoolDesc(ctypes.Structure):
+    _fields_ = [
+        ("base", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("rotary_dim", ctypes.c_int32),
+        ("hadamard", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_quantized_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    PD = ctypes.POINTER(_PoolDesc)
+    L.nvfp4kv_pool_bytes.argtypes = [PD]
+    L.nvfp4kv_pool_bytes.restype = sz
+    L.nvfp4kv_rope_table.argtypes = [ctypes.c_double, i32, ctypes.c_double, i32, P, P]
+    L.nvfp4kv_rope_table.restype = ctypes.c_int
+    L.nvfp4kv_append.argtypes = [PD, i32, i32, P, P, ctypes.c_int, P, P, P, P, i32, P]
+    L.nvfp4kv_append.restype = ctypes.c_int
+    L.nvfp4kv_decode_workspace_bytes.argtypes = [PD, i32, i32, i64, i32]
+    L.nvfp4kv_decode_workspace_bytes.restype = sz
+    L.nvfp4kv_decode_attn.argtypes = [PD, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P, i32, P,
+                                      i64, ctypes.c_float, P, P, sz, i32, P]
+    L.nvfp4kv_decode_attn.restype = ctypes.c_int
+    L.nvfp4kv_dequant.argtypes = [PD, i32, i32, P, P, P, ctypes.c_int, i32, P]
+    L.nvfp4kv_dequant.restype = ctypes.c_int
+    L.nvfp4kv_last_error.argtypes = []
+    L.nvfp4kv_last_error.restype = ctypes.c_char_p
+    L.nvfp4kv_version.argtypes = []
+    L.nvfp4kv_version.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
+            "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_dequant",
+            "nvfp4kv_last_error", "nvfp4kv_version"]
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != OK:
+        raise NVFP4KVError(fn, rc, _lib.nvfp4kv_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+@dataclass
+class Pool:
+    """A paged NVFP4 KV pool: one uint8 device tensor plus its descriptor."""
+    data: torch.Tensor          # uint8, nvfp4kv_pool_bytes(...) bytes
+    num_pages: int
+    num_layers: int
+    num_kv_heads: int
+    rotary_dim: int = 0
+    hadamard: bool = True
+
+    @classmethod
+    def allocate(cls, num_pages: int, num_layers: int, num_kv_heads: int, rotary_dim: int = 0,
+                 hadamard: bool = True, device="cuda") -> "Pool":
+        desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE,
+                         rotary_dim, int(hadamard))
+        nbytes = _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
+        if nbytes == 0:
+            raise ValueError("invalid pool shape")
+        data = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, hadamard)
+
+    def desc(self) -> _PoolDesc:
+        return _PoolDesc(self.data.data_ptr(), self.num_pages, self.num_layers, self.num_kv_heads,
+                         HEAD_DIM, PAGE_SIZE, self.rotary_dim, int(self.hadamard))
+
+
+def nvfp4kv_version() -> str:
+    return _lib.nvfp4kv_version().decode()
+
+
+def nvfp4kv_last_error() -> str:
+    return _lib.nvfp4kv_last_error().decode()
+
+
+def nvfp4kv_pool_bytes(num_pages: int, num_layers: int, num_kv_heads: int) -> int:
+    desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE, 0, 1)
+    return _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
+
+
+def nvfp4kv_rope_table(theta: float, rotary_dim: int, pos_scale: float, max_pos: int):
+    """Host RoPE table (cos, sin), each a float32 CPU tensor [max_pos][rotary_dim/2]."""
+    half = rotary_dim // 2
+    c = torch.empty((max_pos, half), dtype=torch.float32)
+    s = torch.empty((max_pos, half), dtype=torch.float32)
+    _check("nvfp4kv_rope_table",
+           _lib.nvfp4kv_rope_table(float(theta), int(rotary_dim), float(pos_scale), int(max_pos),
+                                   c.data_ptr(), s.data_ptr()))
+    return c, s
+
+
+def nvfp4kv_append(pool: Pool, layer: int, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor,
+                   positions: torch.Tensor | None = None, rope_cos: torch.Tensor | None = None,
+                   rope_sin: torch.Tensor | None = None, stream=None) -> None:
+    """Quantize k, v [n_tok][Hkv][128] into `slots` (int64) of `layer`."""
+    assert k.is_contiguous() and v.is_contiguous() and k.dtype == v.dtype and k.shape == v.shape
+    assert slots.dtype == torch.int64 and slots.is_contiguous()
+    assert positions is None or (positions.dtype == torch.int32 and positions.is_contiguous())
+    n_tok = k.shape[0]
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    d = pool.desc()
+    _check("nvfp4kv_append",
+           _lib.nvfp4kv_append(ctypes.byref(d), layer, n_tok, _ptr(k), _ptr(v), _dtype_code(k),
+                               _ptr(slots), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), max_pos,
+                               _stream(stream)))
+
+
+def nvfp4kv_decode_workspace_bytes(pool: Pool, n_seq: int, n_q_heads: int, max_seq_len: int,
+                                   pages_per_split: int = 0) -> int:
+    d = pool.desc()
+    return _lib.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), n_seq, n_q_heads, max_seq_len,
+                                               pages_per_split)
+
+
+def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: torch.Tensor | None,
+                        page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                        sm_scale: float, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, rope_cos: torch.Tensor | None = None,
+                        rope_sin: torch.Tensor | None = None, pages_per_split: int = 0,
+                        stream=None) -> torch.Tensor:
+    """Decode attention; q [n_seq][Hq][128] -> out [n_seq][Hq][128] float32."""
+    assert q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    n_seq, n_q_heads, _ = q.shape
+    if out is None:
+        out = torch.empty((n_seq, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = nvfp4kv_decode_workspace_bytes(pool, n_seq, n_q_heads, max_seq_len, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    d = pool.desc()
+    _check("nvfp4kv_decode_attn",
+           _lib.nvfp4kv_decode_attn(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q), _dtype_code(q),
+                                    _ptr(q_positions), _ptr(rope_cos), _ptr(rope_sin), max_pos,
+                                    _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                    int(max_seq_len), float(sm_scale), _ptr(out), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), pages_per_split,
+                                    _stream(stream)))
+    return out
+
+
+def nvfp4kv_dequant(pool: Pool, layer: int, slots: torch.Tensor, out_dtype=torch.float32,
+                    unrotate: bool = False, want_k: bool = True, want_v: bool = True, stream=None):
+    """Dequantized K-hat, V-hat [n_tok][Hkv][128] of the given slots."""
+    assert slots.dtype == torch.int64 and slots.is_contiguous()
+    n_tok = slots.shape[0]
+    shape = (n_tok, pool.num_kv_heads, HEAD_DIM)
+    k_out = torch.empty(shape, dtype=out_dtype, device=slots.device) if want_k else None
+    v_out = torch.empty(shape, dtype=out_dtype, device=slots.device) if want_v else None
+    code = F32 if out_dtype == torch.float32 else BF16
+    d = pool.desc()
+    _check("nvfp4kv_dequant",
+           _lib.nvfp4kv_dequant(ctypes.byref(d), layer, n_tok, _ptr(slots), _ptr(k_out), _ptr(v_out),
+                                code, int(unrotate), _stream(stream)))
+    return k_out, v_out
+
+
+def default_sm_scale() -> float:
+    return 1.0 / math.sqrt(HEAD_DIM)

@@ -1,0 +1,239 @@
+// C ABI of libnvfp4kv: argument checks, split-K planning and kernel launches.
+// Every check runs on the host before anything is queued; no exception
+// crosses the interface and no device memory is allocated here.
+#include "nvfp4kv.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "nvfp4kv_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Sizes and flags of the descriptor (the base pointer is not looked at).
+int check_pool_shape(const nvfp4kv_pool* p) {
+  if (p == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "pool descriptor is null");
+  if (p->head_dim != 128) return fail(NVFP4KV_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", p->head_dim);
+  if (p->page_size != 64) return fail(NVFP4KV_ERR_UNSUPPORTED, "page_size %d unsupported (only 64)", p->page_size);
+  if (p->num_pages <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_pages must be positive (got %lld)", (long long)p->num_pages);
+  if (p->num_layers <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_layers must be positive (got %d)", p->num_layers);
+  if (p->num_kv_heads <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", p->num_kv_heads);
+  if (p->rotary_dim < 0 || p->rotary_dim > 128 || p->rotary_dim % 16 != 0)
+    return fail(NVFP4KV_ERR_UNSUPPORTED, "rotary_dim %d unsupported (0..128, multiple of 16)", p->rotary_dim);
+  if (p->hadamard != 0 && p->hadamard != 1) return fail(NVFP4KV_ERR_INVALID_ARG, "hadamard must be 0 or 1 (got %d)", p->hadamard);
+  return NVFP4KV_OK;
+}
+
+int check_pool(const nvfp4kv_pool* p) {
+  int rc = check_pool_shape(p);
+  if (rc != NVFP4KV_OK) return rc;
+  if (p->base == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "pool base pointer is null");
+  if (!aligned(p->base, 256)) return fail(NVFP4KV_ERR_INVALID_ARG, "pool base must be 256-byte aligned");
+  return NVFP4KV_OK;
+}
+
+int check_layer(const nvfp4kv_pool* p, int32_t layer) {
+  if (layer < 0 || layer >= p->num_layers)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, p->num_layers);
+  return NVFP4KV_OK;
+}
+
+int check_dtype(nvfp4kv_dtype d, const char* what) {
+  if (d != NVFP4KV_F32 && d != NVFP4KV_BF16) return fail(NVFP4KV_ERR_INVALID_ARG, "%s dtype %d is not F32 or BF16", what, (int)d);
+  return NVFP4KV_OK;
+}
+
+int check_rope(const nvfp4kv_pool* p, const float* c, const float* s, int32_t max_pos) {
+  if (p->rotary_dim == 0) return NVFP4KV_OK;
+  if (c == nullptr || s == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs rope_cos and rope_sin");
+  if (max_pos <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "max_pos must be positive when rotary_dim > 0");
+  return NVFP4KV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(NVFP4KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
+  nvfp4kv::LaunchPool L;
+  L.base = reinterpret_cast<uint8_t*>(p->base);
+  L.num_pages = p->num_pages;
+  L.hkv = p->num_kv_heads;
+  L.rotary_dim = p->rotary_dim;
+  L.hadamard = p->hadamard;
+  return L;
+}
+
+// Split-K plan.  The work items are (sequence, kv head, run of pages); the
+// grid is sized from max_seq_len, items past a sequence's end exit at once.
+// The automatic choice aims at about 2048 non-trivial items (a few waves of
+// one-wavefront workgroups over 256 CUs) and never fewer than 2 pages per item.
+int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t max_seq_len,
+              int32_t pages_per_split, nvfp4kv::DecodePlan* out) {
+  if (n_seq <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+  if (n_q_heads <= 0 || n_q_heads % p->num_kv_heads != 0)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of num_kv_heads %d", n_q_heads, p->num_kv_heads);
+  const int group = n_q_heads / p->num_kv_heads;
+  if (group > 16) return fail(NVFP4KV_ERR_UNSUPPORTED, "%d query heads per kv head unsupported (at most 16)", group);
+  if (max_seq_len <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "max_seq_len must be positive");
+  const int64_t max_pages = (max_seq_len + 63) / 64;
+  if (max_pages > ((int64_t)1 << 30)) return fail(NVFP4KV_ERR_INVALID_ARG, "max_seq_len too large");
+  if (pages_per_split < 0 || pages_per_split > 4096)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "pages_per_split %d out of range (0 = automatic, else 1..4096)", pages_per_split);
+  int pps = pages_per_split;
+  if (pps == 0) {
+    const int64_t total = (int64_t)n_seq * p->num_kv_heads * max_pages;
+    int64_t want = (total + 2047) / 2048;
+    pps = (int)std::min<int64_t>(std::max<int64_t>(want, 2), 512);
+  }
+  const int64_t n_splits = (max_pages + pps - 1) / pps;
+  if (n_splits > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "too many splits (%lld); raise pages_per_split", (long long)n_splits);
+  if ((int64_t)n_seq > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "n_seq %d too large (at most 65535)", n_seq);
+  out->pages_per_split = pps;
+  out->n_splits = (int)n_splits;
+  out->group = group;
+  return NVFP4KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p) {
+  if (p == nullptr || p->num_pages <= 0 || p->num_layers <= 0 || p->num_kv_heads <= 0 ||
+      p->head_dim != 128 || p->page_size != 64)
+    return 0;
+  return (size_t)p->num_layers * (size_t)p->num_pages * (size_t)p->num_kv_heads * (size_t)nvfp4kv::kPoolBlockBytes;
+}
+
+int nvfp4kv_rope_table(double theta, int32_t rotary_dim, double pos_scale, int32_t max_pos,
+                       float* cos_out, float* sin_out) {
+  g_last_error.clear();
+  if (cos_out == nullptr || sin_out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null output table");
+  if (rotary_dim <= 0 || rotary_dim > 128 || rotary_dim % 2 != 0) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim %d invalid", rotary_dim);
+  if (max_pos <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "max_pos must be positive");
+  if (!(theta > 0.0) || !(pos_scale > 0.0)) return fail(NVFP4KV_ERR_INVALID_ARG, "theta and pos_scale must be positive");
+  const int half = rotary_dim / 2;
+  for (int32_t pos = 0; pos < max_pos; ++pos) {
+    for (int i = 0; i < half; ++i) {
+      const double inv = pow(theta, -(2.0 * i) / (double)rotary_dim);
+      const double ang = ((double)pos / pos_scale) * inv;
+      cos_out[(size_t)pos * half + i] = (float)cos(ang);
+      sin_out[(size_t)pos * half + i] = (float)sin(ang);
+    }
+  }
+  return NVFP4KV_OK;
+}
+
+int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const void* k,
+                   const void* v, nvfp4kv_dtype in_dtype, const int64_t* slots,
+                   const int32_t* positions, const float* rope_cos, const float* rope_sin,
+                   int32_t max_pos, hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
+  if ((rc = check_dtype(in_dtype, "input")) != NVFP4KV_OK) return rc;
+  if (n_tok < 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_tok must not be negative (got %d)", n_tok);
+  if (n_tok == 0) return NVFP4KV_OK;
+  if ((int64_t)n_tok * p->num_kv_heads * 2 > (int64_t)1 << 30) return fail(NVFP4KV_ERR_UNSUPPORTED, "too many rows in one append");
+  if (k == nullptr || v == nullptr || slots == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null k, v or slots");
+  if (!aligned(k, 16) || !aligned(v, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (p->rotary_dim > 0 && positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs positions");
+  if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
+  hipError_t e = nvfp4kv::launch_append(launch_pool(p), layer, n_tok, k, v, (int)in_dtype, slots,
+                                        positions, rope_cos, rope_sin, stream);
+  if (e != hipSuccess) return hip_fail(e, "kv_quant_append launch");
+  return NVFP4KV_OK;
+}
+
+size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
+                                      int64_t max_seq_len, int32_t pages_per_split) {
+  g_last_error.clear();
+  if (check_pool_shape(p) != NVFP4KV_OK) return 0;
+  nvfp4kv::DecodePlan plan;
+  if (make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan) != NVFP4KV_OK) return 0;
+  return nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+}
+
+int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
+                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                        const int32_t* page_table, int32_t page_table_stride,
+                        const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, float* out,
+                        void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
+  if ((rc = check_dtype(q_dtype, "query")) != NVFP4KV_OK) return rc;
+  nvfp4kv::DecodePlan plan;
+  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan)) != NVFP4KV_OK) return rc;
+  if (q == nullptr || out == nullptr || page_table == nullptr || seq_lens == nullptr)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "null q, out, page_table or seq_lens");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (p->rotary_dim > 0 && q_positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs q_positions");
+  if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
+  const int64_t max_pages = (max_seq_len + 63) / 64;
+  if (page_table_stride < max_pages)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride %d smaller than the %lld pages of max_seq_len", page_table_stride, (long long)max_pages);
+  if (!(sm_scale >= 0.0f) || !isfinite(sm_scale)) return fail(NVFP4KV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  const size_t need = nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NVFP4KV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(NVFP4KV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipError_t e = nvfp4kv::launch_decode(launch_pool(p), layer, n_seq, n_q_heads, q, (int)q_dtype,
+                                        q_positions, rope_cos, rope_sin, page_table,
+                                        page_table_stride, seq_lens, sm_scale, out, workspace, plan,
+                                        stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_attn launch");
+  return NVFP4KV_OK;
+}
+
+int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const int64_t* slots,
+                    void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
+                    hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
+  if ((rc = check_dtype(out_dtype, "output")) != NVFP4KV_OK) return rc;
+  if (n_tok < 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_tok must not be negative (got %d)", n_tok);
+  if (n_tok == 0) return NVFP4KV_OK;
+  if ((int64_t)n_tok * p->num_kv_heads * 2 > (int64_t)1 << 30) return fail(NVFP4KV_ERR_UNSUPPORTED, "too many rows in one dequant");
+  if (slots == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null slots");
+  if (k_out == nullptr && v_out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "k_out and v_out are both null");
+  if ((k_out && !aligned(k_out, 16)) || (v_out && !aligned(v_out, 16)))
+    return fail(NVFP4KV_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  if (unrotate != 0 && unrotate != 1) return fail(NVFP4KV_ERR_INVALID_ARG, "unrotate must be 0 or 1");
+  hipError_t e = nvfp4kv::launch_dequant(launch_pool(p), layer, n_tok, slots, k_out, v_out,
+                                         (int)out_dtype, unrotate, stream);
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return NVFP4KV_OK;
+}
+
+const char* nvfp4kv_last_error(void) { return g_last_error.c_str(); }
+
+const char* nvfp4kv_version(void) { return "nvfp4kv 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// Device-side NVFP4 codec for gfx950: RoPE, 128-point Hadamard rotation and
+// E4M3/E2M1 quantization of one 128-element row held by 16 lanes of a
+// wavefront (8 consecutive elements per lane).
+//
+// Method: release post of the gzenz/ninfer fork (prismix.dev), section
+// "NVFP4 KV cache (from scratch)", bullets 1-2 (E2M1 values with E4M3 block
+// scales; Hadamard rotation of K and Q before quantization) and section
+// "YaRN context extension" (rotary part of the head, theta, linear scaling).
+//
+// The floating-point steps that decide codes are written so that every
+// operation is one IEEE binary32 operation in a fixed order, with contraction
+// into fused multiply-adds switched off: RoPE products and sums rounded one by
+// one, the fast Walsh-Hadamard transform in ascending strides 1..64 with
+// (a, b) -> (a + b, a - b), then one multiply by the float nearest 1/sqrt(128).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4kv {
+
+constexpr int kHeadDim = 128;
+constexpr int kPageSize = 64;
+constexpr int kBlockBytes = 9216;   // one (layer, page, kv head) block
+constexpr int kKCodeOff = 0;
+constexpr int kVCodeOff = 4096;
+constexpr int kKScaleOff = 8192;
+constexpr int kVScaleOff = 8704;
+
+// Byte offset, inside a block, of the 4-byte word holding code bytes
+// 4w .. 4w+3 of token t (w = 0..15).
+__host__ __device__ inline uint32_t k_code_word_off(uint32_t t, uint32_t w) {
+  return kKCodeOff + (t / 16) * 1024 + (w / 4) * 256 + (t % 16) * 16 + (w % 4) * 4;
+}
+__host__ __device__ inline uint32_t v_code_word_off(uint32_t t, uint32_t w) {
+  return kVCodeOff + (t / 4) * 256 + w * 16 + (t % 4) * 4;
+}
+
+// E4M3 code of the scale for a block with largest magnitude `amax`: the E4M3
+// value nearest amax/6, ties to the even code, 448 (0x7E) on overflow.
+// fl32(amax/6) rounds to the same E4M3 value as the exact quotient: the
+// E4M3 decision points have at most 5 significant bits, so the quotient can
+// only sit on one when amax = 6 * point exactly, in which case the division
+// is exact too.
+__host__ __device__ inline uint32_t e4m3_scale_code(float amax) {
+  const float x = amax / 6.0f;               // correctly rounded division
+  if (!(x < 448.0f)) return 0x7Eu;           // also catches x == 448
+  if (x < 0.015625f) {                       // below 2^-6: steps of 2^-9
+    const float m = rintf(x * 512.0f);       // exact scaling, round half even
+    return (uint32_t)m;                      // 0..8; 8 is 2^-6 (code 0x08)
+  }
+  uint32_t bits = __float_as_uint(x);
+  // keep 3 mantissa bits, round to nearest even; a carry moves the exponent
+  bits = bits + 0x7FFFFu + ((bits >> 20) & 1u);
+  bits &= 0xFFF00000u;
+  const uint32_t e = (bits >> 23) & 0xFFu;   // biased fp32 exponent, >= 121
+  const uint32_t m = (bits >> 20) & 7u;
+  return ((e - 120u) << 3) | m;              // E4M3 bias 7 = 127 - 120
+}
+
+// E4M3 code -> float (exact).  Codes are never NaN here.
+__host__ __device__ inline float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;      // m * 2^-9
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude code of |y| for block scale s, nearest with ties to the even
+// code: the products t*s below are exact in binary32 (t has at most 3
+// significant bits, s at most 4), so each comparison is exact.
+__host__ __device__ inline uint32_t e2m1_code(float y, float s) {
+  const float a = fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) +
+               (uint32_t)(a > 1.25f * s) + (uint32_t)(a >= 1.75f * s) +
+               (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) + (uint32_t)(a > 5.0f * s);
+  if (s == 0.0f) c = 0;
+  return c | (signbit(y) ? 8u : 0u);
+}
+
+__host__ __device__ inline float e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7u;
+  // 0, .5, 1, 1.5, 2, 3, 4, 6
+  const float mag = (m < 2) ? 0.5f * (float)m : (float)((2u + (m & 1u)) << ((m >> 1) - 1u)) * 0.5f;
+  return (nib & 8u) ? -mag : mag;
+}
+
+// Quantize one 128-element row held by the 16 lanes of a lane group.  `x`
+// holds elements 8r .. 8r+7 of the row, r = lane % 16.  On return `x` holds
+// the rotated (RoPE'd, Hadamard'd) floats, `codes` the lane's 8 E2M1 codes
+// (element 8r+k in bits 4k..4k+3) and `scode` the E4M3 code of the lane's
+// block (elements 16(r/2) .. 16(r/2)+15).  All 64 lanes of the wavefront must
+// call it together (it uses cross-lane shuffles).
+__device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
+                                   const float* sin_row, bool hadamard, uint32_t& codes,
+                                   uint32_t& scode) {
+#pragma clang fp contract(off)
+  const int lane = (int)__lane_id();
+  // RoPE, rotate-half pairs (i, i + R/2) on the first R dims.
+  if (rotary_dim > 0) {
+    const int half = rotary_dim / 2;          // a multiple of 8
+    const int hl = half / 8;                  // lanes per half
+    const bool first = r < hl;
+    const bool second = (r >= hl) && (r < 2 * hl);
+    const int src = first ? r + hl : (second ? r - hl : r);
+    const int src_lane = (lane & ~15) + src;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float other = __shfl(x[k], src_lane, 64);
+      if (first) {
+        const int i = 8 * r + k;
+        const float c = cos_row[i], s = sin_row[i];
+        const float ac = x[k] * c;
+        const float bs = other * s;
+        x[k] = ac - bs;
+      } else if (second) {
+        const int i = 8 * r + k - half;
+        const float c = cos_row[i], s = sin_row[i];
+        const float bc = x[k] * c;
+        const float as = other * s;
+        x[k] = bc + as;
+      }
+    }
+  }
+  if (hadamard) {
+    // strides 1, 2, 4 inside the lane
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k & h) continue;
+        const float a = x[k], b = x[k + h];
+        x[k] = a + b;
+        x[k + h] = a - b;
+      }
+    }
+    // strides 8, 16, 32, 64 across lanes r ^ 1, r ^ 2, r ^ 4, r ^ 8
+#pragma unroll
+    for (int bit = 1; bit < 16; bit <<= 1) {
+      const bool upper = (r & bit) != 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float p = __shfl_xor(x[k], bit, 64);
+        x[k] = upper ? (p - x[k]) : (x[k] + p);
+      }
+    }
+    const float inv_sqrt128 = __uint_as_float(0x3DB504F3u);  // nearest float to 2^-3.5
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = x[k] * inv_sqrt128;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
+  am = fmaxf(am, __shfl_xor(am, 1, 64));
+  scode = e4m3_scale_code(am);
+  const float s = e4m3_value(scode);
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= e2m1_code(x[k], s) << (4 * k);
+  codes = w;
+}
+
+}  // namespace nvfp4kv

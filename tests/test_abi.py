@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/nvfp4kv.h declares, and rejects bad arguments on the host with the
+documented status codes before anything touches a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kv():
+    from nvfp4_quantized_kv_amd import build as B
+    if B.stale():
+        B.build()
+    import nvfp4_quantized_kv_amd as kv
+    return kv
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "nvfp4kv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4kv_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for must in ("nvfp4kv_append", "nvfp4kv_decode_attn", "nvfp4kv_dequant", "nvfp4kv_pool_bytes",
+                 "nvfp4kv_decode_workspace_bytes", "nvfp4kv_last_error"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(kv):
+    lib = ctypes.CDLL(kv.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) <= set(kv.EXPORTED)
+    assert "gfx950" in kv.nvfp4kv_version()
+
+
+def _desc(kv, **over):
+    d = dict(base=256, num_pages=10, num_layers=2, num_kv_heads=4, head_dim=128, page_size=64,
+             rotary_dim=32, hadamard=1)
+    d.update(over)
+    return kv._PoolDesc(d["base"], d["num_pages"], d["num_layers"], d["num_kv_heads"], d["head_dim"],
+                        d["page_size"], d["rotary_dim"], d["hadamard"])
+
+
+def test_pool_bytes_is_144_per_token_per_kv_head(kv):
+    d = _desc(kv)
+    assert kv.lib().nvfp4kv_pool_bytes(ctypes.byref(d)) == 2 * 10 * 4 * 64 * 144
+    assert kv.lib().nvfp4kv_pool_bytes(None) == 0
+    assert kv.lib().nvfp4kv_pool_bytes(ctypes.byref(_desc(kv, head_dim=64))) == 0
+
+
+def test_rope_table_matches_oracle_bitwise(kv):
+    import oracle
+    for scale in (1.0, 2.3):
+        c, s = kv.nvfp4kv_rope_table(1e7, 32, scale, 5000)
+        oc, os_ = oracle.rope_table(1e7, 32, scale, 5000)
+        assert (c.numpy() == oc).all() and (s.numpy() == os_).all()
+
+
+def _append(kv, d, layer=0, n_tok=4, k=4096, v=4096, dtype=1, slots=4096, pos=4096, c=4096, s=4096,
+            max_pos=10):
+    return kv.lib().nvfp4kv_append(ctypes.byref(d) if d is not None else None, layer, n_tok, k, v,
+                                   dtype, slots, pos, c, s, max_pos, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(rotary_dim=24), -2),
+    (dict(rotary_dim=-16), -2), (dict(hadamard=2), -1), (dict(num_pages=0), -1),
+    (dict(num_kv_heads=0), -1), (dict(base=0), -1), (dict(base=4100), -1)])
+def test_append_rejects_bad_pool(kv, over, code):
+    assert _append(kv, _desc(kv, **over)) == code
+    assert kv.nvfp4kv_last_error() != ""
+
+
+def test_append_rejects_bad_arguments(kv):
+    d = _desc(kv)
+    assert _append(kv, None) == -1
+    assert _append(kv, d, layer=2) == -1
+    assert _append(kv, d, layer=-1) == -1
+    assert _append(kv, d, n_tok=-1) == -1
+    assert _append(kv, d, k=None) == -1
+    assert _append(kv, d, slots=None) == -1
+    assert _append(kv, d, k=4100) == -1               # misaligned
+    assert _append(kv, d, dtype=7) == -1
+    assert _append(kv, d, c=None) == -1               # rotary needs the table
+    assert _append(kv, d, pos=None) == -1
+    assert _append(kv, d, max_pos=0) == -1
+    assert "max_pos" in kv.nvfp4kv_last_error()
+    assert _append(kv, d, n_tok=0) == 0               # nothing to do is not an error
+
+
+def _decode(kv, d, n_seq=2, hq=24, q=4096, pt=4096, stride=100, lens=4096, max_len=6000,
+            scale=0.1, out=4096, ws=4096, ws_bytes=1 << 30, pps=0, qpos=4096):
+    return kv.lib().nvfp4kv_decode_attn(ctypes.byref(d), 0, n_seq, hq, q, 1, qpos, 4096, 4096, 10,
+                                        pt, stride, lens, max_len, scale, out, ws, ws_bytes, pps, None)
+
+
+def test_decode_rejects_bad_arguments(kv):
+    d = _desc(kv)
+    assert _decode(kv, d, hq=25) == -1                # not a multiple of the kv heads
+    assert _decode(kv, d, hq=4 * 17) == -2            # more than 16 query heads per kv head
+    assert _decode(kv, d, n_seq=0) == -1
+    assert _decode(kv, d, max_len=0) == -1
+    assert _decode(kv, d, stride=10) == -1            # table narrower than max_seq_len's pages
+    assert _decode(kv, d, scale=-1.0) == -1
+    assert _decode(kv, d, scale=float("nan")) == -1
+    assert _decode(kv, d, q=None) == -1
+    assert _decode(kv, d, qpos=None) == -1
+    assert _decode(kv, d, pps=5000) == -1
+    assert _decode(kv, d, ws_bytes=16) == -3
+    assert _decode(kv, d, ws=None) == -3
+    assert _decode(kv, d, ws=4100) == -3
+    assert "workspace" in kv.nvfp4kv_last_error()
+
+
+def test_workspace_size_query(kv):
+    d = _desc(kv)
+    L = kv.lib()
+    a = L.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 3, 24, 470001, 0)
+    b = L.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 3, 24, 470001, 64)
+    assert a > 0 and b > 0
+    splits = (470001 + 63) // 64 // 64 + 1
+    assert b >= 3 * 4 * splits * 6 * 130 * 4 - 3 * 4 * 6 * 130 * 4
+    assert L.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 3, 25, 1000, 0) == 0
+
+
+def test_dequant_rejects_bad_arguments(kv):
+    d = _desc(kv)
+    L = kv.lib()
+    assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 4, None, 4096, 4096, 0, 0, None) == -1
+    assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 4, 4096, None, None, 0, 0, None) == -1
+    assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 4, 4096, 4096, 4096, 0, 3, None) == -1
+    assert L.nvfp4kv_dequant(ctypes.byref(d), 5, 4, 4096, 4096, 4096, 0, 0, None) == -1
+    assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 0, 4096, 4096, 4096, 0, 0, None) == 0

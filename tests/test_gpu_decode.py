@@ -1,0 +1,171 @@
+"""GPU parity of nvfp4kv_decode_attn against the CPU oracle.
+
+The oracle computes fp64 attention on the GPU's own pool bytes (the same
+dequantized cache) with its own query quantization.  Bar: every element
+within 2e-3 absolute or 1e-2 relative, and relative L2 error at most 1e-2.
+
+Method: release post of the gzenz/ninfer fork, section "NVFP4 KV cache (from
+scratch)", bullets 1-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ABS_TOL, REL_TOL = 2e-3, 1e-2
+
+
+def assert_attention_close(gpu, ref, what=""):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(gpu).all(), what
+    err = np.abs(gpu - ref)
+    ok = (err <= ABS_TOL) | (err <= REL_TOL * np.abs(ref))
+    if not ok.all():
+        i = np.unravel_index(np.argmax(np.where(ok, 0, err)), err.shape)
+        raise AssertionError(f"{what}: {np.count_nonzero(~ok)} elements out of tolerance, worst at {i}: "
+                             f"gpu {gpu[i]} oracle {ref[i]} (max abs err {err.max():.3g})")
+    rel = np.linalg.norm(gpu - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= REL_TOL, f"{what}: relative L2 error {rel}"
+
+
+class Case:
+    """A small paged cache filled on the GPU, plus queries."""
+
+    def __init__(self, seed, lens, hkv, hq, rotary=32, hadamard=True, pos_scale=1.0,
+                 dtype=torch.bfloat16, outliers=3, outlier_scale=16.0, extra_pages=3,
+                 student_t=False):
+        import nvfp4_quantized_kv_amd as kv
+        self.kv = kv
+        rng = np.random.default_rng(seed)
+        self.lens = list(lens)
+        self.hkv, self.hq, self.rotary, self.hadamard = hkv, hq, rotary, hadamard
+        pages = [(t + 63) // 64 for t in lens]
+        self.num_pages = sum(pages) + extra_pages
+        perm = rng.permutation(self.num_pages).astype(np.int32)
+        width = max(pages)
+        self.table = np.zeros((len(lens), width), np.int32)
+        at = 0
+        for n, p in enumerate(pages):
+            self.table[n, :p] = perm[at:at + p]
+            at += p
+        mult = np.ones(128, np.float32)
+        if outliers:
+            mult[rng.choice(128, outliers, replace=False)] = outlier_scale
+
+        def draw(*shape):
+            x = rng.standard_normal(shape)
+            if student_t:
+                x = x / np.sqrt((rng.standard_normal((3,) + shape) ** 2).sum(0) / 3)
+            x = (x * mult).astype(np.float32)
+            return torch.from_numpy(x).to(dtype)
+
+        self.max_pos = max(lens) + 1
+        self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard)
+        self.pool.data.fill_(0x7F)  # stale bytes decode to NaN if ever read unmasked
+        self.rc = self.rs = self.oc = self.os = None
+        if rotary:
+            c, s = kv.nvfp4kv_rope_table(1e7, rotary, pos_scale, self.max_pos)
+            self.rc, self.rs = c.cuda(), s.cuda()
+            self.oc, self.os = oracle.rope_table(1e7, rotary, pos_scale, self.max_pos)
+        self.k, self.v = [], []
+        for n, T in enumerate(lens):
+            k, v = draw(T, hkv, 128), draw(T, hkv, 128)
+            self.k.append(k)
+            self.v.append(v)
+            pos = np.arange(T)
+            sl = self.table[n, pos // 64].astype(np.int64) * 64 + pos % 64
+            kv.nvfp4kv_append(self.pool, 0, k.cuda(), v.cuda(), torch.from_numpy(sl).cuda(),
+                              torch.from_numpy(pos.astype(np.int32)).cuda(), self.rc, self.rs)
+        self.q = draw(len(lens), hq, 128)
+        self.q_pos = np.array([T - 1 for T in lens], np.int32)
+
+    def gpu(self, pages_per_split=0, sm_scale=1 / np.sqrt(128)):
+        out = self.kv.nvfp4kv_decode_attn(
+            self.pool, 0, self.q.cuda(), torch.from_numpy(self.q_pos).cuda(),
+            torch.from_numpy(self.table).cuda(), torch.tensor(self.lens, dtype=torch.int32).cuda(),
+            max(self.lens), sm_scale, rope_cos=self.rc, rope_sin=self.rs,
+            pages_per_split=pages_per_split)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle(self, sm_scale=1 / np.sqrt(128)):
+        pool = self.pool.data.cpu().numpy()
+        return oracle.decode_attention(pool, self.num_pages, self.hkv, 0, self.rotary, self.hadamard,
+                                       self.q.float().numpy(), self.q_pos, self.table, self.lens,
+                                       sm_scale, self.oc, self.os)
+
+
+def test_decode_tiny_workload():
+    """1 sequence, 1 kv head, 2 query heads, 256 cached + 1 appended token,
+    fp32 N(0,1) with 4 outlier channels x20, no RoPE, Hadamard on."""
+    c = Case(1, [257], 1, 2, rotary=0, dtype=torch.float32, outliers=4, outlier_scale=20.0)
+    assert_attention_close(c.gpu(), c.oracle(), "tiny")
+
+
+def test_decode_layer8k_workload():
+    """1 sequence of 8192 + 1 tokens, 24 query / 4 kv heads, bf16 with 3
+    outlier channels x16, RoPE on 32 dims."""
+    c = Case(2, [8193], 4, 24)
+    assert_attention_close(c.gpu(), c.oracle(), "layer8k")
+
+
+@pytest.mark.parametrize("lens", [[1], [2], [63], [64], [65], [127, 128, 129], [1000, 3, 2049, 777]])
+def test_decode_ragged_lengths(lens):
+    c = Case(sum(lens), lens, 2, 12)
+    assert_attention_close(c.gpu(), c.oracle(), str(lens))
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 6, 8, 16])
+def test_decode_group_sizes(group):
+    c = Case(100 + group, [700, 1500], 2, 2 * group, rotary=16)
+    assert_attention_close(c.gpu(), c.oracle(), f"group {group}")
+
+
+@pytest.mark.parametrize("hadamard,rotary,pos_scale", [(False, 32, 2.3), (True, 32, 2.3), (True, 0, 1.0),
+                                                        (True, 128, 1.0), (False, 0, 1.0)])
+def test_decode_flags(hadamard, rotary, pos_scale):
+    c = Case(7, [3000, 1234], 4, 24, rotary=rotary, hadamard=hadamard, pos_scale=pos_scale,
+             outlier_scale=32.0)
+    assert_attention_close(c.gpu(), c.oracle(), f"hadamard={hadamard} rotary={rotary}")
+
+
+def test_decode_heavy_tailed_f32_inputs():
+    c = Case(8, [4096, 5000, 300], 4, 24, dtype=torch.float32, student_t=True, outliers=0)
+    assert_attention_close(c.gpu(), c.oracle(), "student-t")
+
+
+def test_decode_split_count_invariance():
+    c = Case(9, [5000, 2300], 4, 24)
+    ref = c.oracle()
+    outs = [c.gpu(pages_per_split=p) for p in (1, 2, 3, 7, 64, 4096)]
+    for o in outs:
+        assert_attention_close(o, ref, "split")
+        assert np.abs(o - outs[0]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
+
+
+def test_decode_sm_scale_zero_and_large():
+    c = Case(10, [900], 2, 4)
+    assert_attention_close(c.gpu(sm_scale=0.0), c.oracle(sm_scale=0.0), "sm_scale 0")
+    assert_attention_close(c.gpu(sm_scale=0.5), c.oracle(sm_scale=0.5), "sm_scale 0.5")
+
+
+def test_decode_page_permutation_invariance():
+    a = Case(11, [3000], 2, 8, extra_pages=5)
+    b_out = None
+    # same inputs, different page placement: rebuild with a shifted table
+    import nvfp4_quantized_kv_amd as kv
+    pool2 = kv.Pool.allocate(a.num_pages, 1, a.hkv, a.rotary, a.hadamard)
+    table2 = np.roll(a.table, 7, axis=1) % a.num_pages
+    table2[0] = np.random.default_rng(3).permutation(a.num_pages)[:a.table.shape[1]]
+    pos = np.arange(3000)
+    sl = table2[0, pos // 64].astype(np.int64) * 64 + pos % 64
+    kv.nvfp4kv_append(pool2, 0, a.k[0].cuda(), a.v[0].cuda(), torch.from_numpy(sl).cuda(),
+                      torch.from_numpy(pos.astype(np.int32)).cuda(), a.rc, a.rs)
+    b_out = kv.nvfp4kv_decode_attn(pool2, 0, a.q.cuda(), torch.from_numpy(a.q_pos).cuda(),
+                                   torch.from_numpy(table2.astype(np.int32)).cuda(),
+                                   torch.tensor(a.lens, dtype=torch.int32).cuda(), 3000, 1 / np.sqrt(128),
+                                   rope_cos=a.rc, rope_sin=a.rs).cpu().numpy()
+    assert np.abs(a.gpu() - b_out).max() <= 1e-5 * max(1.0, np.abs(b_out).max())
