@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark: NVFP4 decode attention over a paged NVFP4 KV cache on one MI355X.
+
+A step is the whole decode-time path for every layer of the workload: the
+fused append of each sequence's new token (RoPE, Hadamard-128, NVFP4 quantize,
+in-place write), the split-K decode attention kernel and the reduce kernel.
+The default workload is three concurrent sequences of 330K/400K/470K cached
+tokens, 16 layers, 24 query / 4 KV heads, head_dim 128, 64-token pages with a
+randomly permuted page table; all inputs are seeded synthetic data resident in
+HBM before the timed region starts.
+
+Prints one JSON line.  `value` is the algorithmic KV bytes of a step (144
+bytes per cached token per KV head per layer) divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+ALGO_BYTES_PER_TOKEN_HEAD = 144
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="three_long")
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM copy-ceiling measurement")
+    return ap.parse_args()
+
+
+def copy_ceiling_gbps(torch) -> float:
+    """Achieved HBM bandwidth of a plain device copy of 4 GiB (read + write)."""
+    n = 1 << 32
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def traffic_from_profiles(kernel_tag: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source (same hash); else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "nvfp4_quantized_kv_amd", "csrc", rec.get("source", "decode_attn.hip"))
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if h != rec.get("source_sha256"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(step, wl, torch):
+    """Time the CPU oracle on a bounded sample of the same step: layer 0 of
+    the workload, i.e. the append of every sequence's new token and decode
+    attention of every sequence and query head over the layer's cache."""
+    import numpy as np
+    import oracle
+    from nvfp4_quantized_kv_amd import workloads as W
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    torch.cuda.synchronize()
+    layer_bytes = step.pool.data.numel() // wl.layers
+    pool0 = step.pool.data[:layer_bytes].cpu().numpy()       # layer 0 blocks (the layer is first)
+    oc = os_ = None
+    if wl.rotary_dim:
+        oc, os_ = oracle.rope_table(wl.theta, wl.rotary_dim, wl.pos_scale, step.max_pos)
+    k = step.k_new[0].float().cpu().numpy()
+    v = step.v_new[0].float().cpu().numpy()
+    q = step.q[0].float().cpu().numpy()
+    slots = step.new_slots.cpu().numpy()
+    pos = np.array(wl.cached, np.int32)
+    t0 = time.perf_counter()
+    oracle.append(pool0, step.pool.num_pages, wl.hkv, wl.rotary_dim, wl.hadamard, 0, k, v, slots, pos, oc, os_)
+    ref = oracle.decode_attention(pool0, step.pool.num_pages, wl.hkv, 0, wl.rotary_dim, wl.hadamard, q,
+                                  pos, step.table_np, wl.seq_lens, W.sm_scale(), oc, os_)
+    sec = time.perf_counter() - t0
+    nbytes = ALGO_BYTES_PER_TOKEN_HEAD * wl.hkv * sum(wl.seq_lens)
+    # the same layer on the GPU, for a parity figure
+    step.append(0)
+    out = step.decode(0).clone()
+    torch.cuda.synchronize()
+    err = float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max())
+    return {
+        "value": nbytes / sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": f"layer 0 of {wl.layers}: append of {wl.n_seq} new tokens + fp64 decode attention "
+                  f"for {wl.n_seq} sequences x {wl.hq} query heads over {sum(wl.seq_lens)} tokens "
+                  f"({sec:.1f} s)",
+        "seconds": sec,
+    }, err
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("multi-GPU runs are not part of this build (see DESIGN.md for how the path would shard)")
+        sys.exit(2)
+    import torch
+    import nvfp4_quantized_kv_amd as kv
+    from nvfp4_quantized_kv_amd import workloads as W
+    from nvfp4_quantized_kv_amd.runner import DecodeStep
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    wl = W.config(args.workload)
+    log(f"workload {wl.name}: {wl.n_seq} seqs {wl.cached} cached, {wl.layers} layers, "
+        f"hq {wl.hq} hkv {wl.hkv}, {kv.nvfp4kv_version()}")
+    ceiling = None if args.no_ceiling else copy_ceiling_gbps(torch)
+    if ceiling:
+        log(f"plain copy ceiling {ceiling:.0f} GB/s")
+    step = DecodeStep(wl, pages_per_split=args.pages_per_split)
+    t0 = time.perf_counter()
+    for layer in range(wl.layers):
+        step.fill([layer])
+        torch.cuda.synchronize()
+        log(f"filled layer {layer + 1}/{wl.layers} ({time.perf_counter() - t0:.1f} s)")
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * wl.layers)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    i = 0
+    for _ in range(args.steps):
+        for layer in range(wl.layers):
+            step.append(layer)
+            ev[i][0].record(stream)
+            step.decode_splits(layer)
+            ev[i][1].record(stream)
+            step.decode_reduce(layer)
+            i += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_kernel_ms = sum(kern_ms) / len(kern_ms)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, decode kernel avg {avg_kernel_ms * 1e3:.1f} us")
+
+    bytes_per_layer = wl.decode_bytes_per_layer()
+    bytes_per_step = bytes_per_layer * wl.layers
+    value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    tok_heads = sum(wl.seq_lens) * wl.hkv * wl.layers
+    achieved = bytes_per_layer / (avg_kernel_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("decode_attn_splitk", wl.name)
+
+    cpu = None
+    parity_err = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on layer 0")
+        cpu, parity_err = cpu_baseline(step, wl, torch)
+        cpu.pop("seconds", None)
+        log(f"oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads; max |gpu - oracle| = {parity_err:.2e}")
+
+    rec = {
+        "metric": "NVFP4 decode-attn achieved HBM GB/s (% peak) and KV tokens·heads/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: {wl.n_seq} sequences at {'/'.join(str(t) for t in wl.cached)} cached "
+                        f"tokens + 1 appended, {wl.layers} layers, {wl.hq} query / {wl.hkv} KV heads, "
+                        f"head_dim 128, 64-token pages, randomly permuted page table",
+            "n_seq": wl.n_seq, "layers": wl.layers, "q_heads": wl.hq, "kv_heads": wl.hkv,
+            "rotary_dim": wl.rotary_dim, "hadamard": wl.hadamard, "input_dtype": wl.dtype,
+            "step": "per layer: kv_quant_append + decode_attn_splitk + decode_reduce",
+            "pages_per_split": args.pages_per_split or "auto",
+        },
+        "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "kv_token_heads_per_s": round(tok_heads / (ms_per_step * 1e-3), 1),
+        "bytes_per_step": bytes_per_step,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_attn_splitk_kernel",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_kernel_ms * 1e3, 2),
+            "algo_bytes_per_launch": bytes_per_layer,
+        },
+        "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_layer0": parity_err,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

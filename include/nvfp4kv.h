@@ -145,6 +145,32 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                         float* out, void* workspace, size_t workspace_bytes,
                         int32_t pages_per_split, hipStream_t stream);
 
+/* The two stages of nvfp4kv_decode_attn, for callers that combine split
+ * partials themselves (for example across devices) or time the stages apart.
+ * nvfp4kv_decode_attn_splits takes the arguments of nvfp4kv_decode_attn
+ * except `out` and writes only the workspace: for every work item (sequence,
+ * kv head, run of pages_per_split pages) and query head of the group, the
+ * running max m (log2 units of sm_scale * score), the weight sum l and the
+ * weighted V sum acc[128].  Layout, for item = (seq * num_kv_heads + kvh) *
+ * n_splits + split: acc at float offset (item * group + h) * 128, then (at
+ * the next 256-byte boundary after all acc) the pairs (m, l) at float2 index
+ * item * group + h.  Items past a sequence's last page are not written.
+ * nvfp4kv_decode_reduce reads them and writes out = sum_s 2^(m_s - M) acc_s
+ * / sum_s 2^(m_s - M) l_s per (sequence, query head).  Both must get the
+ * same n_seq, n_q_heads, max_seq_len and pages_per_split. */
+int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
+                               int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                               const int32_t* q_positions, const float* rope_cos,
+                               const float* rope_sin, int32_t max_pos, const int32_t* page_table,
+                               int32_t page_table_stride, const int32_t* seq_lens,
+                               int64_t max_seq_len, float sm_scale, void* workspace,
+                               size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
+
+int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
+                          const int32_t* seq_lens, int64_t max_seq_len, float* out,
+                          const void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+                          hipStream_t stream);
+
 /* Dequantize cached rows (element = E2M1 value * E4M3 scale, exact in f32 and
  * bf16).  K comes back in the rotated domain unless `unrotate` is 1, which
  * applies the Hadamard transform once more (it is its own inverse; the

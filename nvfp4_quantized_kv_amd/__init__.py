@@ -60,6 +60,11 @@ def _load():
     L.nvfp4kv_decode_attn.argtypes = [PD, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P, i32, P,
                                       i64, ctypes.c_float, P, P, sz, i32, P]
     L.nvfp4kv_decode_attn.restype = ctypes.c_int
+    L.nvfp4kv_decode_attn_splits.argtypes = [PD, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P,
+                                             i32, P, i64, ctypes.c_float, P, sz, i32, P]
+    L.nvfp4kv_decode_attn_splits.restype = ctypes.c_int
+    L.nvfp4kv_decode_reduce.argtypes = [PD, i32, i32, P, i64, P, P, sz, i32, P]
+    L.nvfp4kv_decode_reduce.restype = ctypes.c_int
     L.nvfp4kv_dequant.argtypes = [PD, i32, i32, P, P, P, ctypes.c_int, i32, P]
     L.nvfp4kv_dequant.restype = ctypes.c_int
     L.nvfp4kv_last_error.argtypes = []
@@ -72,7 +77,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
-            "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_dequant",
+            "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_splits",
+            "nvfp4kv_decode_reduce", "nvfp4kv_dequant",
             "nvfp4kv_last_error", "nvfp4kv_version"]
 
 
@@ -202,6 +208,40 @@ def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: to
                                     int(max_seq_len), float(sm_scale), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), pages_per_split,
                                     _stream(stream)))
+    return out
+
+
+def nvfp4kv_decode_attn_splits(pool: Pool, layer: int, q: torch.Tensor,
+                               q_positions: torch.Tensor | None, page_table: torch.Tensor,
+                               seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                               workspace: torch.Tensor, rope_cos: torch.Tensor | None = None,
+                               rope_sin: torch.Tensor | None = None, pages_per_split: int = 0,
+                               stream=None) -> None:
+    """First stage of decode attention: split partials into `workspace`."""
+    assert q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    n_seq, n_q_heads, _ = q.shape
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    d = pool.desc()
+    _check("nvfp4kv_decode_attn_splits",
+           _lib.nvfp4kv_decode_attn_splits(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q),
+                                           _dtype_code(q), _ptr(q_positions), _ptr(rope_cos),
+                                           _ptr(rope_sin), max_pos, _ptr(page_table),
+                                           page_table.shape[1], _ptr(seq_lens), int(max_seq_len),
+                                           float(sm_scale), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(),
+                                           pages_per_split, _stream(stream)))
+
+
+def nvfp4kv_decode_reduce(pool: Pool, n_seq: int, n_q_heads: int, seq_lens: torch.Tensor,
+                          max_seq_len: int, out: torch.Tensor, workspace: torch.Tensor,
+                          pages_per_split: int = 0, stream=None) -> torch.Tensor:
+    """Second stage: combine the split partials into out [n_seq][n_q_heads][128]."""
+    d = pool.desc()
+    _check("nvfp4kv_decode_reduce",
+           _lib.nvfp4kv_decode_reduce(ctypes.byref(d), n_seq, n_q_heads, _ptr(seq_lens),
+                                      int(max_seq_len), _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), pages_per_split,
+                                      _stream(stream)))
     return out
 
 

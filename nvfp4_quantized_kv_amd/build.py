@@ -21,6 +21,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep packed-fp32 instructions out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-instruction accumulators in VGPRs: the softmax rescales them with
+    # ordinary vector instructions, which cannot address AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

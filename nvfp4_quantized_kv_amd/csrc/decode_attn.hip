@@ -41,20 +41,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
-struct PageRegs {
-  u4 k[4];   // K codes, tile i: token 16i + (lane%16), dims 32*(lane/16) .. +31
-  u4 v[4];   // V codes, load j: token quad 2*(j/2)*4 + (j%2)*4 + lane/16 ... see v_code_word_off
-  u4 s;      // 16 bytes of the page's 1 KB of scales (K then V)
-};
-
-__device__ inline void load_page(PageRegs& r, const u4* __restrict__ blk, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.k[i] = __builtin_nontemporal_load(blk + lane + 64 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(blk + 256 + lane + 64 * i);
-  r.s = __builtin_nontemporal_load(blk + 512 + lane);
-}
-
 __device__ inline h2 bits_h2(uint32_t b) { return __builtin_bit_cast(h2, b); }
 
 __device__ inline h2 fp4x2(uint32_t w, int byte_sel) {
@@ -82,25 +68,159 @@ __device__ inline float sum4lanes(float v) {
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
-__global__ __launch_bounds__(64) void decode_attn_splitk_kernel(
+// QK^T and the online softmax for one 64-token page.  `sk` points at this
+// lane's K scale pair of token c16 (tile stride 128 bytes).  MASKED pages hold
+// fewer than 64 valid tokens: the invalid ones get zero weight (and, in
+// page_pv, a zero V scale), chosen by selects so that stale bytes, which may
+// decode to NaN, never reach the sums.
+template <bool MASKED>
+__device__ __forceinline__ void page_qk_softmax(const u4 (&kc)[4], const uint8_t* __restrict__ sk,
+                                                int nvalid, int g4, const h8 (&qb)[4],
+                                                float c_log2, f4 (&acc)[8], float& m_run,
+                                                float& l_run, float (&P)[4][4]) {
+  // ---- QK^T: S[i] holds tokens 16i + 4*g4 + r for query head c16
+  f4 S[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * i);
+    // f16 bits of (s0 * 2^-8, s1 * 2^-8): an E4M3 byte shifted left by 7 is
+    // the f16 encoding of its value times 2^-8 (both subnormal and normal)
+    const uint32_t both = (__builtin_amdgcn_perm(0u, ku, 0x0c010c00u)) << 7;
+    const h2 sc = bits_h2(both);
+    const h2 sc0 = __builtin_shufflevector(sc, sc, 0, 0), sc1 = __builtin_shufflevector(sc, sc, 1, 1);
+    S[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = kc[i][c];
+      const h2 scl = (c < 2) ? sc0 : sc1;
+      h8 a;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const h2 x = fp4x2(w, b) * scl;
+        a[2 * b] = x[0];
+        a[2 * b + 1] = x[1];
+      }
+      S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], S[i], 0, 0, 0);
+    }
+  }
+
+  // ---- online softmax (log2 domain, weights scaled by 2^15)
+  float smax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (MASKED) {
+        if (16 * i + 4 * g4 + r < nvalid) smax = fmaxf(smax, S[i][r]);
+      } else {
+        smax = fmaxf(smax, S[i][r]);
+      }
+    }
+  smax = max4lanes(smax);
+  const float m_new = fmaxf(m_run, smax * c_log2);
+  if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    m_run = m_new;
+  }
+  const float off = 15.0f - m_run;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
+      if (MASKED && 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
+      P[i][r] = e;
+      l_run += e;
+    }
+}
+
+// PV for one page: O^T[d][h] += V-hat^T[d][t] P^T[t][h] over two chunks of
+// 32 tokens.  `sv` points at this lane's V scale byte of token 4*g4.
+template <bool MASKED>
+__device__ __forceinline__ void page_pv(const u4 (&vc)[4], const uint8_t* __restrict__ sv,
+                                        int nvalid, int g4, const float (&P)[4][4],
+                                        f4 (&acc)[8]) {
+  // ---- PV over two chunks of 32 tokens
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+    h8 bhi, blo;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float pa = P[2 * ch + (s2 >> 1)][(2 * s2) & 3];
+      const float pb = P[2 * ch + (s2 >> 1)][(2 * s2 + 1) & 3];
+      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
+      const float ra = pa - (float)hi[0];     // exact remainders
+      const float rb = pb - (float)hi[1];
+      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+      bhi[2 * s2] = hi[0];
+      bhi[2 * s2 + 1] = hi[1];
+      blo[2 * s2] = lo[0];
+      blo[2 * s2 + 1] = lo[1];
+    }
+    // V words of the 8 tokens of this lane group; token of k-slot s:
+    // s < 4: 32ch + 4*g4 + s, s >= 4: 32ch + 16 + 4*g4 + (s-4)
+    const u4 va = vc[2 * ch], vb = vc[2 * ch + 1];
+    const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+    uint32_t A[4], B[4];
+    h2 svp[4];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      const uint32_t w0 = w[2 * pr], w1 = w[2 * pr + 1];
+      A[pr] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // even dims
+      B[pr] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);                                       // odd dims
+      const int s0 = 2 * pr, s1 = 2 * pr + 1;
+      const int t0 = 32 * ch + (s0 >= 4 ? 16 : 0) + (s0 & 3);   // token offset from 4*g4
+      const int t1 = 32 * ch + (s1 >= 4 ? 16 : 0) + (s1 & 3);
+      uint32_t b0 = sv[8 * t0], b1 = sv[8 * t1];
+      if (MASKED) {
+        if (t0 + 4 * g4 >= nvalid) b0 = 0;   // stale slot: zero value
+        if (t1 + 4 * g4 >= nvalid) b1 = 0;
+      }
+      svp[pr] = bits_h2((b0 | (b1 << 16)) << 7);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      h8 ae, ao;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const h2 e = fp4x2(A[pr], b) * svp[pr];
+        const h2 o = fp4x2(B[pr], b) * svp[pr];
+        ae[2 * pr] = e[0];
+        ae[2 * pr + 1] = e[1];
+        ao[2 * pr] = o[0];
+        ao[2 * pr + 1] = o[1];
+      }
+      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bhi, acc[2 * b], 0, 0, 0);
+      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, blo, acc[2 * b], 0, 0, 0);
+      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bhi, acc[2 * b + 1], 0, 0, 0);
+      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, blo, acc[2 * b + 1], 0, 0, 0);
+    }
+  }
+}
+
+// Pages of sequence `s`.
+__device__ inline int64_t seq_pages(const int32_t* __restrict__ seq_lens, int s) {
+  return (seq_lens[s] + kPageSize - 1) / kPageSize;
+}
+
+// The wave whose range [w*TP/W, (w+1)*TP/W) holds flattened page index x.
+__device__ inline int64_t wave_of(int64_t x, int64_t TP, int64_t W) { return ((x + 1) * W - 1) / TP; }
+
+// One piece of work: pages [p0, p1) of (seq, kvh).  Writes (m, l, acc) for
+// the group's query heads to partial slot `slot`.
+__device__ __forceinline__ void decode_piece(
     const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_q_heads,
     int group, const void* __restrict__ q, int q_dtype, const int32_t* __restrict__ q_positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard, const int32_t* __restrict__ page_table, int pt_stride,
-    const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml, int pages_per_split, int n_splits) {
-  const int split = (int)blockIdx.x, kvh = (int)blockIdx.y, seq = (int)blockIdx.z;
+    int hadamard, const int32_t* __restrict__ page_table, int pt_stride, int T, float c_log2,
+    float* __restrict__ ws_acc, float2* __restrict__ ws_ml, int seq, int kvh, int p0, int p1,
+    size_t slot, _Float16* qhat, u4 (*sc_lds)[64]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4;     // lane group
   const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
-  const int T = seq_lens[seq];
-  const int n_pages_seq = (T + kPageSize - 1) / kPageSize;
-  const int p0 = split * pages_per_split;
-  if (p0 >= n_pages_seq) return;
-  const int p1 = min(p0 + pages_per_split, n_pages_seq);
-
-  __shared__ __attribute__((aligned(16))) _Float16 qhat[16 * kHeadDim];
-  __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
 
   // ---- query prologue: RoPE, Hadamard, NVFP4 round trip, fp16 Q-hat in LDS
   for (int pass = 0; pass < (group + 3) / 4; ++pass) {
@@ -145,13 +265,22 @@ __global__ __launch_bounds__(64) void decode_attn_splitk_kernel(
     qb[c] = (c16 < group) ? *reinterpret_cast<const h8*>(&qhat[c16 * kHeadDim + 32 * g4 + 8 * c]) : z;
   }
 
-  // ---- main loop over the item's pages
+  // ---- main loop over the piece's pages
   const u4* layer_blocks = reinterpret_cast<const u4*>(
       pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes);
   const int32_t* pt = page_table + (size_t)seq * pt_stride;
   const size_t blk_stride = (size_t)hkv * (kBlockBytes / 16);  // in u4 units
-  PageRegs cur, nxt;
-  load_page(cur, layer_blocks + (size_t)pt[p0] * blk_stride + (size_t)kvh * (kBlockBytes / 16), lane);
+  // One page in registers at a time.  The next page's K codes are requested
+  // as soon as QK^T has consumed the current ones, its V codes as soon as PV
+  // has, and its scales right after the current scales went to LDS, so every
+  // load overlaps the rest of the current page.
+  const u4* blk = layer_blocks + (size_t)pt[p0] * blk_stride + (size_t)kvh * (kBlockBytes / 16);
+  u4 kc[4], vc[4], sc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kc[i] = __builtin_nontemporal_load(blk + lane + 64 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vc[i] = __builtin_nontemporal_load(blk + 256 + lane + 64 * i);
+  sc = __builtin_nontemporal_load(blk + 512 + lane);
 
   f4 acc[8];
 #pragma unroll
@@ -159,195 +288,220 @@ __global__ __launch_bounds__(64) void decode_attn_splitk_kernel(
   float m_run = -INFINITY;
   float l_run = 0.0f;
 
+  // lane-invariant LDS byte offsets of this lane's scales inside a staged page
+  const int sk_off = 8 * c16 + 2 * g4;            // K scales of token c16 (+16i), blocks 2g4, 2g4+1
+  const int sv_off = 512 + 32 * g4 + (c16 >> 1);  // V scales of token 4*g4 (+...), block c16/2
   for (int p = p0; p < p1; ++p) {
-    if (p + 1 < p1)
-      load_page(nxt, layer_blocks + (size_t)pt[p + 1] * blk_stride + (size_t)kvh * (kBlockBytes / 16), lane);
+    const bool more = p + 1 < p1;
+    const u4* nblk = layer_blocks + (size_t)pt[more ? p + 1 : p] * blk_stride + (size_t)kvh * (kBlockBytes / 16);
     const int buf = (p - p0) & 1;
-    sc_lds[buf][lane] = cur.s;
+    sc_lds[buf][lane] = sc;
     __syncthreads();
+    if (more) sc = __builtin_nontemporal_load(nblk + 512 + lane);
     const uint8_t* scb = reinterpret_cast<const uint8_t*>(&sc_lds[buf][0]);
     const int nvalid = T - p * kPageSize;  // tokens of this page that exist, >= 1
-
-    // ---- QK^T: S[i] holds tokens 16i + 4*g4 + r for query head c16
-    f4 S[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * i + c16;
-      const uint32_t ku = *reinterpret_cast<const uint16_t*>(scb + t * 8 + 2 * g4);
-      const uint32_t s0 = (ku & 0xFFu) << 7, s1 = (ku >> 8) << 7;  // f16 bits of scale * 2^-8
-      const h2 sc0 = bits_h2(s0 | (s0 << 16)), sc1 = bits_h2(s1 | (s1 << 16));
-      S[i] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w = cur.k[i][c];
-        const h2 sc = (c < 2) ? sc0 : sc1;
-        h8 a;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const h2 x = fp4x2(w, b) * sc;
-          a[2 * b] = x[0];
-          a[2 * b + 1] = x[1];
-        }
-        S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], S[i], 0, 0, 0);
-      }
-    }
-
-    // ---- online softmax (log2 domain, weights scaled by 2^15)
-    float smax = -INFINITY;
-    if (nvalid >= kPageSize) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) smax = fmaxf(smax, S[i][r]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * i + 4 * g4 + r < nvalid) smax = fmaxf(smax, S[i][r]);
-    }
-    smax = max4lanes(smax);
-    const float m_new = fmaxf(m_run, smax * c_log2);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-      m_run = m_new;
-    }
-    const float off = 15.0f - m_run;
     float P[4][4];
+    if (nvalid >= kPageSize)
+      page_qk_softmax<false>(kc, scb + sk_off, nvalid, g4, qb, c_log2, acc, m_run, l_run, P);
+    else
+      page_qk_softmax<true>(kc, scb + sk_off, nvalid, g4, qb, c_log2, acc, m_run, l_run, P);
+    if (more) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float e = exp2f(fmaf(S[i][r], c_log2, off));
-        if (nvalid < kPageSize && 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
-        P[i][r] = e;
-        l_run += e;
-      }
-
-    // ---- PV over two chunks of 32 tokens
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      h8 bhi, blo;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const float pa = P[2 * ch + (s2 >> 1)][(2 * s2) & 3];
-        const float pb = P[2 * ch + (s2 >> 1)][(2 * s2 + 1) & 3];
-        const float ha = __uint_as_float(__float_as_uint(pa) & 0xFFFFE000u);
-        const float hb = __uint_as_float(__float_as_uint(pb) & 0xFFFFE000u);
-        const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(ha, hb));
-        const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - ha, pb - hb));
-        bhi[2 * s2] = hi[0];
-        bhi[2 * s2 + 1] = hi[1];
-        blo[2 * s2] = lo[0];
-        blo[2 * s2 + 1] = lo[1];
-      }
-      // V words of the 8 tokens of this lane group; token of k-slot s:
-      // s < 4: 32ch + 4*g4 + s, s >= 4: 32ch + 16 + 4*g4 + (s-4)
-      const u4 va = cur.v[2 * ch], vb = cur.v[2 * ch + 1];
-      const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-      uint32_t sb[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int t = 32 * ch + (s >= 4 ? 16 : 0) + 4 * g4 + (s & 3);
-        uint32_t b = scb[512 + t * 8 + (c16 >> 1)];
-        if (t >= nvalid) b = 0;  // stale slot: zero weight and zero value
-        sb[s] = b;
-      }
-      uint32_t A[4], B[4];
-      h2 sv[4];
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const uint32_t w0 = w[2 * pr], w1 = w[2 * pr + 1];
-        A[pr] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);          // even dims
-        B[pr] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);          // odd dims
-        sv[pr] = bits_h2((sb[2 * pr] << 7) | (sb[2 * pr + 1] << 23));
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        h8 ae, ao;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const h2 e = fp4x2(A[pr], b) * sv[pr];
-          const h2 o = fp4x2(B[pr], b) * sv[pr];
-          ae[2 * pr] = e[0];
-          ae[2 * pr + 1] = e[1];
-          ao[2 * pr] = o[0];
-          ao[2 * pr + 1] = o[1];
-        }
-        acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bhi, acc[2 * b], 0, 0, 0);
-        acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, blo, acc[2 * b], 0, 0, 0);
-        acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bhi, acc[2 * b + 1], 0, 0, 0);
-        acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, blo, acc[2 * b + 1], 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) kc[i] = __builtin_nontemporal_load(nblk + lane + 64 * i);
     }
-    cur = nxt;
+    if (nvalid >= kPageSize)
+      page_pv<false>(vc, scb + sv_off, nvalid, g4, P, acc);
+    else
+      page_pv<true>(vc, scb + sv_off, nvalid, g4, P, acc);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vc[i] = __builtin_nontemporal_load(nblk + 256 + lane + 64 * i);
+    }
   }
 
-  // ---- partial results of this item
+  // ---- partial results of this piece
   const float l_tot = sum4lanes(l_run);
-  const size_t item = ((size_t)seq * hkv + kvh) * n_splits + split;
   if (c16 < group) {
     // lane holds dims 32*g4 + 8i + j in acc[j][i]
-    float* dst = ws_acc + (item * group + c16) * kHeadDim + 32 * g4;
+    float* dst = ws_acc + (slot * group + c16) * kHeadDim + 32 * g4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       reinterpret_cast<float4*>(dst + 8 * i)[0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
       reinterpret_cast<float4*>(dst + 8 * i)[1] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
     }
-    if (g4 == 0) ws_ml[item * group + c16] = make_float2(m_run, l_tot);
+    if (g4 == 0) ws_ml[slot * group + c16] = make_float2(m_run, l_tot);
+  }
+  __syncthreads();  // the next piece rewrites qhat
+}
+
+// Stream-K decode.  All (sequence, kv head, page) work is laid out flat:
+// segment g = seq * hkv + kvh holds that pair's pages, segments in order.
+// With TP pages in all and W = gridDim.x wavefronts, wave w takes the range
+// [w*TP/W, (w+1)*TP/W), so every wave gets the same number of pages (+-1)
+// whatever the sequence lengths.  A range may start or end inside a segment
+// and may cover several; the wave writes one partial per segment piece, to
+// slot g + w (distinct for every (segment, wave) pair that overlaps).
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_splitk_kernel(
+    const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq,
+    int n_q_heads, int group, const void* __restrict__ q, int q_dtype,
+    const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int rotary_dim, int hadamard,
+    const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens,
+    float c_log2, float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
+  __shared__ __attribute__((aligned(16))) _Float16 qhat[16 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
+
+  const int64_t W = gridDim.x, w = blockIdx.x;
+  int64_t TP = 0;
+  for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
+  TP *= hkv;
+  int64_t x = (w * TP) / W;
+  const int64_t end = ((w + 1) * TP) / W;
+  if (x >= end) return;
+  // find the sequence holding x
+  int seq = 0;
+  int64_t seq_base = 0;  // flat index of the first page of seq's first segment
+  int64_t pg = seq_pages(seq_lens, 0);
+  while (x >= seq_base + hkv * pg) {
+    seq_base += hkv * pg;
+    ++seq;
+    pg = seq_pages(seq_lens, seq);
+  }
+  while (x < end) {
+    const int kvh = (int)((x - seq_base) / pg);
+    const int64_t seg_start = seq_base + kvh * pg;
+    const int p0 = (int)(x - seg_start);
+    const int64_t seg_end = seg_start + pg;
+    const int p1 = (int)((end < seg_end ? end : seg_end) - seg_start);
+    const size_t slot = (size_t)seq * hkv + kvh + (size_t)w;
+    decode_piece(pool, num_pages, hkv, layer, n_q_heads, group, q, q_dtype, q_positions, rope_cos,
+                 rope_sin, rotary_dim, hadamard, page_table, pt_stride, seq_lens[seq], c_log2,
+                 ws_acc, ws_ml, seq, kvh, p0, p1, slot, qhat, sc_lds);
+    x = seg_start + p1;
+    if (kvh == hkv - 1 && x < end) {
+      seq_base += hkv * pg;
+      ++seq;
+      pg = seq_pages(seq_lens, seq);
+    }
   }
 }
 
-// Combine the split partials of one (sequence, query head): 128 threads, one
-// output dim each.
-__global__ __launch_bounds__(128) void decode_reduce_kernel(
+// Combine the partials of one (sequence, query head) for 32 output dims:
+// 256 threads = 32 dims x 8 groups that stride over the pieces.  The pieces
+// of segment g come from waves w_first .. w_last, found with the same flat
+// indexing as the decode kernel; waves with an empty range (more waves than
+// pages) wrote nothing and are skipped.
+__global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
-    const int32_t* __restrict__ seq_lens, int hkv, int group, int n_splits, int pages_per_split,
+    const int32_t* __restrict__ seq_lens, int n_seq, int hkv, int group, int64_t W,
     float* __restrict__ out) {
   const int hq_idx = (int)blockIdx.x;     // query head
   const int seq = (int)blockIdx.y;
-  const int d = (int)threadIdx.x;
+  const int d0 = 32 * (int)blockIdx.z;    // first output dim of this block
+  const int tid = (int)threadIdx.x;
+  const int dd = tid & 31, j = tid >> 5;  // dim within the chunk, piece group
   const int kvh = hq_idx / group, h = hq_idx % group;
-  const int T = seq_lens[seq];
-  const int n_pages_seq = (T + kPageSize - 1) / kPageSize;
-  const int n_valid = (n_pages_seq + pages_per_split - 1) / pages_per_split;
-  const size_t item0 = ((size_t)seq * hkv + kvh) * n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < n_valid; ++s) M = fmaxf(M, ws_ml[(item0 + s) * group + h].x);
-  float L = 0.0f, o = 0.0f;
-  for (int s = 0; s < n_valid; ++s) {
-    const float2 ml = ws_ml[(item0 + s) * group + h];
-    const float w = exp2f(ml.x - M);
-    L += w * ml.y;
-    o += w * ws_acc[((item0 + s) * group + h) * kHeadDim + d];
+  int64_t TP = 0, seq_base = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int64_t pg = seq_pages(seq_lens, s);
+    if (s == seq) seq_base = TP;
+    TP += pg;
   }
-  out[((size_t)seq * hkv * group + hq_idx) * kHeadDim + d] = o / L;
+  TP *= hkv;
+  seq_base *= hkv;
+  const int64_t pg = seq_pages(seq_lens, seq);
+  const int64_t S = seq_base + kvh * pg, E = S + pg;
+  const int64_t w0 = wave_of(S, TP, W), w1 = wave_of(E - 1, TP, W);
+  const size_t g = (size_t)seq * hkv + kvh;
+
+  __shared__ float red_m[8];
+  __shared__ float red_o[8][32];
+  __shared__ float red_l[8];
+  // ---- running max over all pieces
+  float M = -INFINITY;
+  for (int64_t w = w0 + tid; w <= w1; w += 256) {
+    if ((w * TP) / W == ((w + 1) * TP) / W) continue;
+    M = fmaxf(M, ws_ml[(g + w) * group + h].x);
+  }
+  for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+  if ((tid & 31) == 0) red_m[tid >> 5] = M;
+  __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
+
+  // ---- weighted sums; 4 pieces per round keep several loads in flight
+  float L = 0.0f, acc = 0.0f;
+  for (int64_t w = w0 + j; w <= w1; w += 32) {
+    float2 ml[4];
+    float a[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t wu = w + 8 * u;
+      ok[u] = wu <= w1 && (wu * TP) / W != ((wu + 1) * TP) / W;
+      const size_t slot = (g + (ok[u] ? wu : w0)) * group + h;
+      ml[u] = ws_ml[slot];
+      a[u] = ws_acc[slot * kHeadDim + d0 + dd];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (!ok[u]) continue;
+      const float wt = exp2f(ml[u].x - M);
+      L += wt * ml[u].y;
+      acc += wt * a[u];
+    }
+  }
+  red_o[j][dd] = acc;
+  if (dd == 0) red_l[j] = L;
+  __syncthreads();
+  if (j == 0) {
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o += red_o[i][dd];
+      l += red_l[i];
+    }
+    out[((size_t)seq * hkv * group + hq_idx) * kHeadDim + d0 + dd] = o / l;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode(const LaunchPool& P, int layer, int n_seq, int n_q_heads, const void* q,
-                         int q_dtype, const int32_t* q_positions, const float* rope_cos,
-                         const float* rope_sin, const int32_t* page_table, int page_table_stride,
-                         const int32_t* seq_lens, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream) {
+hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
+                                const void* q, int q_dtype, const int32_t* q_positions,
+                                const float* rope_cos, const float* rope_sin,
+                                const int32_t* page_table, int page_table_stride,
+                                const int32_t* seq_lens, float sm_scale, void* workspace,
+                                const DecodePlan& plan, hipStream_t stream) {
   float* ws_acc = reinterpret_cast<float*>(workspace);
-  size_t acc_bytes = (ws_acc_bytes(n_seq, P.hkv, plan) + 255) & ~(size_t)255;
+  const size_t acc_bytes = (ws_acc_bytes(n_seq, P.hkv, plan) + 255) & ~(size_t)255;
   float2* ws_ml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(workspace) + acc_bytes);
   const float c_log2 = sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(decode_attn_splitk_kernel, dim3(plan.n_splits, P.hkv, n_seq), dim3(64), 0,
-                     stream, P.base, P.num_pages, P.hkv, layer, n_q_heads, plan.group, q, q_dtype,
+  hipLaunchKernelGGL(decode_attn_splitk_kernel, dim3(plan.n_waves), dim3(64), 0, stream, P.base,
+                     P.num_pages, P.hkv, layer, n_seq, n_q_heads, plan.group, q, q_dtype,
                      q_positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table,
-                     page_table_stride, seq_lens, c_log2, ws_acc, ws_ml, plan.pages_per_split,
-                     plan.n_splits);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(n_q_heads, n_seq), dim3(128), 0, stream, ws_acc,
-                     ws_ml, seq_lens, P.hkv, plan.group, plan.n_splits, plan.pages_per_split, out);
+                     page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
+                                float* out, const void* workspace, const DecodePlan& plan,
+                                hipStream_t stream) {
+  const float* ws_acc = reinterpret_cast<const float*>(workspace);
+  const size_t acc_bytes = (ws_acc_bytes(n_seq, hkv, plan) + 255) & ~(size_t)255;
+  const float2* ws_ml =
+      reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) + acc_bytes);
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(n_q_heads, n_seq, kHeadDim / 32), dim3(256), 0, stream, ws_acc,
+                     ws_ml, seq_lens, n_seq, hkv, plan.group, (int64_t)plan.n_waves, out);
+  return hipGetLastError();
+}
+
+int decode_waves_per_cu() {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_attn_splitk_kernel, 64, 0) != hipSuccess)
+    return 0;
+  return blocks;
 }
 
 }  // namespace nvfp4kv

@@ -83,13 +83,37 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   return L;
 }
 
-// Split-K plan.  The work items are (sequence, kv head, run of pages); the
-// grid is sized from max_seq_len, items past a sequence's end exit at once.
-// The automatic choice aims at about 2048 non-trivial items (a few waves of
-// one-wavefront workgroups over 256 CUs) and never fewer than 2 pages per item.
+// Resident wavefronts of the decode kernel on the current device: CUs times
+// one-wavefront workgroups per CU.  Cached per device; if the device cannot be
+// queried (no GPU), 256 CUs x 8 is assumed so that size queries still work.
+int resident_decode_waves() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256 * 8;
+  }
+  if (cached[dev] == 0) {
+    int cus = 0;
+    const int per_cu = nvfp4kv::decode_waves_per_cu();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      return 256 * 8;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
+// Split-K plan.  The flattened (sequence, kv head, page) work is shared
+// equally by n_waves one-wavefront workgroups.  pages_per_split 0 launches
+// one wavefront per resident slot of the device; a positive value asks for
+// about that many pages per wavefront at max_seq_len.
 int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t max_seq_len,
               int32_t pages_per_split, nvfp4kv::DecodePlan* out) {
   if (n_seq <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+  if (n_seq > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "n_seq %d too large (at most 65535)", n_seq);
   if (n_q_heads <= 0 || n_q_heads % p->num_kv_heads != 0)
     return fail(NVFP4KV_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of num_kv_heads %d", n_q_heads, p->num_kv_heads);
   const int group = n_q_heads / p->num_kv_heads;
@@ -99,18 +123,24 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   if (max_pages > ((int64_t)1 << 30)) return fail(NVFP4KV_ERR_INVALID_ARG, "max_seq_len too large");
   if (pages_per_split < 0 || pages_per_split > 4096)
     return fail(NVFP4KV_ERR_INVALID_ARG, "pages_per_split %d out of range (0 = automatic, else 1..4096)", pages_per_split);
-  int pps = pages_per_split;
-  if (pps == 0) {
-    const int64_t total = (int64_t)n_seq * p->num_kv_heads * max_pages;
-    int64_t want = (total + 2047) / 2048;
-    pps = (int)std::min<int64_t>(std::max<int64_t>(want, 2), 512);
-  }
-  const int64_t n_splits = (max_pages + pps - 1) / pps;
-  if (n_splits > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "too many splits (%lld); raise pages_per_split", (long long)n_splits);
-  if ((int64_t)n_seq > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "n_seq %d too large (at most 65535)", n_seq);
-  out->pages_per_split = pps;
-  out->n_splits = (int)n_splits;
+  const int64_t max_total = (int64_t)n_seq * p->num_kv_heads * max_pages;
+  int64_t waves;
+  if (pages_per_split == 0)
+    waves = resident_decode_waves();
+  else
+    waves = (max_total + pages_per_split - 1) / pages_per_split;
+  waves = std::max<int64_t>(1, std::min<int64_t>(waves, std::min<int64_t>(max_total, (int64_t)1 << 24)));
+  out->n_waves = (int)waves;
   out->group = group;
+  return NVFP4KV_OK;
+}
+
+int check_workspace(const nvfp4kv_pool* p, int32_t n_seq, const nvfp4kv::DecodePlan& plan,
+                    const void* workspace, size_t workspace_bytes) {
+  const size_t need = nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(NVFP4KV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(NVFP4KV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   return NVFP4KV_OK;
 }
 
@@ -175,6 +205,70 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
   return nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
 }
 
+// Checks shared by the decode entry points; fills `plan`.
+static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
+                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                        const int32_t* page_table, int32_t page_table_stride,
+                        const int32_t* seq_lens, int64_t max_seq_len, float sm_scale,
+                        const void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+                        nvfp4kv::DecodePlan* plan) {
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
+  if ((rc = check_dtype(q_dtype, "query")) != NVFP4KV_OK) return rc;
+  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, plan)) != NVFP4KV_OK) return rc;
+  if (q == nullptr || page_table == nullptr || seq_lens == nullptr)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "null q, page_table or seq_lens");
+  if (!aligned(q, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if (p->rotary_dim > 0 && q_positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs q_positions");
+  if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
+  const int64_t max_pages = (max_seq_len + 63) / 64;
+  if (page_table_stride < max_pages)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride %d smaller than the %lld pages of max_seq_len", page_table_stride, (long long)max_pages);
+  if (!(sm_scale >= 0.0f) || !isfinite(sm_scale)) return fail(NVFP4KV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  return check_workspace(p, n_seq, *plan, workspace, workspace_bytes);
+}
+
+int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
+                               int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                               const int32_t* q_positions, const float* rope_cos,
+                               const float* rope_sin, int32_t max_pos, const int32_t* page_table,
+                               int32_t page_table_stride, const int32_t* seq_lens,
+                               int64_t max_seq_len, float sm_scale, void* workspace,
+                               size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream) {
+  g_last_error.clear();
+  nvfp4kv::DecodePlan plan;
+  int rc = check_decode(p, layer, n_seq, n_q_heads, q, q_dtype, q_positions, rope_cos, rope_sin,
+                        max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
+                        workspace, workspace_bytes, pages_per_split, &plan);
+  if (rc != NVFP4KV_OK) return rc;
+  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q,
+                                               (int)q_dtype, q_positions, rope_cos, rope_sin,
+                                               page_table, page_table_stride, seq_lens, sm_scale,
+                                               workspace, plan, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
+  return NVFP4KV_OK;
+}
+
+int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
+                          const int32_t* seq_lens, int64_t max_seq_len, float* out,
+                          const void* workspace, size_t workspace_bytes, int32_t pages_per_split,
+                          hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool_shape(p)) != NVFP4KV_OK) return rc;
+  nvfp4kv::DecodePlan plan;
+  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan)) != NVFP4KV_OK) return rc;
+  if (seq_lens == nullptr || out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null seq_lens or out");
+  if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  if ((rc = check_workspace(p, n_seq, plan, workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
+  hipError_t e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out,
+                                               workspace, plan, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
+  return NVFP4KV_OK;
+}
+
 int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
                         const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
                         const float* rope_cos, const float* rope_sin, int32_t max_pos,
@@ -183,30 +277,21 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                         void* workspace, size_t workspace_bytes, int32_t pages_per_split,
                         hipStream_t stream) {
   g_last_error.clear();
-  int rc;
-  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
-  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
-  if ((rc = check_dtype(q_dtype, "query")) != NVFP4KV_OK) return rc;
   nvfp4kv::DecodePlan plan;
-  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan)) != NVFP4KV_OK) return rc;
-  if (q == nullptr || out == nullptr || page_table == nullptr || seq_lens == nullptr)
-    return fail(NVFP4KV_ERR_INVALID_ARG, "null q, out, page_table or seq_lens");
-  if (!aligned(q, 16) || !aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (p->rotary_dim > 0 && q_positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs q_positions");
-  if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
-  const int64_t max_pages = (max_seq_len + 63) / 64;
-  if (page_table_stride < max_pages)
-    return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride %d smaller than the %lld pages of max_seq_len", page_table_stride, (long long)max_pages);
-  if (!(sm_scale >= 0.0f) || !isfinite(sm_scale)) return fail(NVFP4KV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
-  const size_t need = nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(NVFP4KV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(NVFP4KV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  hipError_t e = nvfp4kv::launch_decode(launch_pool(p), layer, n_seq, n_q_heads, q, (int)q_dtype,
-                                        q_positions, rope_cos, rope_sin, page_table,
-                                        page_table_stride, seq_lens, sm_scale, out, workspace, plan,
-                                        stream);
-  if (e != hipSuccess) return hip_fail(e, "decode_attn launch");
+  int rc = check_decode(p, layer, n_seq, n_q_heads, q, q_dtype, q_positions, rope_cos, rope_sin,
+                        max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
+                        workspace, workspace_bytes, pages_per_split, &plan);
+  if (rc != NVFP4KV_OK) return rc;
+  if (out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null out");
+  if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q,
+                                               (int)q_dtype, q_positions, rope_cos, rope_sin,
+                                               page_table, page_table_stride, seq_lens, sm_scale,
+                                               workspace, plan, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
+  e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out, workspace,
+                                    plan, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
   return NVFP4KV_OK;
 }
 

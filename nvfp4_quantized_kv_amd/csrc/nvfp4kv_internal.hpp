@@ -17,24 +17,32 @@ struct LaunchPool {
   int hadamard;
 };
 
-// Split-K plan of one decode call.
+// Split-K plan of one decode call: the number of wavefronts that share the
+// flattened (sequence, kv head, page) work equally.
 struct DecodePlan {
-  int pages_per_split;
-  int n_splits;          // splits per (sequence, kv head)
+  int n_waves;
   int group;             // query heads per kv head
 };
 
-// Workspace layout: partial accumulators [item][group][128] floats, then the
-// running (max, sum) pairs [item][group] as float2; item = (seq * hkv + kvh)
-// * n_splits + split.
+// Partial slots: one per (segment, wave) pair that overlaps, indexed segment
+// + wave, so at most n_seq * hkv + n_waves of them.
+inline size_t ws_slots(int n_seq, int hkv, const DecodePlan& pl) {
+  return (size_t)n_seq * hkv + (size_t)pl.n_waves;
+}
+
+// Workspace layout: partial accumulators [slot][group][128] floats, then the
+// running (max, sum) pairs [slot][group] as float2.
 inline size_t ws_acc_bytes(int n_seq, int hkv, const DecodePlan& pl) {
-  return (size_t)n_seq * hkv * pl.n_splits * pl.group * 128 * sizeof(float);
+  return ws_slots(n_seq, hkv, pl) * pl.group * 128 * sizeof(float);
 }
 inline size_t ws_bytes(int n_seq, int hkv, const DecodePlan& pl) {
   size_t a = ws_acc_bytes(n_seq, hkv, pl);
   a = (a + 255) & ~(size_t)255;
-  return a + (size_t)n_seq * hkv * pl.n_splits * pl.group * 2 * sizeof(float);
+  return a + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float);
 }
+
+// Resident one-wavefront decode workgroups per CU (0 if the query fails).
+int decode_waves_per_cu();
 
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,
@@ -43,10 +51,15 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
 hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64_t* slots,
                           void* k_out, void* v_out, int dtype, int unrotate, hipStream_t stream);
 
-hipError_t launch_decode(const LaunchPool& P, int layer, int n_seq, int n_q_heads, const void* q,
-                         int q_dtype, const int32_t* q_positions, const float* rope_cos,
-                         const float* rope_sin, const int32_t* page_table, int page_table_stride,
-                         const int32_t* seq_lens, float sm_scale, float* out, void* workspace,
-                         const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
+                                const void* q, int q_dtype, const int32_t* q_positions,
+                                const float* rope_cos, const float* rope_sin,
+                                const int32_t* page_table, int page_table_stride,
+                                const int32_t* seq_lens, float sm_scale, void* workspace,
+                                const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
+                                float* out, const void* workspace, const DecodePlan& plan,
+                                hipStream_t stream);
 
 }  // namespace nvfp4kv

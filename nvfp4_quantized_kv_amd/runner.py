@@ -7,10 +7,11 @@ in the HIP library.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
-from . import (Pool, nvfp4kv_append, nvfp4kv_decode_attn, nvfp4kv_decode_workspace_bytes,
-               nvfp4kv_rope_table)
+from . import (Pool, nvfp4kv_append, nvfp4kv_decode_attn, nvfp4kv_decode_attn_splits,
+               nvfp4kv_decode_reduce, nvfp4kv_decode_workspace_bytes, nvfp4kv_rope_table)
 from . import workloads as W
 
 
@@ -38,7 +39,7 @@ class DecodeStep:
         n = wl.n_seq
         self.new_pos = torch.tensor(wl.cached, dtype=torch.int32, device=device)
         self.new_slots = torch.from_numpy(
-            __import__("numpy").concatenate([W.slots(table, i, [wl.cached[i]]) for i in range(n)])
+            np.concatenate([W.slots(table, i, [wl.cached[i]]) for i in range(n)])
         ).to(device)
         self.k_new, self.v_new, self.q = [], [], []
         for layer in range(wl.layers):
@@ -82,6 +83,17 @@ class DecodeStep:
                                    out=self.out if out is None else out, workspace=self.workspace,
                                    rope_cos=self.rope_cos, rope_sin=self.rope_sin,
                                    pages_per_split=self.pages_per_split)
+
+    def decode_splits(self, layer: int) -> None:
+        nvfp4kv_decode_attn_splits(self.pool, layer, self.q[layer], self.new_pos, self.table,
+                                   self.seq_lens, self.wl.max_seq_len, W.sm_scale(), self.workspace,
+                                   rope_cos=self.rope_cos, rope_sin=self.rope_sin,
+                                   pages_per_split=self.pages_per_split)
+
+    def decode_reduce(self, layer: int, out=None) -> torch.Tensor:
+        return nvfp4kv_decode_reduce(self.pool, self.wl.n_seq, self.wl.hq, self.seq_lens,
+                                     self.wl.max_seq_len, self.out if out is None else out,
+                                     self.workspace, pages_per_split=self.pages_per_split)
 
     def run(self) -> None:
         for layer in range(self.wl.layers):
