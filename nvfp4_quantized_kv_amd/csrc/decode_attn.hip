@@ -43,6 +43,16 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 __device__ inline h2 bits_h2(uint32_t b) { return __builtin_bit_cast(h2, b); }
 
+// Buffer resource over one 9216-byte pool block (raw buffer, gfx9 format
+// word); loads past the block's end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* blk) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, kBlockBytes, 0x00020000);
+}
+// 16 bytes at block byte offset voff + soff (voff per lane, soff uniform).
+__device__ __forceinline__ u4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+}
+
 __device__ inline h2 fp4x2(uint32_t w, int byte_sel) {
   // two E2M1 values of byte `byte_sel` (low nibble first) times 2^8, exact
   switch (byte_sel) {
@@ -68,30 +78,35 @@ __device__ inline float sum4lanes(float v) {
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
-// QK^T and the online softmax for one 64-token page.  `sk` points at this
-// lane's K scale pair of token c16 (tile stride 128 bytes).  MASKED pages hold
-// fewer than 64 valid tokens: the invalid ones get zero weight (and, in
-// page_pv, a zero V scale), chosen by selects so that stale bytes, which may
+// One 32-token half of a page: QK^T for tiles 2hh, 2hh+1, the online
+// softmax over those 32 tokens, and PV for them.  `k0`/`k1` hold the two K
+// tiles (token 16i + lane%16, dims 32*g4 .. +31), `va`/`vb` the two V token
+// quads of this lane group, `sk` this lane's K scale pair of token c16 in the
+// staged page (tile stride 128 bytes), `sv` its V scale byte of token 4*g4.
+// MASKED halves may hold tokens at or past the sequence end: those get zero
+// weight and a zero V scale, chosen by selects so that stale bytes, which may
 // decode to NaN, never reach the sums.
 template <bool MASKED>
-__device__ __forceinline__ void page_qk_softmax(const u4 (&kc)[4], const uint8_t* __restrict__ sk,
-                                                int nvalid, int g4, const h8 (&qb)[4],
-                                                float c_log2, f4 (&acc)[8], float& m_run,
-                                                float& l_run, float (&P)[4][4]) {
-  // ---- QK^T: S[i] holds tokens 16i + 4*g4 + r for query head c16
-  f4 S[4];
+__device__ __forceinline__ void half_step(u4& k0, u4& k1, u4& va, u4& vb, __amdgpu_buffer_rsrc_t nrs,
+                                          int voff, const uint8_t* __restrict__ sk,
+                                          const uint8_t* __restrict__ sv, int hh, int nvalid,
+                                          int g4, const h8 (&qb)[4], float c_log2, f4 (&acc)[8],
+                                          float& m_run, float& l_run) {
+  // ---- QK^T: S[i] holds tokens 32hh + 16i + 4*g4 + r for query head c16
+  f4 S[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * i);
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * (2 * hh + i));
     // f16 bits of (s0 * 2^-8, s1 * 2^-8): an E4M3 byte shifted left by 7 is
     // the f16 encoding of its value times 2^-8 (both subnormal and normal)
     const uint32_t both = (__builtin_amdgcn_perm(0u, ku, 0x0c010c00u)) << 7;
     const h2 sc = bits_h2(both);
     const h2 sc0 = __builtin_shufflevector(sc, sc, 0, 0), sc1 = __builtin_shufflevector(sc, sc, 1, 1);
+    const u4& kc = i ? k1 : k0;
     S[i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const uint32_t w = kc[i][c];
+      const uint32_t w = kc[c];
       const h2 scl = (c < 2) ? sc0 : sc1;
       h8 a;
 #pragma unroll
@@ -103,15 +118,21 @@ __device__ __forceinline__ void page_qk_softmax(const u4 (&kc)[4], const uint8_t
       S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], S[i], 0, 0, 0);
     }
   }
+  // this half's K registers are free: request the next page's.  The loads
+  // are unconditional (past a piece's end `nrs` is an empty resource) so that
+  // the wait counters stay exact across the loop: a conditional load makes
+  // the compiler drain every outstanding load at the join.
+  k0 = ld16(nrs, voff, 1024 * (2 * hh));
+  k1 = ld16(nrs, voff, 1024 * (2 * hh + 1));
 
   // ---- online softmax (log2 domain, weights scaled by 2^15)
   float smax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (MASKED) {
-        if (16 * i + 4 * g4 + r < nvalid) smax = fmaxf(smax, S[i][r]);
+        if (32 * hh + 16 * i + 4 * g4 + r < nvalid) smax = fmaxf(smax, S[i][r]);
       } else {
         smax = fmaxf(smax, S[i][r]);
       }
@@ -126,79 +147,73 @@ __device__ __forceinline__ void page_qk_softmax(const u4 (&kc)[4], const uint8_t
     m_run = m_new;
   }
   const float off = 15.0f - m_run;
+  float P[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
-      if (MASKED && 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
+      if (MASKED && 32 * hh + 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
       P[i][r] = e;
       l_run += e;
     }
-}
 
-// PV for one page: O^T[d][h] += V-hat^T[d][t] P^T[t][h] over two chunks of
-// 32 tokens.  `sv` points at this lane's V scale byte of token 4*g4.
-template <bool MASKED>
-__device__ __forceinline__ void page_pv(const u4 (&vc)[4], const uint8_t* __restrict__ sv,
-                                        int nvalid, int g4, const float (&P)[4][4],
-                                        f4 (&acc)[8]) {
-  // ---- PV over two chunks of 32 tokens
+  // ---- PV: O^T[d][h] += V-hat^T[d][t] P^T[t][h] over these 32 tokens; the
+  // weights go in as fp16 hi + lo parts (two MFMAs) to keep ~22 bits
+  h8 bhi, blo;
 #pragma unroll
-  for (int ch = 0; ch < 2; ++ch) {
-    h8 bhi, blo;
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const float pa = P[s2 >> 1][(2 * s2) & 3];
+    const float pb = P[s2 >> 1][(2 * s2 + 1) & 3];
+    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
+    const float ra = pa - (float)hi[0];     // exact remainders
+    const float rb = pb - (float)hi[1];
+    const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+    bhi[2 * s2] = hi[0];
+    bhi[2 * s2 + 1] = hi[1];
+    blo[2 * s2] = lo[0];
+    blo[2 * s2 + 1] = lo[1];
+  }
+  // V words of the 8 tokens of this lane group; token of k-slot s:
+  // s < 4: 32hh + 4*g4 + s, s >= 4: 32hh + 16 + 4*g4 + (s-4)
+  const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+  uint32_t A[4], B[4];
+  h2 svp[4];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const float pa = P[2 * ch + (s2 >> 1)][(2 * s2) & 3];
-      const float pb = P[2 * ch + (s2 >> 1)][(2 * s2 + 1) & 3];
-      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
-      const float ra = pa - (float)hi[0];     // exact remainders
-      const float rb = pb - (float)hi[1];
-      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
-      bhi[2 * s2] = hi[0];
-      bhi[2 * s2 + 1] = hi[1];
-      blo[2 * s2] = lo[0];
-      blo[2 * s2 + 1] = lo[1];
+  for (int pr = 0; pr < 4; ++pr) {
+    const uint32_t w0 = w[2 * pr], w1 = w[2 * pr + 1];
+    A[pr] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // even dims
+    B[pr] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);   // odd dims
+    const int s0 = 2 * pr, s1 = 2 * pr + 1;
+    const int t0 = 32 * hh + (s0 >= 4 ? 16 : 0) + (s0 & 3);   // token offset from 4*g4
+    const int t1 = 32 * hh + (s1 >= 4 ? 16 : 0) + (s1 & 3);
+    uint32_t b0 = sv[8 * t0], b1 = sv[8 * t1];
+    if (MASKED) {
+      if (t0 + 4 * g4 >= nvalid) b0 = 0;   // stale slot: zero value
+      if (t1 + 4 * g4 >= nvalid) b1 = 0;
     }
-    // V words of the 8 tokens of this lane group; token of k-slot s:
-    // s < 4: 32ch + 4*g4 + s, s >= 4: 32ch + 16 + 4*g4 + (s-4)
-    const u4 va = vc[2 * ch], vb = vc[2 * ch + 1];
-    const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-    uint32_t A[4], B[4];
-    h2 svp[4];
+    svp[pr] = bits_h2((b0 | (b1 << 16)) << 7);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    h8 ae, ao;
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
-      const uint32_t w0 = w[2 * pr], w1 = w[2 * pr + 1];
-      A[pr] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // even dims
-      B[pr] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);                                       // odd dims
-      const int s0 = 2 * pr, s1 = 2 * pr + 1;
-      const int t0 = 32 * ch + (s0 >= 4 ? 16 : 0) + (s0 & 3);   // token offset from 4*g4
-      const int t1 = 32 * ch + (s1 >= 4 ? 16 : 0) + (s1 & 3);
-      uint32_t b0 = sv[8 * t0], b1 = sv[8 * t1];
-      if (MASKED) {
-        if (t0 + 4 * g4 >= nvalid) b0 = 0;   // stale slot: zero value
-        if (t1 + 4 * g4 >= nvalid) b1 = 0;
-      }
-      svp[pr] = bits_h2((b0 | (b1 << 16)) << 7);
+      const h2 e = fp4x2(A[pr], b) * svp[pr];
+      const h2 o = fp4x2(B[pr], b) * svp[pr];
+      ae[2 * pr] = e[0];
+      ae[2 * pr + 1] = e[1];
+      ao[2 * pr] = o[0];
+      ao[2 * pr + 1] = o[1];
     }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      h8 ae, ao;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const h2 e = fp4x2(A[pr], b) * svp[pr];
-        const h2 o = fp4x2(B[pr], b) * svp[pr];
-        ae[2 * pr] = e[0];
-        ae[2 * pr + 1] = e[1];
-        ao[2 * pr] = o[0];
-        ao[2 * pr + 1] = o[1];
-      }
-      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bhi, acc[2 * b], 0, 0, 0);
-      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, blo, acc[2 * b], 0, 0, 0);
-      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bhi, acc[2 * b + 1], 0, 0, 0);
-      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, blo, acc[2 * b + 1], 0, 0, 0);
-    }
+    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bhi, acc[2 * b], 0, 0, 0);
+    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, blo, acc[2 * b], 0, 0, 0);
+    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bhi, acc[2 * b + 1], 0, 0, 0);
+    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, blo, acc[2 * b + 1], 0, 0, 0);
   }
+  // and the V registers: request the next page's
+  va = ld16(nrs, voff, kVCodeOff + 1024 * (2 * hh));
+  vb = ld16(nrs, voff, kVCodeOff + 1024 * (2 * hh + 1));
 }
 
 // Pages of sequence `s`.
@@ -266,21 +281,31 @@ __device__ __forceinline__ void decode_piece(
   }
 
   // ---- main loop over the piece's pages
-  const u4* layer_blocks = reinterpret_cast<const u4*>(
-      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes);
+  const uint8_t* layer_base =
+      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes;
   const int32_t* pt = page_table + (size_t)seq * pt_stride;
-  const size_t blk_stride = (size_t)hkv * (kBlockBytes / 16);  // in u4 units
-  // One page in registers at a time.  The next page's K codes are requested
-  // as soon as QK^T has consumed the current ones, its V codes as soon as PV
-  // has, and its scales right after the current scales went to LDS, so every
-  // load overlaps the rest of the current page.
-  const u4* blk = layer_blocks + (size_t)pt[p0] * blk_stride + (size_t)kvh * (kBlockBytes / 16);
+  const size_t blk_stride = (size_t)hkv * kBlockBytes;
+  const int voff = 16 * lane;
+  // One page in registers at a time.  Each half-page's K codes are requested
+  // for the next page as soon as QK^T has consumed them, its V codes as soon
+  // as PV has, and the scales right after the current ones went to LDS, so
+  // every load overlaps the rest of the current page.
+  __amdgpu_buffer_rsrc_t rs = block_rsrc(layer_base + (size_t)pt[p0] * blk_stride + (size_t)kvh * kBlockBytes);
+  // Issued in the order the loop issues them (scales, then K and V of each
+  // half), so the wait counts at the loop head are the same on entry and on
+  // the back edge.
   u4 kc[4], vc[4], sc;
+  sc = ld16(rs, voff, kKScaleOff);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kc[i] = __builtin_nontemporal_load(blk + lane + 64 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) vc[i] = __builtin_nontemporal_load(blk + 256 + lane + 64 * i);
-  sc = __builtin_nontemporal_load(blk + 512 + lane);
+  for (int hh = 0; hh < 2; ++hh) {
+    kc[2 * hh] = ld16(rs, voff, 1024 * (2 * hh));
+    kc[2 * hh + 1] = ld16(rs, voff, 1024 * (2 * hh + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    vc[2 * hh] = ld16(rs, voff, kVCodeOff + 1024 * (2 * hh));
+    vc[2 * hh + 1] = ld16(rs, voff, kVCodeOff + 1024 * (2 * hh + 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   f4 acc[8];
 #pragma unroll
@@ -292,30 +317,28 @@ __device__ __forceinline__ void decode_piece(
   const int sk_off = 8 * c16 + 2 * g4;            // K scales of token c16 (+16i), blocks 2g4, 2g4+1
   const int sv_off = 512 + 32 * g4 + (c16 >> 1);  // V scales of token 4*g4 (+...), block c16/2
   for (int p = p0; p < p1; ++p) {
+    // the next page; past the piece's end an empty resource (loads return
+    // zeros without memory traffic) keeps the load sequence unchanged
     const bool more = p + 1 < p1;
-    const u4* nblk = layer_blocks + (size_t)pt[more ? p + 1 : p] * blk_stride + (size_t)kvh * (kBlockBytes / 16);
+    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(layer_base + (size_t)pt[more ? p + 1 : p] * blk_stride + (size_t)kvh * kBlockBytes),
+        0, more ? kBlockBytes : 0, 0x00020000);
     const int buf = (p - p0) & 1;
     sc_lds[buf][lane] = sc;
     __syncthreads();
-    if (more) sc = __builtin_nontemporal_load(nblk + 512 + lane);
+    sc = ld16(nrs, voff, kKScaleOff);
     const uint8_t* scb = reinterpret_cast<const uint8_t*>(&sc_lds[buf][0]);
     const int nvalid = T - p * kPageSize;  // tokens of this page that exist, >= 1
-    float P[4][4];
-    if (nvalid >= kPageSize)
-      page_qk_softmax<false>(kc, scb + sk_off, nvalid, g4, qb, c_log2, acc, m_run, l_run, P);
-    else
-      page_qk_softmax<true>(kc, scb + sk_off, nvalid, g4, qb, c_log2, acc, m_run, l_run, P);
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kc[i] = __builtin_nontemporal_load(nblk + lane + 64 * i);
-    }
-    if (nvalid >= kPageSize)
-      page_pv<false>(vc, scb + sv_off, nvalid, g4, P, acc);
-    else
-      page_pv<true>(vc, scb + sv_off, nvalid, g4, P, acc);
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) vc[i] = __builtin_nontemporal_load(nblk + 256 + lane + 64 * i);
+    for (int hh = 0; hh < 2; ++hh) {
+      // each half's registers are refilled with the next page's data as soon
+      // as this half has consumed them (inside half_step)
+      if (nvalid >= kPageSize)
+        half_step<false>(kc[2 * hh], kc[2 * hh + 1], vc[2 * hh], vc[2 * hh + 1], nrs, voff,
+                         scb + sk_off, scb + sv_off, hh, nvalid, g4, qb, c_log2, acc, m_run, l_run);
+      else
+        half_step<true>(kc[2 * hh], kc[2 * hh + 1], vc[2 * hh], vc[2 * hh + 1], nrs, voff,
+                        scb + sk_off, scb + sv_off, hh, nvalid, g4, qb, c_log2, acc, m_run, l_run);
     }
   }
 
