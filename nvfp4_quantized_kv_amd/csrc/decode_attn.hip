@@ -437,9 +437,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int64_t w0 = wave_of(S, TP, W), w1 = wave_of(E - 1, TP, W);
   const size_t g = (size_t)seq * hkv + kvh;
 
+  constexpr int kChunk = 1024;             // pieces whose weights are staged at once
   __shared__ float red_m[8];
   __shared__ float red_o[8][32];
   __shared__ float red_l[8];
+  __shared__ float wts[kChunk];
   // ---- running max over all pieces
   float M = -INFINITY;
   for (int64_t w = w0 + tid; w <= w1; w += 256) {
@@ -453,28 +455,38 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 #pragma unroll
   for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
 
-  // ---- weighted sums; 4 pieces per round keep several loads in flight
+  // ---- weighted sums, a chunk of pieces at a time: weights 2^(m - M) go to
+  // LDS once, then 8 groups stride over the pieces with 16 independent loads
+  // in flight per thread
   float L = 0.0f, acc = 0.0f;
-  for (int64_t w = w0 + j; w <= w1; w += 32) {
-    float2 ml[4];
-    float a[4];
-    bool ok[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t wu = w + 8 * u;
-      ok[u] = wu <= w1 && (wu * TP) / W != ((wu + 1) * TP) / W;
-      const size_t slot = (g + (ok[u] ? wu : w0)) * group + h;
-      ml[u] = ws_ml[slot];
-      a[u] = ws_acc[slot * kHeadDim + d0 + dd];
+  for (int64_t c0 = w0; c0 <= w1; c0 += kChunk) {
+    const int n = (int)((w1 - c0 + 1) < kChunk ? (w1 - c0 + 1) : kChunk);
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const int64_t w = c0 + i;
+      float wt = 0.0f;
+      if ((w * TP) / W != ((w + 1) * TP) / W) {
+        const float2 ml = ws_ml[(g + w) * group + h];
+        wt = exp2f(ml.x - M);
+        L += wt * ml.y;
+      }
+      wts[i] = wt;
     }
+    __syncthreads();
+    for (int i = j; i < n; i += 128) {
+      float a[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!ok[u]) continue;
-      const float wt = exp2f(ml[u].x - M);
-      L += wt * ml[u].y;
-      acc += wt * a[u];
+      for (int u = 0; u < 16; ++u) {
+        const int iu = i + 8 * u < n ? i + 8 * u : i;
+        a[u] = ws_acc[((g + c0 + iu) * group + h) * kHeadDim + d0 + dd];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (i + 8 * u < n) acc += wts[i + 8 * u] * a[u];
     }
   }
+  // L was summed per thread over its pieces; combine across the block
+  for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o, 32);
   red_o[j][dd] = acc;
   if (dd == 0) red_l[j] = L;
   __syncthreads();
