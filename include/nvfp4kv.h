@@ -110,7 +110,7 @@ int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok,
                    hipStream_t stream);
 
 /* Workspace bytes nvfp4kv_decode_attn needs for this shape (split-K
- * partials).  pages_per_split 0 selects the library's own split plan; the
+ * partials and the quantized queries).  pages_per_split 0 selects the library's own split plan; the
  * same value must be passed to nvfp4kv_decode_attn.  Returns 0 on invalid
  * arguments. */
 size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
@@ -122,8 +122,10 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
  * rotation (when the pool has it), is quantized to NVFP4 and dequantized;
  * scores against the dequantized cached K of tokens 0 .. seq_lens[n]-1 are
  * scaled by sm_scale, softmax-normalized, and weight the dequantized V.
- * Split-K: each (sequence, kv head, page range) is one work item writing
- * partial results to the workspace; a second kernel combines them.
+ * Three kernels: the queries are quantized once per (sequence, kv head);
+ * the pages of all (sequence, kv head) pairs are split evenly over the
+ * decode wavefronts, each writing partial results to the workspace; a
+ * reduce kernel combines them.
  *   q           [n_seq][n_q_heads][128], dtype q_dtype, before RoPE
  *   q_positions [n_seq] int32
  *   page_table  [n_seq][page_table_stride] int32 page ids; token t of
@@ -148,13 +150,17 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
 /* The two stages of nvfp4kv_decode_attn, for callers that combine split
  * partials themselves (for example across devices) or time the stages apart.
  * nvfp4kv_decode_attn_splits takes the arguments of nvfp4kv_decode_attn
- * except `out` and writes only the workspace: for every work item (sequence,
- * kv head, run of pages_per_split pages) and query head of the group, the
- * running max m (log2 units of sm_scale * score), the weight sum l and the
- * weighted V sum acc[128].  Layout, for item = (seq * num_kv_heads + kvh) *
- * n_splits + split: acc at float offset (item * group + h) * 128, then (at
- * the next 256-byte boundary after all acc) the pairs (m, l) at float2 index
- * item * group + h.  Items past a sequence's last page are not written.
+ * except `out` and writes only the workspace.  Work layout: the pages of
+ * segment g = seq * num_kv_heads + kvh, segments in order, form one flat
+ * list of TP pages; the plan's W ranges [w*TP/W, (w+1)*TP/W) split it, and
+ * every (segment, range) pair that overlaps yields one partial in slot
+ * g + w: per query head h of the group, a reference m (log2 units of
+ * sm_scale * score), the weight sum l and the weighted V sum acc[128], with
+ * weights 2^(s - m + 8) for the pair's tokens.  Layout, each part starting
+ * at a 256-byte boundary: acc at float offset (slot * group + h) * 128 for
+ * slots 0 .. n_seq*num_kv_heads + W - 1; the pairs (m, l) at float2 index
+ * slot * group + h; then 4 KiB per segment of quantized queries (internal).
+ * Slots of pairs that do not overlap are not written.
  * nvfp4kv_decode_reduce reads them and writes out = sum_s 2^(m_s - M) acc_s
  * / sum_s 2^(m_s - M) l_s per (sequence, query head).  Both must get the
  * same n_seq, n_q_heads, max_seq_len and pages_per_split. */

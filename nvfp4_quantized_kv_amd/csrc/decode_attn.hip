@@ -10,21 +10,25 @@
 // in registers to fp16, which holds every E2M1 x E4M3 value exactly, and run
 // on v_mfma_f32_16x16x32_f16.
 //
-// One wavefront (one workgroup) handles a work item (sequence, kv head, range
-// of pages).  Per 64-token page it loads 9216 contiguous bytes with nine
-// 16-byte loads per lane (the code tiling of the pool makes each load land
-// directly in the lane's matrix operand), keeps the next page's loads in
-// flight while it computes the current one, and
+// A small kernel quantizes each (sequence, kv head) pair's queries once and
+// stores them as MFMA operands.  The decode kernel then splits the pages of
+// all pairs evenly over its wavefronts (one workgroup each, all resident)
+// and each wavefront streams its range page by page: per 64-token page it
+// loads 9216 contiguous bytes with nine 16-byte loads per lane (the code
+// tiling of the pool makes each load land directly in the lane's matrix
+// operand), two pages ahead of use, and
 //   QK  : 4 MFMAs per 16 tokens; A = K-hat (16 tokens x 32 dims per lane
-//         group), B = Q-hat (query heads of the group on N, zero-padded to 16)
-//   soft: running max per head in log2 units, scores scaled by
-//         sm_scale*log2(e), weights 2^(s - m + 15) so that fp16 keeps them
-//         normal; reductions across the four lane groups with permlane swaps
+//         group), B = Q-hat (query heads of the group on N)
+//   soft: per-head reference in log2 units, scores scaled by
+//         sm_scale*log2(e), weights 2^(s - m + 8) kept below 2^15 so that
+//         fp16 keeps them normal; reductions across the four lane groups
+//         with permlane swaps, only when the reference has to move
 //   PV  : O^T[d][h] += V-hat^T[d][t] P^T[t][h]; A = V-hat (16 dims x 32
-//         tokens), B = P split into fp16 hi + lo parts (2 MFMAs) so the
-//         weights keep ~22 bits.
-// Partial (m, l, acc) per item go to the workspace; decode_reduce combines
-// them per (sequence, query head).
+//         tokens), B = the weights split into fp16 high and low parts, so
+//         they keep ~22 bits (for groups of up to 8 heads both parts share
+//         one MFMA: columns 0-7 carry the high parts, 8-15 the low parts).
+// Partial (m, l, acc) per (pair, wavefront) go to the workspace;
+// decode_reduce combines them per (sequence, query head).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -78,29 +82,27 @@ __device__ inline float sum4lanes(float v) {
   return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
 
-// One 32-token half of a page: QK^T for tiles 2hh, 2hh+1, the online
-// softmax over those 32 tokens, and PV for them.  `k0`/`k1` hold the two K
-// tiles (token 16i + lane%16, dims 32*g4 .. +31), `va`/`vb` the two V token
-// quads of this lane group, `sk` this lane's K scale pair of token c16 in the
-// staged page (tile stride 128 bytes), `sv` its V scale byte of token 4*g4.
-// MASKED halves may hold tokens at or past the sequence end: those get zero
-// weight and a zero V scale, chosen by selects so that stale bytes, which may
-// decode to NaN, never reach the sums.
-template <bool MASKED>
-__device__ __forceinline__ void half_step(u4& k0, u4& k1, u4& va, u4& vb, __amdgpu_buffer_rsrc_t nrs,
-                                          int voff, const uint8_t* __restrict__ sk,
-                                          const uint8_t* __restrict__ sv, int hh, int nvalid,
-                                          int g4, const h8 (&qb)[4], float c_log2, f4 (&acc)[8],
-                                          float& m_run, float& l_run) {
-  // ---- QK^T: S[i] holds tokens 32hh + 16i + 4*g4 + r for query head c16
-  f4 S[2];
+// The online softmax works in log2 units: a score s (already multiplied by
+// sm_scale * log2(e)) gets the weight 2^(s - m + kOff), where m is a per-head
+// reference that is raised only when some score passes m + kMargin.  Weights
+// therefore stay below 2^(kOff + kMargin) = 2^15, inside fp16's normal range,
+// and most 32-token units skip the cross-lane maximum and the rescale.
+constexpr float kOff = 8.0f;
+constexpr float kMargin = 7.0f;
+
+// QK^T of one 32-token unit (K tiles i = 0, 1 of the unit): S[i] holds
+// tokens 16i + 4*g4 + r of the unit for query column c16.  `k0`/`k1` hold
+// the lane's 32 codes of token c16 (+16) for dims 32*g4 .. +31; `sk` points
+// at the lane's K scale pair (blocks 2*g4, 2*g4+1) of the unit's first token
+// row in the staged page (tile stride 128 bytes).
+__device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_t* __restrict__ sk,
+                                        const h8 (&qb)[4], f4 (&S)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * (2 * hh + i));
+    const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * i);
     // f16 bits of (s0 * 2^-8, s1 * 2^-8): an E4M3 byte shifted left by 7 is
     // the f16 encoding of its value times 2^-8 (both subnormal and normal)
-    const uint32_t both = (__builtin_amdgcn_perm(0u, ku, 0x0c010c00u)) << 7;
-    const h2 sc = bits_h2(both);
+    const h2 sc = bits_h2(__builtin_amdgcn_perm(0u, ku, 0x0c010c00u) << 7);
     const h2 sc0 = __builtin_shufflevector(sc, sc, 0, 0), sc1 = __builtin_shufflevector(sc, sc, 1, 1);
     const u4& kc = i ? k1 : k0;
     S[i] = f4{0.f, 0.f, 0.f, 0.f};
@@ -118,64 +120,19 @@ __device__ __forceinline__ void half_step(u4& k0, u4& k1, u4& va, u4& vb, __amdg
       S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], S[i], 0, 0, 0);
     }
   }
-  // this half's K registers are free: request the next page's.  The loads
-  // are unconditional (past a piece's end `nrs` is an empty resource) so that
-  // the wait counters stay exact across the loop: a conditional load makes
-  // the compiler drain every outstanding load at the join.
-  k0 = ld16(nrs, voff, 1024 * (2 * hh));
-  k1 = ld16(nrs, voff, 1024 * (2 * hh + 1));
+}
 
-  // ---- online softmax (log2 domain, weights scaled by 2^15)
-  float smax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (MASKED) {
-        if (32 * hh + 16 * i + 4 * g4 + r < nvalid) smax = fmaxf(smax, S[i][r]);
-      } else {
-        smax = fmaxf(smax, S[i][r]);
-      }
-    }
-  smax = max4lanes(smax);
-  const float m_new = fmaxf(m_run, smax * c_log2);
-  if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-    m_run = m_new;
-  }
-  const float off = 15.0f - m_run;
-  float P[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
-      if (MASKED && 32 * hh + 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
-      P[i][r] = e;
-      l_run += e;
-    }
-
-  // ---- PV: O^T[d][h] += V-hat^T[d][t] P^T[t][h] over these 32 tokens; the
-  // weights go in as fp16 hi + lo parts (two MFMAs) to keep ~22 bits
-  h8 bhi, blo;
-#pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2) {
-    const float pa = P[s2 >> 1][(2 * s2) & 3];
-    const float pb = P[s2 >> 1][(2 * s2 + 1) & 3];
-    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
-    const float ra = pa - (float)hi[0];     // exact remainders
-    const float rb = pb - (float)hi[1];
-    const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(ra, rb));
-    bhi[2 * s2] = hi[0];
-    bhi[2 * s2 + 1] = hi[1];
-    blo[2 * s2] = lo[0];
-    blo[2 * s2 + 1] = lo[1];
-  }
+// PV of one 32-token unit: O^T[d][h] += V-hat^T[d][t] P^T[t][h].  `va`/`vb`
+// hold the V codes of tokens 4*g4 + r and 16 + 4*g4 + r of the unit (dims
+// 8*c16 .. +7); `sv` points at the V scale byte of the unit's token 4*g4,
+// block c16/2, in the staged page.  PACKED: `p0` carries the fp16 high part
+// of the weights in columns 0-7 and the low part in columns 8-15, one MFMA
+// per tile; otherwise `p0`/`p1` are the high/low parts, two MFMAs per tile.
+template <bool PACKED>
+__device__ __forceinline__ void pv_unit(const u4& va, const u4& vb, const uint8_t* __restrict__ sv,
+                                        const h8& p0, const h8& p1, f4 (&acc)[8]) {
   // V words of the 8 tokens of this lane group; token of k-slot s:
-  // s < 4: 32hh + 4*g4 + s, s >= 4: 32hh + 16 + 4*g4 + (s-4)
+  // s < 4: 4*g4 + s, s >= 4: 16 + 4*g4 + (s-4)
   const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
   uint32_t A[4], B[4];
   h2 svp[4];
@@ -184,14 +141,8 @@ __device__ __forceinline__ void half_step(u4& k0, u4& k1, u4& va, u4& vb, __amdg
     const uint32_t w0 = w[2 * pr], w1 = w[2 * pr + 1];
     A[pr] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);   // even dims
     B[pr] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);   // odd dims
-    const int s0 = 2 * pr, s1 = 2 * pr + 1;
-    const int t0 = 32 * hh + (s0 >= 4 ? 16 : 0) + (s0 & 3);   // token offset from 4*g4
-    const int t1 = 32 * hh + (s1 >= 4 ? 16 : 0) + (s1 & 3);
-    uint32_t b0 = sv[8 * t0], b1 = sv[8 * t1];
-    if (MASKED) {
-      if (t0 + 4 * g4 >= nvalid) b0 = 0;   // stale slot: zero value
-      if (t1 + 4 * g4 >= nvalid) b1 = 0;
-    }
+    const int t0 = (pr >= 2 ? 16 : 0) + 2 * (pr & 1);          // token offset from 4*g4
+    const uint32_t b0 = sv[8 * t0], b1 = sv[8 * (t0 + 1)];
     svp[pr] = bits_h2((b0 | (b1 << 16)) << 7);
   }
 #pragma unroll
@@ -206,14 +157,13 @@ __device__ __forceinline__ void half_step(u4& k0, u4& k1, u4& va, u4& vb, __amdg
       ao[2 * pr] = o[0];
       ao[2 * pr + 1] = o[1];
     }
-    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, bhi, acc[2 * b], 0, 0, 0);
-    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, blo, acc[2 * b], 0, 0, 0);
-    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, bhi, acc[2 * b + 1], 0, 0, 0);
-    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, blo, acc[2 * b + 1], 0, 0, 0);
+    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p0, acc[2 * b], 0, 0, 0);
+    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p0, acc[2 * b + 1], 0, 0, 0);
+    if (!PACKED) {
+      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p1, acc[2 * b], 0, 0, 0);
+      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p1, acc[2 * b + 1], 0, 0, 0);
+    }
   }
-  // and the V registers: request the next page's
-  va = ld16(nrs, voff, kVCodeOff + 1024 * (2 * hh));
-  vb = ld16(nrs, voff, kVCodeOff + 1024 * (2 * hh + 1));
 }
 
 // Pages of sequence `s`.
@@ -224,20 +174,21 @@ __device__ inline int64_t seq_pages(const int32_t* __restrict__ seq_lens, int s)
 // The wave whose range [w*TP/W, (w+1)*TP/W) holds flattened page index x.
 __device__ inline int64_t wave_of(int64_t x, int64_t TP, int64_t W) { return ((x + 1) * W - 1) / TP; }
 
-// One piece of work: pages [p0, p1) of (seq, kvh).  Writes (m, l, acc) for
-// the group's query heads to partial slot `slot`.
-__device__ __forceinline__ void decode_piece(
-    const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_q_heads,
-    int group, const void* __restrict__ q, int q_dtype, const int32_t* __restrict__ q_positions,
-    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard, const int32_t* __restrict__ page_table, int pt_stride, int T, float c_log2,
-    float* __restrict__ ws_acc, float2* __restrict__ ws_ml, int seq, int kvh, int p0, int p1,
-    size_t slot, _Float16* qhat, u4 (*sc_lds)[64]) {
+// Query prologue, once per (sequence, kv head) segment: RoPE, Hadamard and
+// the NVFP4 round trip of the group's query heads, written as the B
+// operands of QK^T: qws[(seg * 4 + c) * 64 + lane] holds, for lane (c16,
+// g4), dims 32*g4 + 8c .. +7 of the query head of column c16 (fp16, exact).
+// PACKED: columns 8-15 repeat heads 0-7.  Columns past the group are zero.
+template <bool PACKED>
+__global__ __launch_bounds__(64) void decode_q_prep_kernel(
+    int hkv, int n_q_heads, int group, const void* __restrict__ q, int q_dtype,
+    const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int rotary_dim, int hadamard, h8* __restrict__ qws) {
+  __shared__ __attribute__((aligned(16))) _Float16 qhat[16 * kHeadDim];
+  const int seg = (int)blockIdx.x;
+  const int seq = seg / hkv, kvh = seg % hkv;
   const int lane = (int)threadIdx.x;
-  const int g4 = lane >> 4;     // lane group
-  const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
-
-  // ---- query prologue: RoPE, Hadamard, NVFP4 round trip, fp16 Q-hat in LDS
+  const int g4 = lane >> 4, c16 = lane & 15;
   for (int pass = 0; pass < (group + 3) / 4; ++pass) {
     const int h = pass * 4 + g4;
     const int hh = h < group ? h : group - 1;
@@ -273,140 +224,413 @@ __device__ __forceinline__ void decode_piece(
     if (h < group) *reinterpret_cast<h8*>(&qhat[h * kHeadDim + 8 * c16]) = qv;
   }
   __syncthreads();
-  h8 qb[4];
+  const int qcol = PACKED ? (c16 & 7) : c16;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    qb[c] = (c16 < group) ? *reinterpret_cast<const h8*>(&qhat[c16 * kHeadDim + 32 * g4 + 8 * c]) : z;
+    qws[((size_t)seg * 4 + c) * 64 + lane] =
+        (qcol < group) ? *reinterpret_cast<const h8*>(&qhat[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
   }
+}
 
-  // ---- main loop over the piece's pages
-  const uint8_t* layer_base =
-      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes;
-  const int32_t* pt = page_table + (size_t)seq * pt_stride;
-  const size_t blk_stride = (size_t)hkv * kBlockBytes;
-  const int voff = 16 * lane;
-  // One page in registers at a time.  Each half-page's K codes are requested
-  // for the next page as soon as QK^T has consumed them, its V codes as soon
-  // as PV has, and the scales right after the current ones went to LDS, so
-  // every load overlaps the rest of the current page.
-  __amdgpu_buffer_rsrc_t rs = block_rsrc(layer_base + (size_t)pt[p0] * blk_stride + (size_t)kvh * kBlockBytes);
-  // Issued in the order the loop issues them (scales, then K and V of each
-  // half), so the wait counts at the loop head are the same on entry and on
-  // the back edge.
-  u4 kc[4], vc[4], sc;
-  sc = ld16(rs, voff, kKScaleOff);
-  __builtin_amdgcn_sched_barrier(0);
+// Partial (m, l, acc) of the group's query heads to slot `slot`.
+template <bool PACKED>
+__device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, float l_run, int c16,
+                                              int g4, int group, float* __restrict__ ws_acc,
+                                              float2* __restrict__ ws_ml, size_t slot) {
+  f4 o[8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    kc[2 * hh] = ld16(rs, voff, 1024 * (2 * hh));
-    kc[2 * hh + 1] = ld16(rs, voff, 1024 * (2 * hh + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    vc[2 * hh] = ld16(rs, voff, kVCodeOff + 1024 * (2 * hh));
-    vc[2 * hh + 1] = ld16(rs, voff, kVCodeOff + 1024 * (2 * hh + 1));
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  f4 acc[8];
+  for (int j = 0; j < 8; ++j) {
+    o[j] = acc[j];
+    if (PACKED) {
+      // column h += column h + 8 (high + low parts of the weights)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
-
-  // lane-invariant LDS byte offsets of this lane's scales inside a staged page
-  const int sk_off = 8 * c16 + 2 * g4;            // K scales of token c16 (+16i), blocks 2g4, 2g4+1
-  const int sv_off = 512 + 32 * g4 + (c16 >> 1);  // V scales of token 4*g4 (+...), block c16/2
-  for (int p = p0; p < p1; ++p) {
-    // the next page; past the piece's end an empty resource (loads return
-    // zeros without memory traffic) keeps the load sequence unchanged
-    const bool more = p + 1 < p1;
-    const __amdgpu_buffer_rsrc_t nrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(layer_base + (size_t)pt[more ? p + 1 : p] * blk_stride + (size_t)kvh * kBlockBytes),
-        0, more ? kBlockBytes : 0, 0x00020000);
-    const int buf = (p - p0) & 1;
-    sc_lds[buf][lane] = sc;
-    __syncthreads();
-    sc = ld16(nrs, voff, kKScaleOff);
-    const uint8_t* scb = reinterpret_cast<const uint8_t*>(&sc_lds[buf][0]);
-    const int nvalid = T - p * kPageSize;  // tokens of this page that exist, >= 1
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      // each half's registers are refilled with the next page's data as soon
-      // as this half has consumed them (inside half_step)
-      if (nvalid >= kPageSize)
-        half_step<false>(kc[2 * hh], kc[2 * hh + 1], vc[2 * hh], vc[2 * hh + 1], nrs, voff,
-                         scb + sk_off, scb + sv_off, hh, nvalid, g4, qb, c_log2, acc, m_run, l_run);
-      else
-        half_step<true>(kc[2 * hh], kc[2 * hh + 1], vc[2 * hh], vc[2 * hh + 1], nrs, voff,
-                        scb + sk_off, scb + sv_off, hh, nvalid, g4, qb, c_log2, acc, m_run, l_run);
+      for (int i = 0; i < 4; ++i)
+        o[j][i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[j][i]), 0x128, 0xF, 0xF, false));
     }
   }
-
-  // ---- partial results of this piece
   const float l_tot = sum4lanes(l_run);
   if (c16 < group) {
-    // lane holds dims 32*g4 + 8i + j in acc[j][i]
+    // lane holds dims 32*g4 + 8i + j in o[j][i]
     float* dst = ws_acc + (slot * group + c16) * kHeadDim + 32 * g4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      reinterpret_cast<float4*>(dst + 8 * i)[0] = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-      reinterpret_cast<float4*>(dst + 8 * i)[1] = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+      reinterpret_cast<float4*>(dst + 8 * i)[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
+      reinterpret_cast<float4*>(dst + 8 * i)[1] = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
     }
-    if (g4 == 0) ws_ml[slot * group + c16] = make_float2(m_run, l_tot);
+    if (g4 == 0) ws_ml[slot * group + c16] = make_float2(m_ref, l_tot);
   }
-  __syncthreads();  // the next piece rewrites qhat
 }
+
+// Where a finished segment's partial goes and which slot comes next.
+struct SegState {
+  size_t slot;        // partial slot of the current segment (segment + wave)
+  int qslot;          // LDS slot of the current segment's query operands
+};
+
+// Online softmax of one unit with the segment switch folded into its rare
+// branch: when `sw` is set, the unit is the first of a new segment, so the
+// finished segment's partial is written and the running state restarts
+// (reference -inf, so the rescale factor is 0).
+template <bool MASKED, bool PACKED>
+__device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, int nvalid,
+                                           float c_log2, float lo_mask, f4 (&acc)[8], float& m_ref,
+                                           float& l_run, h8& p0, h8& p1, bool sw, int group,
+                                           float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+                                           SegState& st) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!MASKED || 16 * i + 4 * g4 + r < nvalid) mx = fmaxf(mx, S[i][r]);
+  mx *= c_log2;
+  if (sw || __builtin_amdgcn_ballot_w64(mx > m_ref + kMargin)) {
+    if (sw) {
+      write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
+      st.slot += 1;
+      st.qslot += 1;
+      m_ref = -INFINITY;
+      l_run = 0.0f;
+    }
+    const float m_new = fmaxf(m_ref, max4lanes(mx));
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    m_ref = m_new;
+  }
+  const float off = kOff - m_ref;
+  float P[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
+      if (MASKED && 16 * i + 4 * g4 + r >= nvalid) e = 0.0f;
+      P[4 * i + r] = e;
+      l_run += e;
+    }
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const float pa = P[2 * s2], pb = P[2 * s2 + 1];
+    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
+    h2 lo;
+    if (PACKED) {
+      // columns 8-15 (lo_mask 1) take the exact remainder, columns 0-7 the
+      // truncated value itself (remainder of nothing subtracted)
+      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-lo_mask, (float)hi[0], pa),
+                                                             fmaf(-lo_mask, (float)hi[1], pb)));
+      p0[2 * s2] = lo[0];
+      p0[2 * s2 + 1] = lo[1];
+    } else {
+      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
+      p0[2 * s2] = hi[0];
+      p0[2 * s2 + 1] = hi[1];
+      p1[2 * s2] = lo[0];
+      p1[2 * s2 + 1] = lo[1];
+    }
+  }
+}
+
+template <bool MASKED_FULL, bool PACKED>
+__device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (&S)[2], int g4,
+                                             int c16, float c_log2, float lo_mask, f4 (&acc)[8],
+                                             float& m_ref, float& l_run, h8& p0, h8& p1, bool sw,
+                                             int group, float* __restrict__ ws_acc,
+                                             float2* __restrict__ ws_ml, SegState& st) {
+  if (nvalid >= full_at)
+    softmax_sw<false, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
+                              group, ws_acc, ws_ml, st);
+  else
+    softmax_sw<true, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
+                             group, ws_acc, ws_ml, st);
+}
+
+// Query-operand slots in LDS per wave: the segments one wave covers in the
+// usual case (its range of about TP/W pages crosses at most one or two
+// segment boundaries).  A wave covering more segments reloads the last slot
+// at each further switch.
+constexpr int kQSlots = 3;
 
 // Stream-K decode.  All (sequence, kv head, page) work is laid out flat:
 // segment g = seq * hkv + kvh holds that pair's pages, segments in order.
 // With TP pages in all and W = gridDim.x wavefronts, wave w takes the range
 // [w*TP/W, (w+1)*TP/W), so every wave gets the same number of pages (+-1)
 // whatever the sequence lengths.  A range may start or end inside a segment
-// and may cover several; the wave writes one partial per segment piece, to
-// slot g + w (distinct for every (segment, wave) pair that overlaps).
+// and may cover several; the wave writes one partial per segment it
+// touches, to slot g + w (distinct for every (segment, wave) pair).
+//
+// The wave walks its range as one stream of pages: two register sets, A for
+// the range's even pages and B for its odd pages, so every load is issued
+// two pages before its data is used, and the stream does not stop at a
+// segment boundary.  Within the stream, a software pipeline over 32-token
+// units: one straight-line block does QK^T of unit u+1 and PV of unit u,
+// two independent streams of dequantization and MFMAs, then the softmax of
+// unit u+1 turns its scores into the weights that the next block's PV uses.
+// Loads are unconditional (past the range the buffer resource is empty and
+// returns zeros without memory traffic) so the wait counts stay exact.
+//
+// Each lane of the wave describes one page of a 64-page window of the
+// range: its pool block (page * hkv + kv head), its valid tokens, its page
+// index inside its segment and its segment; the loop reads these with
+// readlane, so no scalar loads sit on its path.
+template <bool PACKED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_splitk_kernel(
-    const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq,
-    int n_q_heads, int group, const void* __restrict__ q, int q_dtype,
-    const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, int rotary_dim, int hadamard,
-    const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens,
-    float c_log2, float* __restrict__ ws_acc, float2* __restrict__ ws_ml) {
-  __shared__ __attribute__((aligned(16))) _Float16 qhat[16 * kHeadDim];
+    const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int group,
+    const h8* __restrict__ qws, const int32_t* __restrict__ page_table, int pt_stride,
+    const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
+    float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
+  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][4][64];
 
+  const int lane = (int)threadIdx.x;
+  const int g4 = lane >> 4;     // lane group
+  const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
   const int64_t W = gridDim.x, w = blockIdx.x;
   int64_t TP = 0;
   for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
   TP *= hkv;
-  int64_t x = (w * TP) / W;
-  const int64_t end = ((w + 1) * TP) / W;
-  if (x >= end) return;
-  // find the sequence holding x
+  const int64_t a = (w * TP) / W;
+  const int64_t b = ((w + 1) * TP) / W;
+  if (a >= b) return;
+
+  // segment holding page a: sequence, kv head, flat index of its first page
   int seq = 0;
-  int64_t seq_base = 0;  // flat index of the first page of seq's first segment
+  int64_t seq_base = 0;
   int64_t pg = seq_pages(seq_lens, 0);
-  while (x >= seq_base + hkv * pg) {
+  while (a >= seq_base + hkv * pg) {
     seq_base += hkv * pg;
     ++seq;
     pg = seq_pages(seq_lens, seq);
   }
-  while (x < end) {
-    const int kvh = (int)((x - seq_base) / pg);
-    const int64_t seg_start = seq_base + kvh * pg;
-    const int p0 = (int)(x - seg_start);
-    const int64_t seg_end = seg_start + pg;
-    const int p1 = (int)((end < seg_end ? end : seg_end) - seg_start);
-    const size_t slot = (size_t)seq * hkv + kvh + (size_t)w;
-    decode_piece(pool, num_pages, hkv, layer, n_q_heads, group, q, q_dtype, q_positions, rope_cos,
-                 rope_sin, rotary_dim, hadamard, page_table, pt_stride, seq_lens[seq], c_log2,
-                 ws_acc, ws_ml, seq, kvh, p0, p1, slot, qhat, sc_lds);
-    x = seg_start + p1;
-    if (kvh == hkv - 1 && x < end) {
-      seq_base += hkv * pg;
-      ++seq;
-      pg = seq_pages(seq_lens, seq);
+  const int kvh0 = (int)((a - seq_base) / pg);
+  const int seg0 = seq * hkv + kvh0;
+
+  // ---- page window: lane i describes flat page win + i of the range
+  int64_t win = a;
+  int w_blk, w_nv, w_j, w_sg;
+  auto load_window = [&](int wseq, int wkvh, int64_t wstart, int64_t wpg) {
+    int lseq = wseq, lkvh = wkvh;
+    int64_t lstart = wstart, lpg = wpg;
+    const int64_t x = min(win + lane, b - 1);
+    while (x >= lstart + lpg) {
+      lstart += lpg;
+      if (++lkvh == hkv) {
+        lkvh = 0;
+        ++lseq;
+        lpg = seq_pages(seq_lens, lseq);
+      }
     }
+    const int j = (int)(x - lstart);
+    w_blk = page_table[(size_t)lseq * pt_stride + j] * hkv + lkvh;
+    w_nv = (win + lane < b) ? seq_lens[lseq] - j * kPageSize : 0;
+    w_j = j;
+    w_sg = lseq * hkv + lkvh;
+  };
+  load_window(seq, kvh0, seq_base + (int64_t)kvh0 * pg, pg);
+
+  const uint8_t* layer_base =
+      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes;
+  // buffer resource of flat page x (empty past the range)
+  auto rsrc_of = [&](int64_t x) {
+    const bool ok = x < b;
+    const int blk = __builtin_amdgcn_readlane(w_blk, (int)((ok ? x : b - 1) - win));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(layer_base + (size_t)blk * kBlockBytes),
+                                             0, ok ? kBlockBytes : 0, 0x00020000);
+  };
+  auto nvalid_of = [&](int64_t x) {
+    return x < b ? __builtin_amdgcn_readlane(w_nv, (int)(x - win)) : 0;
+  };
+  // first page of a segment other than page a's
+  auto starts_segment = [&](int64_t x) {
+    return x < b && __builtin_amdgcn_readlane(w_j, (int)(x - win)) == 0;
+  };
+
+  // segments of the range whose query operands are preloaded to LDS slots
+  // 0 .. nq-1 (slot k: segment seg0 + k)
+  int nq;
+  {
+    int sl = seq;
+    int64_t base = seq_base, pgl = pg;
+    while (b - 1 >= base + hkv * pgl) {
+      base += hkv * pgl;
+      ++sl;
+      pgl = seq_pages(seq_lens, sl);
+    }
+    const int seg_last = sl * hkv + (int)((b - 1 - base) / pgl);
+    nq = min(seg_last - seg0 + 1, kQSlots);
   }
+  const int n_seg = n_seq * hkv;
+  h8 qpre[kQSlots][4];
+#pragma unroll
+  for (int k = 0; k < kQSlots; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qpre[k][c] = qws[((size_t)min(seg0 + k, n_seg - 1) * 4 + c) * 64 + lane];
+
+  const int voff = 16 * lane;
+  // Scale bytes are staged with their sign bits cleared.  Written scales are
+  // positive, so nothing changes for them; stale bytes of slots past the
+  // sequence end then still decode to finite values (an E4M3 byte shifted
+  // left by 7 is an fp16 Inf or NaN only with bit 7 set), and their zero
+  // weights zero them in the MFMAs.
+  // lane-invariant LDS byte offsets of this lane's scales inside a staged page
+  const int sk_off = 8 * c16 + 2 * g4;            // K scales of token c16, blocks 2g4, 2g4+1
+  const int sv_off = 512 + 32 * g4 + (c16 >> 1);  // V scales of token 4*g4, block c16/2
+  const float lo_mask = (PACKED && c16 >= 8) ? 1.0f : 0.0f;
+
+  f4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;
+  float l_run = 0.0f;
+  SegState st{(size_t)seg0 + (size_t)w, 0};
+  int seg_cur = seg0;
+  // query operands of the current segment from LDS; a wave that has used up
+  // its slots loads the next segment's into the last one
+  auto q_of = [&](h8 (&qb)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qb[c] = q_lds[min(st.qslot, kQSlots - 1)][c][lane];
+  };
+  // a page that starts a new segment is coming: its query operands go to
+  // their slot unless they were preloaded (the last slot is free by then:
+  // the finishing segment has no QK^T left)
+  auto prepare_switch = [&]() {
+    ++seg_cur;
+    const int k = st.qslot + 1;
+    if (k >= nq) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        q_lds[min(k, kQSlots - 1)][c][lane] = qws[((size_t)seg_cur * 4 + c) * 64 + lane];
+    }
+  };
+
+  // ---- prologue: loads of the range's first two pages; unit 0's scores and
+  // weights; the loads left in flight and their order are those of the
+  // loop's back edge, so the wait counts at the loop head are the same on
+  // entry and on the back edge.
+  u4 kA[4], vA[4], sA, kB[4], vB[4], sB;
+  {
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a), r1 = rsrc_of(a + 1);
+    sA = ld16(r0, voff, kKScaleOff);
+    kA[0] = ld16(r0, voff, 0);
+    kA[1] = ld16(r0, voff, 1024);
+    __builtin_amdgcn_sched_barrier(0);
+    kA[2] = ld16(r0, voff, 2048);
+    kA[3] = ld16(r0, voff, 3072);
+    vA[0] = ld16(r0, voff, kVCodeOff);
+    vA[1] = ld16(r0, voff, kVCodeOff + 1024);
+    sB = ld16(r1, voff, kKScaleOff);
+    kB[0] = ld16(r1, voff, 0);
+    kB[1] = ld16(r1, voff, 1024);
+    vA[2] = ld16(r0, voff, kVCodeOff + 2048);
+    vA[3] = ld16(r0, voff, kVCodeOff + 3072);
+    kB[2] = ld16(r1, voff, 2048);
+    kB[3] = ld16(r1, voff, 3072);
+    vB[0] = ld16(r1, voff, kVCodeOff);
+    vB[1] = ld16(r1, voff, kVCodeOff + 1024);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int k = 0; k < kQSlots; ++k)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) q_lds[k][c][lane] = qpre[k][c];
+  f4 S[2];
+  h8 pw0, pw1, qb[4];
+  {
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
+    sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
+    sA = ld16(r2, voff, kKScaleOff);
+    q_of(qb);
+    qk_unit(kA[0], kA[1], reinterpret_cast<const uint8_t*>(&sc_lds[0][0]) + sk_off, qb, S);
+    kA[0] = ld16(r2, voff, 0);
+    kA[1] = ld16(r2, voff, 1024);
+    vB[2] = ld16(r1, voff, kVCodeOff + 2048);
+    vB[3] = ld16(r1, voff, kVCodeOff + 3072);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_pick<false, PACKED>(nvalid_of(a), 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+                                pw0, pw1, false, group, ws_acc, ws_ml, st);
+  }
+
+  // ---- main loop, two pages (p in set A, p+1 in set B) per trip.  Page p
+  // is staged in LDS buffer 0, page p+1 in buffer 1.
+  const uint8_t* sb0 = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
+  const uint8_t* sb1 = reinterpret_cast<const uint8_t*>(&sc_lds[1][0]);
+  for (int64_t p = a; p < b; p += 2) {
+    if (min(p + 4, b - 1) - win >= 64) {   // ranges of more than 64 pages
+      const int o = (int)(p - win);
+      const int sg = __builtin_amdgcn_readlane(w_sg, o);
+      const int j = __builtin_amdgcn_readlane(w_j, o);
+      win = p;
+      load_window(sg / hkv, sg % hkv, p - j, seq_pages(seq_lens, sg / hkv));
+    }
+    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(p + 2), r3 = rsrc_of(p + 3), r4 = rsrc_of(p + 4);
+    const int nv0 = nvalid_of(p), nv1 = nvalid_of(p + 1), nv2 = nvalid_of(p + 2);
+    const bool sw1 = starts_segment(p + 1), sw2 = starts_segment(p + 2);
+
+    // page p, tokens 32..63 scored, 0..31 accumulated
+    q_of(qb);
+    qk_unit(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
+    kA[2] = ld16(r2, voff, 2048);
+    kA[3] = ld16(r2, voff, 3072);
+    pv_unit<PACKED>(vA[0], vA[1], sb0 + sv_off, pw0, pw1, acc);
+    vA[0] = ld16(r2, voff, kVCodeOff);
+    vA[1] = ld16(r2, voff, kVCodeOff + 1024);
+    softmax_pick<false, PACKED>(nv0 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                pw1, false, group, ws_acc, ws_ml, st);
+
+    // page p+1 staged; its tokens 0..31 scored, page p's 32..63 accumulated
+    sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
+    sB = ld16(r3, voff, kKScaleOff);
+    if (sw1) prepare_switch();
+    {
+      h8 qn[4];
+      const int s = st.qslot + (sw1 ? 1 : 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qn[c] = q_lds[min(s, kQSlots - 1)][c][lane];
+      qk_unit(kB[0], kB[1], sb1 + sk_off, qn, S);
+    }
+    kB[0] = ld16(r3, voff, 0);
+    kB[1] = ld16(r3, voff, 1024);
+    pv_unit<PACKED>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
+    vA[2] = ld16(r2, voff, kVCodeOff + 2048);
+    vA[3] = ld16(r2, voff, kVCodeOff + 3072);
+    softmax_pick<false, PACKED>(nv1, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
+                                sw1, group, ws_acc, ws_ml, st);
+    if (p + 1 >= b) break;
+
+    // page p+1, tokens 32..63 scored, 0..31 accumulated
+    q_of(qb);
+    qk_unit(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
+    kB[2] = ld16(r3, voff, 2048);
+    kB[3] = ld16(r3, voff, 3072);
+    pv_unit<PACKED>(vB[0], vB[1], sb1 + sv_off, pw0, pw1, acc);
+    vB[0] = ld16(r3, voff, kVCodeOff);
+    vB[1] = ld16(r3, voff, kVCodeOff + 1024);
+    softmax_pick<false, PACKED>(nv1 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                pw1, false, group, ws_acc, ws_ml, st);
+
+    // page p+2 staged; its tokens 0..31 scored, page p+1's 32..63 accumulated
+    sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
+    sA = ld16(r4, voff, kKScaleOff);
+    if (sw2) prepare_switch();
+    {
+      h8 qn[4];
+      const int s = st.qslot + (sw2 ? 1 : 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qn[c] = q_lds[min(s, kQSlots - 1)][c][lane];
+      qk_unit(kA[0], kA[1], sb0 + sk_off, qn, S);
+    }
+    kA[0] = ld16(r4, voff, 0);
+    kA[1] = ld16(r4, voff, 1024);
+    pv_unit<PACKED>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
+    vB[2] = ld16(r3, voff, kVCodeOff + 2048);
+    vB[3] = ld16(r3, voff, kVCodeOff + 3072);
+    softmax_pick<false, PACKED>(nv2, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
+                                sw2, group, ws_acc, ws_ml, st);
+  }
+  write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
 }
 
 // Combine the partials of one (sequence, query head) for 32 output dims:
@@ -509,14 +733,27 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
                                 const int32_t* page_table, int page_table_stride,
                                 const int32_t* seq_lens, float sm_scale, void* workspace,
                                 const DecodePlan& plan, hipStream_t stream) {
-  float* ws_acc = reinterpret_cast<float*>(workspace);
-  const size_t acc_bytes = (ws_acc_bytes(n_seq, P.hkv, plan) + 255) & ~(size_t)255;
-  float2* ws_ml = reinterpret_cast<float2*>(reinterpret_cast<uint8_t*>(workspace) + acc_bytes);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  float* ws_acc = reinterpret_cast<float*>(ws);
+  float2* ws_ml = reinterpret_cast<float2*>(ws + ws_ml_offset(n_seq, P.hkv, plan));
+  h8* qws = reinterpret_cast<h8*>(ws + ws_q_offset(n_seq, P.hkv, plan));
   const float c_log2 = sm_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(decode_attn_splitk_kernel, dim3(plan.n_waves), dim3(64), 0, stream, P.base,
-                     P.num_pages, P.hkv, layer, n_seq, n_q_heads, plan.group, q, q_dtype,
-                     q_positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table,
-                     page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
+  const int n_seg = n_seq * P.hkv;
+  if (plan.group <= 8) {
+    hipLaunchKernelGGL(decode_q_prep_kernel<true>, dim3(n_seg), dim3(64), 0, stream, P.hkv, n_q_heads,
+                       plan.group, q, q_dtype, q_positions, rope_cos, rope_sin, P.rotary_dim,
+                       P.hadamard, qws);
+    hipLaunchKernelGGL(decode_attn_splitk_kernel<true>, dim3(plan.n_waves), dim3(64), 0, stream,
+                       P.base, P.num_pages, P.hkv, layer, n_seq, plan.group, qws, page_table,
+                       page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
+  } else {
+    hipLaunchKernelGGL(decode_q_prep_kernel<false>, dim3(n_seg), dim3(64), 0, stream, P.hkv, n_q_heads,
+                       plan.group, q, q_dtype, q_positions, rope_cos, rope_sin, P.rotary_dim,
+                       P.hadamard, qws);
+    hipLaunchKernelGGL(decode_attn_splitk_kernel<false>, dim3(plan.n_waves), dim3(64), 0, stream,
+                       P.base, P.num_pages, P.hkv, layer, n_seq, plan.group, qws, page_table,
+                       page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
+  }
   return hipGetLastError();
 }
 
@@ -524,9 +761,8 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
                                 float* out, const void* workspace, const DecodePlan& plan,
                                 hipStream_t stream) {
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
-  const size_t acc_bytes = (ws_acc_bytes(n_seq, hkv, plan) + 255) & ~(size_t)255;
-  const float2* ws_ml =
-      reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) + acc_bytes);
+  const float2* ws_ml = reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) +
+                                                        ws_ml_offset(n_seq, hkv, plan));
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(n_q_heads, n_seq, kHeadDim / 32), dim3(256), 0, stream, ws_acc,
                      ws_ml, seq_lens, n_seq, hkv, plan.group, (int64_t)plan.n_waves, out);
   return hipGetLastError();
@@ -534,9 +770,11 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
 
 int decode_waves_per_cu() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_attn_splitk_kernel, 64, 0) != hipSuccess)
+  int other = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_attn_splitk_kernel<true>, 64, 0) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&other, decode_attn_splitk_kernel<false>, 64, 0) != hipSuccess)
     return 0;
-  return blocks;
+  return blocks < other ? blocks : other;
 }
 
 }  // namespace nvfp4kv

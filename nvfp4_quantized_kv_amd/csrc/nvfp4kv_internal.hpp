@@ -30,15 +30,22 @@ inline size_t ws_slots(int n_seq, int hkv, const DecodePlan& pl) {
   return (size_t)n_seq * hkv + (size_t)pl.n_waves;
 }
 
-// Workspace layout: partial accumulators [slot][group][128] floats, then the
-// running (max, sum) pairs [slot][group] as float2.
+// Workspace layout, each part 256-byte aligned: partial accumulators
+// [slot][group][128] floats; the (reference, sum) pairs [slot][group] as
+// float2; the quantized queries as QK^T operands, 4 KiB per (sequence, kv
+// head) segment.
+inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_acc_bytes(int n_seq, int hkv, const DecodePlan& pl) {
   return ws_slots(n_seq, hkv, pl) * pl.group * 128 * sizeof(float);
 }
+inline size_t ws_ml_offset(int n_seq, int hkv, const DecodePlan& pl) {
+  return ws_align(ws_acc_bytes(n_seq, hkv, pl));
+}
+inline size_t ws_q_offset(int n_seq, int hkv, const DecodePlan& pl) {
+  return ws_align(ws_ml_offset(n_seq, hkv, pl) + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float));
+}
 inline size_t ws_bytes(int n_seq, int hkv, const DecodePlan& pl) {
-  size_t a = ws_acc_bytes(n_seq, hkv, pl);
-  a = (a + 255) & ~(size_t)255;
-  return a + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float);
+  return ws_q_offset(n_seq, hkv, pl) + (size_t)n_seq * hkv * 4096;
 }
 
 // Resident one-wavefront decode workgroups per CU (0 if the query fails).
