@@ -2,8 +2,9 @@
 """Benchmark: NVFP4 decode attention over a paged NVFP4 KV cache on one MI355X.
 
 A step is the whole decode-time path for every layer of the workload: the
-fused append of each sequence's new token (RoPE, Hadamard-128, NVFP4 quantize,
-in-place write), the split-K decode attention kernel and the reduce kernel.
+split-K decode attention kernel, which also quantizes each sequence's new
+token into the cache in place (RoPE, Hadamard-128, NVFP4, no separate append
+pass), and the reduce kernel.
 The default workload is three concurrent sequences of 330K/400K/470K cached
 tokens, 16 layers, 24 query / 4 KV heads, head_dim 128, 64-token pages with a
 randomly permuted page table; all inputs are seeded synthetic data resident in
@@ -107,9 +108,8 @@ def cpu_baseline(step, wl, torch):
                                   pos, step.table_np, wl.seq_lens, W.sm_scale(), oc, os_)
     sec = time.perf_counter() - t0
     nbytes = ALGO_BYTES_PER_TOKEN_HEAD * wl.hkv * sum(wl.seq_lens)
-    # the same layer on the GPU, for a parity figure
-    step.append(0)
-    out = step.decode(0).clone()
+    # the same layer on the GPU (new token quantized by the decode kernel), for a parity figure
+    out = step.decode(0, fused=True).clone()
     torch.cuda.synchronize()
     err = float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max())
     return {
@@ -161,9 +161,8 @@ def main():
     i = 0
     for _ in range(args.steps):
         for layer in range(wl.layers):
-            step.append(layer)
             ev[i][0].record(stream)
-            step.decode_splits(layer)
+            step.decode_splits(layer, fused=True)
             ev[i][1].record(stream)
             step.decode_reduce(layer)
             i += 1
@@ -208,7 +207,7 @@ def main():
                         f"head_dim 128, 64-token pages, randomly permuted page table",
             "n_seq": wl.n_seq, "layers": wl.layers, "q_heads": wl.hq, "kv_heads": wl.hkv,
             "rotary_dim": wl.rotary_dim, "hadamard": wl.hadamard, "input_dtype": wl.dtype,
-            "step": "per layer: kv_quant_append + decode_attn_splitk + decode_reduce",
+            "step": "per layer: decode_attn_splitk (new token quantized in place) + decode_reduce",
             "pages_per_split": args.pages_per_split or "auto",
         },
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),

@@ -110,7 +110,7 @@ int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok,
                    hipStream_t stream);
 
 /* Workspace bytes nvfp4kv_decode_attn needs for this shape (split-K
- * partials and the quantized queries).  pages_per_split 0 selects the library's own split plan; the
+ * partials).  pages_per_split 0 selects the library's own split plan; the
  * same value must be passed to nvfp4kv_decode_attn.  Returns 0 on invalid
  * arguments. */
 size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
@@ -122,11 +122,18 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
  * rotation (when the pool has it), is quantized to NVFP4 and dequantized;
  * scores against the dequantized cached K of tokens 0 .. seq_lens[n]-1 are
  * scaled by sm_scale, softmax-normalized, and weight the dequantized V.
- * Three kernels: the queries are quantized once per (sequence, kv head);
- * the pages of all (sequence, kv head) pairs are split evenly over the
- * decode wavefronts, each writing partial results to the workspace; a
- * reduce kernel combines them.
+ * Two kernels: the pages of all (sequence, kv head) pairs are split evenly
+ * over the decode wavefronts, each writing partial results to the
+ * workspace (and quantizing the current token and the queries it needs);
+ * a reduce kernel combines them.
  *   q           [n_seq][n_q_heads][128], dtype q_dtype, before RoPE
+ *   k_new/v_new [n_seq][num_kv_heads][128], dtype q_dtype, before RoPE: the
+ *               current token's K and V, or both null.  When given, the
+ *               decode kernel quantizes them into the cache slot of token
+ *               seq_lens[n]-1 (RoPE at q_positions[n] and the rotation on K),
+ *               bit for bit as nvfp4kv_append would, before that slot's page
+ *               is read: the step needs no separate append.  Only that slot
+ *               is written.
  *   q_positions [n_seq] int32
  *   page_table  [n_seq][page_table_stride] int32 page ids; token t of
  *               sequence n sits in slot page_table[n][t/64]*64 + t%64
@@ -140,7 +147,8 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
  *   pages_per_split 0 = automatic, else 1..4096
  * n_q_heads / num_kv_heads must be an integer from 1 to 16. */
 int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
-                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const void* q, const void* k_new, const void* v_new,
+                        nvfp4kv_dtype q_dtype, const int32_t* q_positions,
                         const float* rope_cos, const float* rope_sin, int32_t max_pos,
                         const int32_t* page_table, int32_t page_table_stride,
                         const int32_t* seq_lens, int64_t max_seq_len, float sm_scale,
@@ -159,13 +167,14 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
  * weights 2^(s - m + 8) for the pair's tokens.  Layout, each part starting
  * at a 256-byte boundary: acc at float offset (slot * group + h) * 128 for
  * slots 0 .. n_seq*num_kv_heads + W - 1; the pairs (m, l) at float2 index
- * slot * group + h; then 4 KiB per segment of quantized queries (internal).
+ * slot * group + h.
  * Slots of pairs that do not overlap are not written.
  * nvfp4kv_decode_reduce reads them and writes out = sum_s 2^(m_s - M) acc_s
  * / sum_s 2^(m_s - M) l_s per (sequence, query head).  Both must get the
  * same n_seq, n_q_heads, max_seq_len and pages_per_split. */
 int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
-                               int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                               int32_t n_q_heads, const void* q, const void* k_new,
+                               const void* v_new, nvfp4kv_dtype q_dtype,
                                const int32_t* q_positions, const float* rope_cos,
                                const float* rope_sin, int32_t max_pos, const int32_t* page_table,
                                int32_t page_table_stride, const int32_t* seq_lens,

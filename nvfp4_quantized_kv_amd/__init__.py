@@ -57,11 +57,11 @@ def _load():
     L.nvfp4kv_append.restype = ctypes.c_int
     L.nvfp4kv_decode_workspace_bytes.argtypes = [PD, i32, i32, i64, i32]
     L.nvfp4kv_decode_workspace_bytes.restype = sz
-    L.nvfp4kv_decode_attn.argtypes = [PD, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P, i32, P,
-                                      i64, ctypes.c_float, P, P, sz, i32, P]
+    L.nvfp4kv_decode_attn.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32, P, i32,
+                                      P, i64, ctypes.c_float, P, P, sz, i32, P]
     L.nvfp4kv_decode_attn.restype = ctypes.c_int
-    L.nvfp4kv_decode_attn_splits.argtypes = [PD, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P,
-                                             i32, P, i64, ctypes.c_float, P, sz, i32, P]
+    L.nvfp4kv_decode_attn_splits.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32,
+                                             P, i32, P, i64, ctypes.c_float, P, sz, i32, P]
     L.nvfp4kv_decode_attn_splits.restype = ctypes.c_int
     L.nvfp4kv_decode_reduce.argtypes = [PD, i32, i32, P, i64, P, P, sz, i32, P]
     L.nvfp4kv_decode_reduce.restype = ctypes.c_int
@@ -177,6 +177,15 @@ def nvfp4kv_append(pool: Pool, layer: int, k: torch.Tensor, v: torch.Tensor, slo
                                _stream(stream)))
 
 
+def _check_new(q, k_new, v_new) -> None:
+    if k_new is None and v_new is None:
+        return
+    assert k_new is not None and v_new is not None, "k_new and v_new go together"
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    assert k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new/v_new take the dtype of q"
+    assert k_new.shape == v_new.shape and k_new.shape[0] == q.shape[0] and k_new.shape[2] == HEAD_DIM
+
+
 def nvfp4kv_decode_workspace_bytes(pool: Pool, n_seq: int, n_q_heads: int, max_seq_len: int,
                                    pages_per_split: int = 0) -> int:
     d = pool.desc()
@@ -189,9 +198,14 @@ def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: to
                         sm_scale: float, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, rope_cos: torch.Tensor | None = None,
                         rope_sin: torch.Tensor | None = None, pages_per_split: int = 0,
+                        k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
-    """Decode attention; q [n_seq][Hq][128] -> out [n_seq][Hq][128] float32."""
+    """Decode attention; q [n_seq][Hq][128] -> out [n_seq][Hq][128] float32.
+
+    With k_new/v_new [n_seq][Hkv][128] (same dtype as q) the current token is
+    quantized into the cache by the decode kernel itself (no separate append)."""
     assert q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    _check_new(q, k_new, v_new)
     assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     n_seq, n_q_heads, _ = q.shape
     if out is None:
@@ -202,7 +216,8 @@ def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: to
     max_pos = rope_cos.shape[0] if rope_cos is not None else 0
     d = pool.desc()
     _check("nvfp4kv_decode_attn",
-           _lib.nvfp4kv_decode_attn(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q), _dtype_code(q),
+           _lib.nvfp4kv_decode_attn(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q), _ptr(k_new),
+                                    _ptr(v_new), _dtype_code(q),
                                     _ptr(q_positions), _ptr(rope_cos), _ptr(rope_sin), max_pos,
                                     _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                                     int(max_seq_len), float(sm_scale), _ptr(out), _ptr(workspace),
@@ -216,15 +231,18 @@ def nvfp4kv_decode_attn_splits(pool: Pool, layer: int, q: torch.Tensor,
                                seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
                                workspace: torch.Tensor, rope_cos: torch.Tensor | None = None,
                                rope_sin: torch.Tensor | None = None, pages_per_split: int = 0,
-                               stream=None) -> None:
-    """First stage of decode attention: split partials into `workspace`."""
+                               k_new: torch.Tensor | None = None,
+                               v_new: torch.Tensor | None = None, stream=None) -> None:
+    """First stage of decode attention: split partials into `workspace` (and, with
+    k_new/v_new, the current token into the cache)."""
     assert q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    _check_new(q, k_new, v_new)
     n_seq, n_q_heads, _ = q.shape
     max_pos = rope_cos.shape[0] if rope_cos is not None else 0
     d = pool.desc()
     _check("nvfp4kv_decode_attn_splits",
            _lib.nvfp4kv_decode_attn_splits(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q),
-                                           _dtype_code(q), _ptr(q_positions), _ptr(rope_cos),
+                                           _ptr(k_new), _ptr(v_new), _dtype_code(q), _ptr(q_positions), _ptr(rope_cos),
                                            _ptr(rope_sin), max_pos, _ptr(page_table),
                                            page_table.shape[1], _ptr(seq_lens), int(max_seq_len),
                                            float(sm_scale), _ptr(workspace),

@@ -174,62 +174,110 @@ __device__ inline int64_t seq_pages(const int32_t* __restrict__ seq_lens, int s)
 // The wave whose range [w*TP/W, (w+1)*TP/W) holds flattened page index x.
 __device__ inline int64_t wave_of(int64_t x, int64_t TP, int64_t W) { return ((x + 1) * W - 1) / TP; }
 
-// Query prologue, once per (sequence, kv head) segment: RoPE, Hadamard and
-// the NVFP4 round trip of the group's query heads, written as the B
-// operands of QK^T: qws[(seg * 4 + c) * 64 + lane] holds, for lane (c16,
-// g4), dims 32*g4 + 8c .. +7 of the query head of column c16 (fp16, exact).
-// PACKED: columns 8-15 repeat heads 0-7.  Columns past the group are zero.
-template <bool PACKED>
-__global__ __launch_bounds__(64) void decode_q_prep_kernel(
-    int hkv, int n_q_heads, int group, const void* __restrict__ q, int q_dtype,
-    const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, int rotary_dim, int hadamard, h8* __restrict__ qws) {
-  __shared__ __attribute__((aligned(16))) _Float16 qhat[16 * kHeadDim];
-  const int seg = (int)blockIdx.x;
-  const int seq = seg / hkv, kvh = seg % hkv;
+// Inputs of one segment's query operands: the query rows of the group (up
+// to 4 heads per pass, one 16-lane group per head) and the lane's RoPE
+// coefficients at the segment's position (the same for every head).
+template <int kPasses>
+struct QIn {
+  float x[kPasses][8];
+  float cv[8], sv[8];
+};
+
+template <int kPasses>
+__device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, int group,
+                                              const void* __restrict__ q, int q_dtype,
+                                              const int32_t* __restrict__ q_positions,
+                                              const float* __restrict__ rope_cos,
+                                              const float* __restrict__ rope_sin, int rotary_dim,
+                                              QIn<kPasses>& in) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
-  for (int pass = 0; pass < (group + 3) / 4; ++pass) {
-    const int h = pass * 4 + g4;
-    const int hh = h < group ? h : group - 1;
-    const size_t off = ((size_t)seq * n_q_heads + (size_t)kvh * group + hh) * kHeadDim + 8 * c16;
-    float x[8];
-    if (q_dtype == 1) {
-      const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(q) + off);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+  const int seq = sg / hkv, kvh = sg % hkv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = __uint_as_float(u[i] << 16);
-        x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(q) + off);
-      const float4 a = p[0], b = p[1];
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-    const float* crow = nullptr;
-    const float* srow = nullptr;
-    if (rotary_dim > 0) {
-      const int pos = q_positions[seq];
-      crow = rope_cos + (size_t)pos * (rotary_dim / 2);
-      srow = rope_sin + (size_t)pos * (rotary_dim / 2);
-    }
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int h = min(pass * 4 + g4, group - 1);
+    load8(q, q_dtype, ((size_t)seq * n_q_heads + (size_t)kvh * group + h) * kHeadDim + 8 * c16,
+          in.x[pass]);
+  }
+  if (rotary_dim > 0) {
+    const int pos = q_positions[seq];
+    rope_coeffs(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
+                rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
+  }
+}
+
+// Query operands of one segment into an LDS slot: RoPE, Hadamard and the
+// NVFP4 round trip of the group's query heads (exact in fp16), laid out as
+// the B operands of QK^T: slot[c][lane] holds, for lane (c16, g4), dims
+// 32*g4 + 8c .. +7 of the query head of column c16.  PACKED: columns 8-15
+// repeat heads 0-7.  Columns past the group are zero.  `qrow` is an LDS
+// scratch of 16 x 128 halves.
+template <bool PACKED, int kPasses>
+__device__ __forceinline__ void make_q_operands(QIn<kPasses>& in, int group, int rotary_dim,
+                                                int hadamard, _Float16* qrow, h8 (*slot)[64]) {
+  const int lane = (int)threadIdx.x;
+  const int g4 = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass * 4 >= group) break;
+    const int h = pass * 4 + g4;
     uint32_t codes, scode;
-    quant_row16(x, c16, rotary_dim, crow, srow, hadamard != 0, codes, scode);
+    quant_row16_v(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0, codes, scode);
     const float s = e4m3_value(scode);
     h8 qv;
 #pragma unroll
     for (int k = 0; k < 8; ++k) qv[k] = (_Float16)(e2m1_value((codes >> (4 * k)) & 15u) * s);
-    if (h < group) *reinterpret_cast<h8*>(&qhat[h * kHeadDim + 8 * c16]) = qv;
+    if (h < group) *reinterpret_cast<h8*>(&qrow[h * kHeadDim + 8 * c16]) = qv;
   }
   __syncthreads();
   const int qcol = PACKED ? (c16 & 7) : c16;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    qws[((size_t)seg * 4 + c) * 64 + lane] =
-        (qcol < group) ? *reinterpret_cast<const h8*>(&qhat[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
+    slot[c][lane] = (qcol < group) ? *reinterpret_cast<const h8*>(&qrow[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
+  }
+  __syncthreads();
+}
+
+// The current token of segment sg (token seq_lens[seq] - 1) quantized into
+// its pool slot exactly as the append kernel does it: lanes 0-15 the K row
+// (RoPE at q_positions[seq], Hadamard), lanes 16-31 the V row; lanes 32-63
+// repeat the two rows (every lane takes part in the shuffles) and store
+// nothing.
+__device__ __forceinline__ void append_new_token(
+    int sg, uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer,
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int in_dtype,
+    const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int rotary_dim, int hadamard,
+    const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens) {
+  const int lane = (int)threadIdx.x;
+  const int c16 = lane & 15;
+  const int which = (lane >> 4) & 1;   // 0 = K, 1 = V
+  const int seq = sg / hkv, kvh = sg % hkv;
+  float x[8];
+  load8(which ? v_new : k_new, in_dtype, ((size_t)seq * hkv + kvh) * kHeadDim + 8 * c16, x);
+  const int rot = which ? 0 : rotary_dim;
+  const float* crow = nullptr;
+  const float* srow = nullptr;
+  if (rot > 0) {
+    const int pos = q_positions[seq];
+    crow = rope_cos + (size_t)pos * (rotary_dim / 2);
+    srow = rope_sin + (size_t)pos * (rotary_dim / 2);
+  }
+  uint32_t codes, scode;
+  quant_row16(x, c16, rot, crow, srow, which ? false : (hadamard != 0), codes, scode);
+  if (lane < 32) {
+    const int tok = seq_lens[seq] - 1;
+    const int page = page_table[(size_t)seq * pt_stride + tok / kPageSize];
+    const uint32_t t = (uint32_t)(tok % kPageSize);
+    uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + kvh) *
+                              (size_t)kBlockBytes;
+    *reinterpret_cast<uint32_t*>(blk + (which ? v_code_word_off(t, (uint32_t)c16)
+                                              : k_code_word_off(t, (uint32_t)c16))) = codes;
+    if ((c16 & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + c16 / 2] = (uint8_t)scode;
   }
 }
 
@@ -347,11 +395,9 @@ __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (
                              group, ws_acc, ws_ml, st);
 }
 
-// Query-operand slots in LDS per wave: the segments one wave covers in the
-// usual case (its range of about TP/W pages crosses at most one or two
-// segment boundaries).  A wave covering more segments reloads the last slot
-// at each further switch.
-constexpr int kQSlots = 3;
+// Query-operand slots in LDS per wave: the current segment's and the next
+// one's, which is made when its first page comes up.
+constexpr int kQSlots = 2;
 
 // Stream-K decode.  All (sequence, kv head, page) work is laid out flat:
 // segment g = seq * hkv + kvh holds that pair's pages, segments in order.
@@ -377,16 +423,21 @@ constexpr int kQSlots = 3;
 // readlane, so no scalar loads sit on its path.
 template <bool PACKED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_splitk_kernel(
-    const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int group,
-    const h8* __restrict__ qws, const int32_t* __restrict__ page_table, int pt_stride,
+    uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int n_q_heads,
+    int group, const void* __restrict__ q, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, int in_dtype, const int32_t* __restrict__ q_positions,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
+    int hadamard, const int32_t* __restrict__ page_table, int pt_stride,
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
   __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][4][64];
+  __shared__ __attribute__((aligned(16))) _Float16 qrow[16 * kHeadDim];
 
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4;     // lane group
   const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
+  __builtin_amdgcn_s_setprio(3);
   const int64_t W = gridDim.x, w = blockIdx.x;
   int64_t TP = 0;
   for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
@@ -447,27 +498,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return x < b && __builtin_amdgcn_readlane(w_j, (int)(x - win)) == 0;
   };
 
-  // segments of the range whose query operands are preloaded to LDS slots
-  // 0 .. nq-1 (slot k: segment seg0 + k)
-  int nq;
-  {
-    int sl = seq;
-    int64_t base = seq_base, pgl = pg;
-    while (b - 1 >= base + hkv * pgl) {
-      base += hkv * pgl;
-      ++sl;
-      pgl = seq_pages(seq_lens, sl);
+  // query inputs of the range's first segment, loaded before any page
+  constexpr int kPasses = PACKED ? 2 : 4;
+  QIn<kPasses> qin;
+  load_q_inputs<kPasses>(seg0, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos, rope_sin,
+                         rotary_dim, qin);
+
+  // ---- the current token of every segment whose last page is in the range
+  // goes into the cache first (only this wavefront reads that page), and
+  // the stores land before any page load below is issued
+  if (k_new != nullptr) {
+    int sq = seq, kv = kvh0;
+    int64_t sstart = seq_base + (int64_t)kvh0 * pg, pgl = pg;
+    bool any = false;
+    while (sstart < b) {
+      const int64_t last = sstart + pgl - 1;
+      if (pgl > 0 && last >= a && last < b) {
+        append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
+                         q_positions, rope_cos, rope_sin, rotary_dim, hadamard, page_table,
+                         pt_stride, seq_lens);
+        any = true;
+      }
+      sstart += pgl;
+      if (++kv == hkv) {
+        kv = 0;
+        if (++sq >= n_seq) break;
+        pgl = seq_pages(seq_lens, sq);
+      }
     }
-    const int seg_last = sl * hkv + (int)((b - 1 - base) / pgl);
-    nq = min(seg_last - seg0 + 1, kQSlots);
+    if (any) {
+      __builtin_amdgcn_s_waitcnt(0);
+      asm volatile("" ::: "memory");
+    }
   }
-  const int n_seg = n_seq * hkv;
-  h8 qpre[kQSlots][4];
-#pragma unroll
-  for (int k = 0; k < kQSlots; ++k)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qpre[k][c] = qws[((size_t)min(seg0 + k, n_seg - 1) * 4 + c) * 64 + lane];
 
   const int voff = 16 * lane;
   // Scale bytes are staged with their sign bits cleared.  Written scales are
@@ -487,23 +550,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   float l_run = 0.0f;
   SegState st{(size_t)seg0 + (size_t)w, 0};
   int seg_cur = seg0;
-  // query operands of the current segment from LDS; a wave that has used up
-  // its slots loads the next segment's into the last one
+  // query operands of the current segment from LDS
   auto q_of = [&](h8 (&qb)[4]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[c] = q_lds[min(st.qslot, kQSlots - 1)][c][lane];
+    for (int c = 0; c < 4; ++c) qb[c] = q_lds[st.qslot & 1][c][lane];
   };
   // a page that starts a new segment is coming: its query operands go to
-  // their slot unless they were preloaded (the last slot is free by then:
-  // the finishing segment has no QK^T left)
+  // the other slot (the finishing segment has no QK^T left)
   auto prepare_switch = [&]() {
     ++seg_cur;
-    const int k = st.qslot + 1;
-    if (k >= nq) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        q_lds[min(k, kQSlots - 1)][c][lane] = qws[((size_t)seg_cur * 4 + c) * 64 + lane];
-    }
+    QIn<kPasses> in;
+    load_q_inputs<kPasses>(seg_cur, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
+                           rope_sin, rotary_dim, in);
+    make_q_operands<PACKED, kPasses>(in, group, rotary_dim, hadamard, qrow, q_lds[(st.qslot + 1) & 1]);
   };
 
   // ---- prologue: loads of the range's first two pages; unit 0's scores and
@@ -532,10 +591,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     vB[1] = ld16(r1, voff, kVCodeOff + 1024);
     __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int k = 0; k < kQSlots; ++k)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q_lds[k][c][lane] = qpre[k][c];
+  // query operands of the first segment, while the first pages load
+  make_q_operands<PACKED, kPasses>(qin, group, rotary_dim, hadamard, qrow, q_lds[0]);
   f4 S[2];
   h8 pw0, pw1, qb[4];
   {
@@ -557,7 +614,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // is staged in LDS buffer 0, page p+1 in buffer 1.
   const uint8_t* sb0 = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
   const uint8_t* sb1 = reinterpret_cast<const uint8_t*>(&sc_lds[1][0]);
+  // Issue priority by progress.  Two wavefronts share each SIMD and, at
+  // equal priority, the older one is issued first, so it would finish its
+  // (equal) range long before the younger one, which then runs alone at a
+  // lower issue rate.  Dropping the priority as the range is worked off
+  // (below 50 % done: 3, then 2, 1 from 75 %, 0 from 90 %) hands the issue
+  // slots to whichever wavefront is behind.
+  const int64_t t50 = a + (b - a) / 2, t75 = a + 3 * (b - a) / 4, t90 = a + 9 * (b - a) / 10;
+  int prio_level = 0;
   for (int64_t p = a; p < b; p += 2) {
+    {
+      const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
+      if (lv != prio_level) {
+        prio_level = lv;
+        if (lv == 1) __builtin_amdgcn_s_setprio(2);
+        else if (lv == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    }
     if (min(p + 4, b - 1) - win >= 64) {   // ranges of more than 64 pages
       const int o = (int)(p - win);
       const int sg = __builtin_amdgcn_readlane(w_sg, o);
@@ -588,7 +662,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       h8 qn[4];
       const int s = st.qslot + (sw1 ? 1 : 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qn[c] = q_lds[min(s, kQSlots - 1)][c][lane];
+      for (int c = 0; c < 4; ++c) qn[c] = q_lds[s & 1][c][lane];
       qk_unit(kB[0], kB[1], sb1 + sk_off, qn, S);
     }
     kB[0] = ld16(r3, voff, 0);
@@ -619,7 +693,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       h8 qn[4];
       const int s = st.qslot + (sw2 ? 1 : 0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qn[c] = q_lds[min(s, kQSlots - 1)][c][lane];
+      for (int c = 0; c < 4; ++c) qn[c] = q_lds[s & 1][c][lane];
       qk_unit(kA[0], kA[1], sb0 + sk_off, qn, S);
     }
     kA[0] = ld16(r4, voff, 0);
@@ -728,32 +802,20 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 }  // namespace
 
 hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
-                                const void* q, int q_dtype, const int32_t* q_positions,
-                                const float* rope_cos, const float* rope_sin,
-                                const int32_t* page_table, int page_table_stride,
-                                const int32_t* seq_lens, float sm_scale, void* workspace,
-                                const DecodePlan& plan, hipStream_t stream) {
+                                const void* q, const void* k_new, const void* v_new, int in_dtype,
+                                const int32_t* q_positions, const float* rope_cos,
+                                const float* rope_sin, const int32_t* page_table,
+                                int page_table_stride, const int32_t* seq_lens, float sm_scale,
+                                void* workspace, const DecodePlan& plan, hipStream_t stream) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   float* ws_acc = reinterpret_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(ws + ws_ml_offset(n_seq, P.hkv, plan));
-  h8* qws = reinterpret_cast<h8*>(ws + ws_q_offset(n_seq, P.hkv, plan));
   const float c_log2 = sm_scale * 1.4426950408889634f;
-  const int n_seg = n_seq * P.hkv;
-  if (plan.group <= 8) {
-    hipLaunchKernelGGL(decode_q_prep_kernel<true>, dim3(n_seg), dim3(64), 0, stream, P.hkv, n_q_heads,
-                       plan.group, q, q_dtype, q_positions, rope_cos, rope_sin, P.rotary_dim,
-                       P.hadamard, qws);
-    hipLaunchKernelGGL(decode_attn_splitk_kernel<true>, dim3(plan.n_waves), dim3(64), 0, stream,
-                       P.base, P.num_pages, P.hkv, layer, n_seq, plan.group, qws, page_table,
-                       page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
-  } else {
-    hipLaunchKernelGGL(decode_q_prep_kernel<false>, dim3(n_seg), dim3(64), 0, stream, P.hkv, n_q_heads,
-                       plan.group, q, q_dtype, q_positions, rope_cos, rope_sin, P.rotary_dim,
-                       P.hadamard, qws);
-    hipLaunchKernelGGL(decode_attn_splitk_kernel<false>, dim3(plan.n_waves), dim3(64), 0, stream,
-                       P.base, P.num_pages, P.hkv, layer, n_seq, plan.group, qws, page_table,
-                       page_table_stride, seq_lens, c_log2, ws_acc, ws_ml);
-  }
+  auto kern = plan.group <= 8 ? decode_attn_splitk_kernel<true> : decode_attn_splitk_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(plan.n_waves), dim3(64), 0, stream, P.base, P.num_pages, P.hkv,
+                     layer, n_seq, n_q_heads, plan.group, q, k_new, v_new, in_dtype, q_positions,
+                     rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table, page_table_stride,
+                     seq_lens, c_log2, ws_acc, ws_ml);
   return hipGetLastError();
 }
 

@@ -17,23 +17,6 @@ namespace nvfp4kv {
 
 namespace {
 
-__device__ inline void load8(const void* src, int dtype, size_t elem_off, float (&x)[8]) {
-  if (dtype == 1) {  // bf16
-    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + elem_off);
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(u[i] << 16);
-      x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-    }
-  } else {
-    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + elem_off);
-    const float4 a = p[0], b = p[1];
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
-
 // Rows are ordered (token, kv head, K|V) so that the 4 rows of a wavefront
 // read neighbouring input rows.
 __global__ __launch_bounds__(256) void kv_quant_append_kernel(

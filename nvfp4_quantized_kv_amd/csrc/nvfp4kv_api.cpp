@@ -207,7 +207,8 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
 
 // Checks shared by the decode entry points; fills `plan`.
 static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
-                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const void* q, const void* k_new, const void* v_new,
+                        nvfp4kv_dtype q_dtype, const int32_t* q_positions,
                         const float* rope_cos, const float* rope_sin, int32_t max_pos,
                         const int32_t* page_table, int32_t page_table_stride,
                         const int32_t* seq_lens, int64_t max_seq_len, float sm_scale,
@@ -221,6 +222,10 @@ static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr)
     return fail(NVFP4KV_ERR_INVALID_ARG, "null q, page_table or seq_lens");
   if (!aligned(q, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(NVFP4KV_ERR_INVALID_ARG, "k_new and v_new must both be given or both be null");
+  if (k_new != nullptr && (!aligned(k_new, 16) || !aligned(v_new, 16)))
+    return fail(NVFP4KV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   if (p->rotary_dim > 0 && q_positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs q_positions");
   if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
   const int64_t max_pages = (max_seq_len + 63) / 64;
@@ -231,7 +236,8 @@ static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
 }
 
 int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
-                               int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                               int32_t n_q_heads, const void* q, const void* k_new,
+                               const void* v_new, nvfp4kv_dtype q_dtype,
                                const int32_t* q_positions, const float* rope_cos,
                                const float* rope_sin, int32_t max_pos, const int32_t* page_table,
                                int32_t page_table_stride, const int32_t* seq_lens,
@@ -239,12 +245,12 @@ int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_s
                                size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream) {
   g_last_error.clear();
   nvfp4kv::DecodePlan plan;
-  int rc = check_decode(p, layer, n_seq, n_q_heads, q, q_dtype, q_positions, rope_cos, rope_sin,
+  int rc = check_decode(p, layer, n_seq, n_q_heads, q, k_new, v_new, q_dtype, q_positions, rope_cos, rope_sin,
                         max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
                         workspace, workspace_bytes, pages_per_split, &plan);
   if (rc != NVFP4KV_OK) return rc;
-  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q,
-                                               (int)q_dtype, q_positions, rope_cos, rope_sin,
+  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
+                                               v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
                                                workspace, plan, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
@@ -270,7 +276,8 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
 }
 
 int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
-                        const void* q, nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                        const void* q, const void* k_new, const void* v_new,
+                        nvfp4kv_dtype q_dtype, const int32_t* q_positions,
                         const float* rope_cos, const float* rope_sin, int32_t max_pos,
                         const int32_t* page_table, int32_t page_table_stride,
                         const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, float* out,
@@ -278,14 +285,14 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                         hipStream_t stream) {
   g_last_error.clear();
   nvfp4kv::DecodePlan plan;
-  int rc = check_decode(p, layer, n_seq, n_q_heads, q, q_dtype, q_positions, rope_cos, rope_sin,
+  int rc = check_decode(p, layer, n_seq, n_q_heads, q, k_new, v_new, q_dtype, q_positions, rope_cos, rope_sin,
                         max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
                         workspace, workspace_bytes, pages_per_split, &plan);
   if (rc != NVFP4KV_OK) return rc;
   if (out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null out");
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
-  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q,
-                                               (int)q_dtype, q_positions, rope_cos, rope_sin,
+  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
+                                               v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
                                                workspace, plan, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");

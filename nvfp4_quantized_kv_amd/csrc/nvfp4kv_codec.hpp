@@ -84,21 +84,58 @@ __host__ __device__ inline float e2m1_value(uint32_t nib) {
   return (nib & 8u) ? -mag : mag;
 }
 
+// Elements elem_off .. +7 of a bf16 (dtype 1) or f32 (dtype 0) array as floats,
+// with one 16-byte load (bf16) or two (f32).
+__device__ inline void load8(const void* src, int dtype, size_t elem_off, float (&x)[8]) {
+  if (dtype == 1) {  // bf16
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + elem_off);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(u[i] << 16);
+      x[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + elem_off);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+// RoPE coefficients of a lane's 8 elements for quant_row16_v: lane r of a
+// row covers elements 8r .. 8r+7; in the first half of the rotary part (i <
+// R/2) it needs cos/sin of pair i, in the second half those of pair i - R/2,
+// beyond the rotary part nothing (zeros are returned, and not used).
+__device__ inline void rope_coeffs(int r, int rotary_dim, const float* cos_row, const float* sin_row,
+                                   float (&cv)[8], float (&sv)[8]) {
+  const int half = rotary_dim / 2;          // a multiple of 8
+  const int hl = half / 8;                  // lanes per half
+  const bool in_rot = r < 2 * hl;
+  const int base = in_rot ? (r < hl ? 8 * r : 8 * r - half) : 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    cv[k] = in_rot ? cos_row[base + k] : 0.0f;
+    sv[k] = in_rot ? sin_row[base + k] : 0.0f;
+  }
+}
+
 // Quantize one 128-element row held by the 16 lanes of a lane group.  `x`
-// holds elements 8r .. 8r+7 of the row, r = lane % 16.  On return `x` holds
-// the rotated (RoPE'd, Hadamard'd) floats, `codes` the lane's 8 E2M1 codes
-// (element 8r+k in bits 4k..4k+3) and `scode` the E4M3 code of the lane's
-// block (elements 16(r/2) .. 16(r/2)+15).  All 64 lanes of the wavefront must
-// call it together (it uses cross-lane shuffles).
-__device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
-                                   const float* sin_row, bool hadamard, uint32_t& codes,
-                                   uint32_t& scode) {
+// holds elements 8r .. 8r+7 of the row, r = lane % 16; `cv`/`sv` the lane's
+// RoPE coefficients from rope_coeffs (unused when rotary_dim is 0).  On
+// return `x` holds the rotated (RoPE'd, Hadamard'd) floats, `codes` the
+// lane's 8 E2M1 codes (element 8r+k in bits 4k..4k+3) and `scode` the E4M3
+// code of the lane's block (elements 16(r/2) .. 16(r/2)+15).  All 64 lanes of
+// the wavefront must call it together (it uses cross-lane shuffles).
+__device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const float (&cv)[8],
+                                     const float (&sv)[8], bool hadamard, uint32_t& codes,
+                                     uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
   // RoPE, rotate-half pairs (i, i + R/2) on the first R dims.
   if (rotary_dim > 0) {
-    const int half = rotary_dim / 2;          // a multiple of 8
-    const int hl = half / 8;                  // lanes per half
+    const int half = rotary_dim / 2;
+    const int hl = half / 8;
     const bool first = r < hl;
     const bool second = (r >= hl) && (r < 2 * hl);
     const int src = first ? r + hl : (second ? r - hl : r);
@@ -107,16 +144,12 @@ __device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const f
     for (int k = 0; k < 8; ++k) {
       const float other = __shfl(x[k], src_lane, 64);
       if (first) {
-        const int i = 8 * r + k;
-        const float c = cos_row[i], s = sin_row[i];
-        const float ac = x[k] * c;
-        const float bs = other * s;
+        const float ac = x[k] * cv[k];
+        const float bs = other * sv[k];
         x[k] = ac - bs;
       } else if (second) {
-        const int i = 8 * r + k - half;
-        const float c = cos_row[i], s = sin_row[i];
-        const float bc = x[k] * c;
-        const float as = other * s;
+        const float bc = x[k] * cv[k];
+        const float as = other * sv[k];
         x[k] = bc + as;
       }
     }
@@ -157,6 +190,20 @@ __device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const f
 #pragma unroll
   for (int k = 0; k < 8; ++k) w |= e2m1_code(x[k], s) << (4 * k);
   codes = w;
+}
+
+// quant_row16_v with the RoPE coefficients read from the table rows.
+__device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
+                                   const float* sin_row, bool hadamard, uint32_t& codes,
+                                   uint32_t& scode) {
+  float cv[8], sv[8];
+  if (rotary_dim > 0) {
+    rope_coeffs(r, rotary_dim, cos_row, sin_row, cv, sv);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) cv[k] = sv[k] = 0.0f;
+  }
+  quant_row16_v(x, r, rotary_dim, cv, sv, hadamard, codes, scode);
 }
 
 }  // namespace nvfp4kv

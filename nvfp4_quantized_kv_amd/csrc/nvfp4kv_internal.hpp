@@ -30,10 +30,9 @@ inline size_t ws_slots(int n_seq, int hkv, const DecodePlan& pl) {
   return (size_t)n_seq * hkv + (size_t)pl.n_waves;
 }
 
-// Workspace layout, each part 256-byte aligned: partial accumulators
-// [slot][group][128] floats; the (reference, sum) pairs [slot][group] as
-// float2; the quantized queries as QK^T operands, 4 KiB per (sequence, kv
-// head) segment.
+// Workspace layout: partial accumulators [slot][group][128] floats, then
+// (at the next 256-byte boundary) the (reference, sum) pairs [slot][group]
+// as float2.
 inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t ws_acc_bytes(int n_seq, int hkv, const DecodePlan& pl) {
   return ws_slots(n_seq, hkv, pl) * pl.group * 128 * sizeof(float);
@@ -41,11 +40,8 @@ inline size_t ws_acc_bytes(int n_seq, int hkv, const DecodePlan& pl) {
 inline size_t ws_ml_offset(int n_seq, int hkv, const DecodePlan& pl) {
   return ws_align(ws_acc_bytes(n_seq, hkv, pl));
 }
-inline size_t ws_q_offset(int n_seq, int hkv, const DecodePlan& pl) {
-  return ws_align(ws_ml_offset(n_seq, hkv, pl) + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float));
-}
 inline size_t ws_bytes(int n_seq, int hkv, const DecodePlan& pl) {
-  return ws_q_offset(n_seq, hkv, pl) + (size_t)n_seq * hkv * 4096;
+  return ws_ml_offset(n_seq, hkv, pl) + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float);
 }
 
 // Resident one-wavefront decode workgroups per CU (0 if the query fails).
@@ -59,11 +55,11 @@ hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64
                           void* k_out, void* v_out, int dtype, int unrotate, hipStream_t stream);
 
 hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
-                                const void* q, int q_dtype, const int32_t* q_positions,
-                                const float* rope_cos, const float* rope_sin,
-                                const int32_t* page_table, int page_table_stride,
-                                const int32_t* seq_lens, float sm_scale, void* workspace,
-                                const DecodePlan& plan, hipStream_t stream);
+                                const void* q, const void* k_new, const void* v_new, int in_dtype,
+                                const int32_t* q_positions, const float* rope_cos,
+                                const float* rope_sin, const int32_t* page_table,
+                                int page_table_stride, const int32_t* seq_lens, float sm_scale,
+                                void* workspace, const DecodePlan& plan, hipStream_t stream);
 
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,

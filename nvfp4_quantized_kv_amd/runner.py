@@ -1,9 +1,10 @@
 """Drive the library on a named workload: fill the pool, run decode steps.
 
-A decode step is, for every layer: append the new token of every sequence
-(nvfp4kv_append), then decode attention for every sequence
-(nvfp4kv_decode_attn).  Inputs come from `workloads`; every computation runs
-in the HIP library.
+A decode step is, for every layer, decode attention for every sequence with
+the new token's K and V handed to the decode kernel, which quantizes them into
+the cache itself (nvfp4kv_decode_attn with k_new/v_new).  The unfused form,
+nvfp4kv_append followed by nvfp4kv_decode_attn, is kept for comparison.
+Inputs come from `workloads`; every computation runs in the HIP library.
 """
 from __future__ import annotations
 
@@ -77,25 +78,32 @@ class DecodeStep:
         nvfp4kv_append(self.pool, layer, self.k_new[layer], self.v_new[layer], self.new_slots,
                        self.new_pos, self.rope_cos, self.rope_sin)
 
-    def decode(self, layer: int, out=None) -> torch.Tensor:
+    def decode(self, layer: int, out=None, fused: bool = False) -> torch.Tensor:
+        """Decode attention of `layer`; fused=True also quantizes the new token
+        into the cache (no append needed before it)."""
         return nvfp4kv_decode_attn(self.pool, layer, self.q[layer], self.new_pos, self.table,
                                    self.seq_lens, self.wl.max_seq_len, W.sm_scale(),
                                    out=self.out if out is None else out, workspace=self.workspace,
                                    rope_cos=self.rope_cos, rope_sin=self.rope_sin,
-                                   pages_per_split=self.pages_per_split)
+                                   pages_per_split=self.pages_per_split,
+                                   k_new=self.k_new[layer] if fused else None,
+                                   v_new=self.v_new[layer] if fused else None)
 
-    def decode_splits(self, layer: int) -> None:
+    def decode_splits(self, layer: int, fused: bool = False) -> None:
         nvfp4kv_decode_attn_splits(self.pool, layer, self.q[layer], self.new_pos, self.table,
                                    self.seq_lens, self.wl.max_seq_len, W.sm_scale(), self.workspace,
                                    rope_cos=self.rope_cos, rope_sin=self.rope_sin,
-                                   pages_per_split=self.pages_per_split)
+                                   pages_per_split=self.pages_per_split,
+                                   k_new=self.k_new[layer] if fused else None,
+                                   v_new=self.v_new[layer] if fused else None)
 
     def decode_reduce(self, layer: int, out=None) -> torch.Tensor:
         return nvfp4kv_decode_reduce(self.pool, self.wl.n_seq, self.wl.hq, self.seq_lens,
                                      self.wl.max_seq_len, self.out if out is None else out,
                                      self.workspace, pages_per_split=self.pages_per_split)
 
-    def run(self) -> None:
+    def run(self, fused: bool = True) -> None:
         for layer in range(self.wl.layers):
-            self.append(layer)
-            self.decode(layer)
+            if not fused:
+                self.append(layer)
+            self.decode(layer, fused=fused)

@@ -97,9 +97,10 @@ def test_append_rejects_bad_arguments(kv):
 
 
 def _decode(kv, d, n_seq=2, hq=24, q=4096, pt=4096, stride=100, lens=4096, max_len=6000,
-            scale=0.1, out=4096, ws=4096, ws_bytes=1 << 30, pps=0, qpos=4096):
-    return kv.lib().nvfp4kv_decode_attn(ctypes.byref(d), 0, n_seq, hq, q, 1, qpos, 4096, 4096, 10,
-                                        pt, stride, lens, max_len, scale, out, ws, ws_bytes, pps, None)
+            scale=0.1, out=4096, ws=4096, ws_bytes=1 << 30, pps=0, qpos=4096, k_new=None, v_new=None):
+    return kv.lib().nvfp4kv_decode_attn(ctypes.byref(d), 0, n_seq, hq, q, k_new, v_new, 1, qpos, 4096,
+                                        4096, 10, pt, stride, lens, max_len, scale, out, ws, ws_bytes,
+                                        pps, None)
 
 
 def test_decode_rejects_bad_arguments(kv):
@@ -118,6 +119,10 @@ def test_decode_rejects_bad_arguments(kv):
     assert _decode(kv, d, ws=None) == -3
     assert _decode(kv, d, ws=4100) == -3
     assert "workspace" in kv.nvfp4kv_last_error()
+    assert _decode(kv, d, k_new=4096) == -1           # k_new without v_new
+    assert _decode(kv, d, v_new=4096) == -1
+    assert _decode(kv, d, k_new=4100, v_new=4096) == -1   # misaligned
+    assert "k_new" in kv.nvfp4kv_last_error()
 
 
 def test_workspace_size_query(kv):

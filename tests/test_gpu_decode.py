@@ -36,7 +36,7 @@ class Case:
 
     def __init__(self, seed, lens, hkv, hq, rotary=32, hadamard=True, pos_scale=1.0,
                  dtype=torch.bfloat16, outliers=3, outlier_scale=16.0, extra_pages=3,
-                 student_t=False):
+                 student_t=False, hold_last=False):
         import nvfp4_quantized_kv_amd as kv
         self.kv = kv
         rng = np.random.default_rng(seed)
@@ -75,19 +75,33 @@ class Case:
             k, v = draw(T, hkv, 128), draw(T, hkv, 128)
             self.k.append(k)
             self.v.append(v)
-            pos = np.arange(T)
+            # hold_last: the current token (the last) is left for the decode
+            # call to quantize into the cache itself
+            pos = np.arange(T - 1 if hold_last else T)
+            if len(pos) == 0:
+                continue
             sl = self.table[n, pos // 64].astype(np.int64) * 64 + pos % 64
-            kv.nvfp4kv_append(self.pool, 0, k.cuda(), v.cuda(), torch.from_numpy(sl).cuda(),
-                              torch.from_numpy(pos.astype(np.int32)).cuda(), self.rc, self.rs)
+            kv.nvfp4kv_append(self.pool, 0, k[:len(pos)].contiguous().cuda(), v[:len(pos)].contiguous().cuda(),
+                              torch.from_numpy(sl).cuda(), torch.from_numpy(pos.astype(np.int32)).cuda(),
+                              self.rc, self.rs)
         self.q = draw(len(lens), hq, 128)
         self.q_pos = np.array([T - 1 for T in lens], np.int32)
 
-    def gpu(self, pages_per_split=0, sm_scale=1 / np.sqrt(128)):
+    def new_token_rows(self):
+        """The current token's K and V, [n_seq][hkv][128]."""
+        k = torch.stack([x[-1] for x in self.k]).contiguous()
+        v = torch.stack([x[-1] for x in self.v]).contiguous()
+        return k, v
+
+    def gpu(self, pages_per_split=0, sm_scale=1 / np.sqrt(128), fused=False):
+        k_new = v_new = None
+        if fused:
+            k_new, v_new = (x.cuda() for x in self.new_token_rows())
         out = self.kv.nvfp4kv_decode_attn(
             self.pool, 0, self.q.cuda(), torch.from_numpy(self.q_pos).cuda(),
             torch.from_numpy(self.table).cuda(), torch.tensor(self.lens, dtype=torch.int32).cuda(),
             max(self.lens), sm_scale, rope_cos=self.rc, rope_sin=self.rs,
-            pages_per_split=pages_per_split)
+            pages_per_split=pages_per_split, k_new=k_new, v_new=v_new)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
@@ -169,3 +183,48 @@ def test_decode_page_permutation_invariance():
                                    torch.tensor(a.lens, dtype=torch.int32).cuda(), 3000, 1 / np.sqrt(128),
                                    rope_cos=a.rc, rope_sin=a.rs).cpu().numpy()
     assert np.abs(a.gpu() - b_out).max() <= 1e-5 * max(1.0, np.abs(b_out).max())
+
+
+FUSED_CASES = [
+    dict(lens=[1]),                                   # empty cache before the step
+    dict(lens=[64]),                                  # new token in the last slot of a page
+    dict(lens=[65], rotary=0, hadamard=False),        # new token opens a page
+    dict(lens=[1000, 3, 2049, 777], dtype=torch.float32),
+    dict(lens=[700, 1500], hq=32, rotary=16),         # 16 query heads per kv head
+    dict(lens=[3000, 1234], rotary=128, pos_scale=2.3),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(FUSED_CASES)))
+@pytest.mark.parametrize("pages_per_split", [0, 1, 4096])
+def test_decode_quantizes_current_token_in_place(idx, pages_per_split):
+    """Decode with k_new/v_new on a cache missing the current token == append
+    of the token + decode: the pool bytes bit for bit (the whole pool, so no
+    other slot is touched) and the attention output exactly; both within the
+    oracle's tolerance.  pages_per_split 1 puts a token's page first in a
+    wavefront's range, 4096 gives one wavefront many segments (appends and
+    query switches past the preloaded slots)."""
+    kw = dict(FUSED_CASES[idx])
+    lens = kw.pop("lens")
+    hq = kw.pop("hq", 8)
+    full = Case(300 + idx, lens, 2, hq, **kw)
+    held = Case(300 + idx, lens, 2, hq, hold_last=True, **kw)
+    out_full = full.gpu(pages_per_split=pages_per_split)
+    out_fused = held.gpu(pages_per_split=pages_per_split, fused=True)
+    assert torch.equal(held.pool.data, full.pool.data), "pool bytes differ from append + decode"
+    assert np.array_equal(out_fused, out_full), "output differs from append + decode"
+    assert_attention_close(out_fused, held.oracle(), f"fused {lens}")
+
+
+def test_decode_quantizes_current_token_many_segments_one_wave():
+    """16 (sequence, kv head) segments of 1 to 3 pages in one wavefront's
+    range: every segment end appends its token, every segment switch makes
+    its own query operands."""
+    lens = [5, 70, 130, 1]
+    full = Case(400, lens, 4, 8)
+    held = Case(400, lens, 4, 8, hold_last=True)
+    out_full = full.gpu(pages_per_split=4096)
+    out_fused = held.gpu(pages_per_split=4096, fused=True)
+    assert torch.equal(held.pool.data, full.pool.data)
+    assert np.array_equal(out_fused, out_full)
+    assert_attention_close(out_fused, held.oracle(), "many segments")
