@@ -310,10 +310,9 @@ __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, f
   }
 }
 
-// Where a finished segment's partial goes and which slot comes next.
+// Where a finished segment's partial goes.
 struct SegState {
   size_t slot;        // partial slot of the current segment (segment + wave)
-  int qslot;          // LDS slot of the current segment's query operands
 };
 
 // Online softmax of one unit with the segment switch folded into its rare
@@ -337,7 +336,6 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
     if (sw) {
       write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
       st.slot += 1;
-      st.qslot += 1;
       m_ref = -INFINITY;
       l_run = 0.0f;
     }
@@ -395,9 +393,10 @@ __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (
                              group, ws_acc, ws_ml, st);
 }
 
-// Query-operand slots in LDS per wave: the current segment's and the next
-// one's, which is made when its first page comes up.
-constexpr int kQSlots = 2;
+// Query-operand slots in LDS per wave: segment s of the range uses slot
+// (s - first segment) % 3, enough for the (at most three) segments one trip
+// of the page loop touches.
+constexpr int kQSlots = 3;
 
 // Stream-K decode.  All (sequence, kv head, page) work is laid out flat:
 // segment g = seq * hkv + kvh holds that pair's pages, segments in order.
@@ -548,22 +547,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   for (int j = 0; j < 8; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;
   float l_run = 0.0f;
-  SegState st{(size_t)seg0 + (size_t)w, 0};
-  int seg_cur = seg0;
-  // query operands of the current segment from LDS
-  auto q_of = [&](h8 (&qb)[4]) {
+  SegState st{(size_t)seg0 + (size_t)w};
+  int q_ready = seg0;   // last segment whose query operands are in LDS
+  // query operands of a segment from its LDS slot
+  auto q_of = [&](int sg, h8 (&qb)[4]) {
+    const int sl = (sg - seg0) % kQSlots;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[c] = q_lds[st.qslot & 1][c][lane];
+    for (int c = 0; c < 4; ++c) qb[c] = q_lds[sl][c][lane];
   };
-  // a page that starts a new segment is coming: its query operands go to
-  // the other slot (the finishing segment has no QK^T left)
-  auto prepare_switch = [&]() {
-    ++seg_cur;
-    QIn<kPasses> in;
-    load_q_inputs<kPasses>(seg_cur, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
-                           rope_sin, rotary_dim, in);
-    make_q_operands<PACKED, kPasses>(in, group, rotary_dim, hadamard, qrow, q_lds[(st.qslot + 1) & 1]);
-  };
+  auto seg_of = [&](int64_t x) { return __builtin_amdgcn_readlane(w_sg, (int)(min(x, b - 1) - win)); };
 
   // ---- prologue: loads of the range's first two pages; unit 0's scores and
   // weights; the loads left in flight and their order are those of the
@@ -599,7 +591,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r2, voff, kKScaleOff);
-    q_of(qb);
+    q_of(seg0, qb);
     qk_unit(kA[0], kA[1], reinterpret_cast<const uint8_t*>(&sc_lds[0][0]) + sk_off, qb, S);
     kA[0] = ld16(r2, voff, 0);
     kA[1] = ld16(r2, voff, 1024);
@@ -642,9 +634,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const __amdgpu_buffer_rsrc_t r2 = rsrc_of(p + 2), r3 = rsrc_of(p + 3), r4 = rsrc_of(p + 4);
     const int nv0 = nvalid_of(p), nv1 = nvalid_of(p + 1), nv2 = nvalid_of(p + 2);
     const bool sw1 = starts_segment(p + 1), sw2 = starts_segment(p + 2);
+    const int sg0 = seg_of(p), sg1 = seg_of(p + 1), sg2 = seg_of(p + 2);
+    // query operands of segments that start in this trip (rare: a range
+    // crosses few segment boundaries)
+    while (q_ready < sg2) {
+      ++q_ready;
+      QIn<kPasses> in;
+      load_q_inputs<kPasses>(q_ready, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
+                             rope_sin, rotary_dim, in);
+      make_q_operands<PACKED, kPasses>(in, group, rotary_dim, hadamard, qrow,
+                                       q_lds[(q_ready - seg0) % kQSlots]);
+    }
 
     // page p, tokens 32..63 scored, 0..31 accumulated
-    q_of(qb);
+    q_of(sg0, qb);
     qk_unit(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
     kA[2] = ld16(r2, voff, 2048);
     kA[3] = ld16(r2, voff, 3072);
@@ -657,14 +660,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // page p+1 staged; its tokens 0..31 scored, page p's 32..63 accumulated
     sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
     sB = ld16(r3, voff, kKScaleOff);
-    if (sw1) prepare_switch();
-    {
-      h8 qn[4];
-      const int s = st.qslot + (sw1 ? 1 : 0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qn[c] = q_lds[s & 1][c][lane];
-      qk_unit(kB[0], kB[1], sb1 + sk_off, qn, S);
-    }
+    q_of(sg1, qb);
+    qk_unit(kB[0], kB[1], sb1 + sk_off, qb, S);
     kB[0] = ld16(r3, voff, 0);
     kB[1] = ld16(r3, voff, 1024);
     pv_unit<PACKED>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
@@ -675,7 +672,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     if (p + 1 >= b) break;
 
     // page p+1, tokens 32..63 scored, 0..31 accumulated
-    q_of(qb);
+    q_of(sg1, qb);
     qk_unit(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
     kB[2] = ld16(r3, voff, 2048);
     kB[3] = ld16(r3, voff, 3072);
@@ -688,14 +685,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // page p+2 staged; its tokens 0..31 scored, page p+1's 32..63 accumulated
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r4, voff, kKScaleOff);
-    if (sw2) prepare_switch();
-    {
-      h8 qn[4];
-      const int s = st.qslot + (sw2 ? 1 : 0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qn[c] = q_lds[s & 1][c][lane];
-      qk_unit(kA[0], kA[1], sb0 + sk_off, qn, S);
-    }
+    q_of(sg2, qb);
+    qk_unit(kA[0], kA[1], sb0 + sk_off, qb, S);
     kA[0] = ld16(r4, voff, 0);
     kA[1] = ld16(r4, voff, 1024);
     pv_unit<PACKED>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
