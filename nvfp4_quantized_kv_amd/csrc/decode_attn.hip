@@ -379,6 +379,50 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
   }
 }
 
+// Softmax of one unit in the common case: every token valid, no segment
+// switch.  Returns true, leaving everything untouched, when some score
+// passes the reference by kMargin (the caller then takes the general path,
+// which moves the reference and rescales); else turns the scores into the
+// weight operands.  Having no rescale here keeps the accumulators free of
+// any conditional update on the common path.
+template <bool PACKED>
+__device__ __forceinline__ bool softmax_fast(const f4 (&S)[2], float c_log2, float lo_mask,
+                                             float m_ref, float& l_run, h8& p0, h8& p1) {
+  float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+  mx *= c_log2;
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_ref + kMargin) != 0, 0)) return true;
+  const float off = kOff - m_ref;
+  float P[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
+      P[4 * i + r] = e;
+      l_run += e;
+    }
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const float pa = P[2 * s2], pb = P[2 * s2 + 1];
+    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
+    h2 lo;
+    if (PACKED) {
+      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-lo_mask, (float)hi[0], pa),
+                                                             fmaf(-lo_mask, (float)hi[1], pb)));
+      p0[2 * s2] = lo[0];
+      p0[2 * s2 + 1] = lo[1];
+    } else {
+      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
+      p0[2 * s2] = hi[0];
+      p0[2 * s2 + 1] = hi[1];
+      p1[2 * s2] = lo[0];
+      p1[2 * s2 + 1] = lo[1];
+    }
+  }
+  return false;
+}
+
 template <bool MASKED_FULL, bool PACKED>
 __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (&S)[2], int g4,
                                              int c16, float c_log2, float lo_mask, f4 (&acc)[8],
@@ -646,52 +690,82 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                                        q_lds[(q_ready - seg0) % kQSlots]);
     }
 
-    // page p, tokens 32..63 scored, 0..31 accumulated
-    q_of(sg0, qb);
-    qk_unit(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
-    kA[2] = ld16(r2, voff, 2048);
-    kA[3] = ld16(r2, voff, 3072);
-    pv_unit<PACKED>(vA[0], vA[1], sb0 + sv_off, pw0, pw1, acc);
-    vA[0] = ld16(r2, voff, kVCodeOff);
-    vA[1] = ld16(r2, voff, kVCodeOff + 1024);
-    softmax_pick<false, PACKED>(nv0 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
-                                pw1, false, group, ws_acc, ws_ml, st);
+    // The four blocks of a trip: each does QK^T of one unit and PV of the
+    // unit before it, and refills the registers it consumed with the page
+    // two ahead.
+    auto blk1 = [&]() {   // page p: tokens 32..63 scored, 0..31 accumulated
+      q_of(sg0, qb);
+      qk_unit(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
+      kA[2] = ld16(r2, voff, 2048);
+      kA[3] = ld16(r2, voff, 3072);
+      pv_unit<PACKED>(vA[0], vA[1], sb0 + sv_off, pw0, pw1, acc);
+      vA[0] = ld16(r2, voff, kVCodeOff);
+      vA[1] = ld16(r2, voff, kVCodeOff + 1024);
+    };
+    auto blk2 = [&]() {   // page p+1 staged; its 0..31 scored, page p's 32..63 accumulated
+      sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
+      sB = ld16(r3, voff, kKScaleOff);
+      q_of(sg1, qb);
+      qk_unit(kB[0], kB[1], sb1 + sk_off, qb, S);
+      kB[0] = ld16(r3, voff, 0);
+      kB[1] = ld16(r3, voff, 1024);
+      pv_unit<PACKED>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
+      vA[2] = ld16(r2, voff, kVCodeOff + 2048);
+      vA[3] = ld16(r2, voff, kVCodeOff + 3072);
+    };
+    auto blk3 = [&]() {   // page p+1: tokens 32..63 scored, 0..31 accumulated
+      q_of(sg1, qb);
+      qk_unit(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
+      kB[2] = ld16(r3, voff, 2048);
+      kB[3] = ld16(r3, voff, 3072);
+      pv_unit<PACKED>(vB[0], vB[1], sb1 + sv_off, pw0, pw1, acc);
+      vB[0] = ld16(r3, voff, kVCodeOff);
+      vB[1] = ld16(r3, voff, kVCodeOff + 1024);
+    };
+    auto blk4 = [&]() {   // page p+2 staged; its 0..31 scored, page p+1's 32..63 accumulated
+      sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
+      sA = ld16(r4, voff, kKScaleOff);
+      q_of(sg2, qb);
+      qk_unit(kA[0], kA[1], sb0 + sk_off, qb, S);
+      kA[0] = ld16(r4, voff, 0);
+      kA[1] = ld16(r4, voff, 1024);
+      pv_unit<PACKED>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
+      vB[2] = ld16(r3, voff, kVCodeOff + 2048);
+      vB[3] = ld16(r3, voff, kVCodeOff + 3072);
+    };
 
-    // page p+1 staged; its tokens 0..31 scored, page p's 32..63 accumulated
-    sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
-    sB = ld16(r3, voff, kKScaleOff);
-    q_of(sg1, qb);
-    qk_unit(kB[0], kB[1], sb1 + sk_off, qb, S);
-    kB[0] = ld16(r3, voff, 0);
-    kB[1] = ld16(r3, voff, 1024);
-    pv_unit<PACKED>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
-    vA[2] = ld16(r2, voff, kVCodeOff + 2048);
-    vA[3] = ld16(r2, voff, kVCodeOff + 3072);
-    softmax_pick<false, PACKED>(nv1, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
-                                sw1, group, ws_acc, ws_ml, st);
+    // Common trips (every unit full, no segment switch) take a path whose
+    // softmax has no rescale branch; the first unit that needs one sends
+    // the rest of the trip to the general path below, which picks up at
+    // that unit.  Either way the loads go out in the same order.
+    const bool regular = !sw1 && !sw2 && nv0 >= 64 && nv1 >= 64 && nv2 >= 32 && p + 1 < b;
+    int bail = 0;
+    if (__builtin_expect(regular, 1)) {
+      blk1();
+      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 1; goto general; }
+      blk2();
+      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 2; goto general; }
+      blk3();
+      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 3; goto general; }
+      blk4();
+      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 4; goto general; }
+      continue;
+    }
+  general:
+    if (bail < 1) blk1();
+    if (bail <= 1)
+      softmax_pick<false, PACKED>(nv0 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                  pw1, false, group, ws_acc, ws_ml, st);
+    if (bail < 2) blk2();
+    if (bail <= 2)
+      softmax_pick<false, PACKED>(nv1, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
+                                  sw1, group, ws_acc, ws_ml, st);
     if (p + 1 >= b) break;
-
-    // page p+1, tokens 32..63 scored, 0..31 accumulated
-    q_of(sg1, qb);
-    qk_unit(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
-    kB[2] = ld16(r3, voff, 2048);
-    kB[3] = ld16(r3, voff, 3072);
-    pv_unit<PACKED>(vB[0], vB[1], sb1 + sv_off, pw0, pw1, acc);
-    vB[0] = ld16(r3, voff, kVCodeOff);
-    vB[1] = ld16(r3, voff, kVCodeOff + 1024);
-    softmax_pick<false, PACKED>(nv1 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
-                                pw1, false, group, ws_acc, ws_ml, st);
-
-    // page p+2 staged; its tokens 0..31 scored, page p+1's 32..63 accumulated
-    sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
-    sA = ld16(r4, voff, kKScaleOff);
-    q_of(sg2, qb);
-    qk_unit(kA[0], kA[1], sb0 + sk_off, qb, S);
-    kA[0] = ld16(r4, voff, 0);
-    kA[1] = ld16(r4, voff, 1024);
-    pv_unit<PACKED>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
-    vB[2] = ld16(r3, voff, kVCodeOff + 2048);
-    vB[3] = ld16(r3, voff, kVCodeOff + 3072);
+    if (bail < 3) blk3();
+    if (bail <= 3)
+      softmax_pick<false, PACKED>(nv1 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                  pw1, false, group, ws_acc, ws_ml, st);
+    if (bail < 4) blk4();
     softmax_pick<false, PACKED>(nv2, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
                                 sw2, group, ws_acc, ws_ml, st);
   }
