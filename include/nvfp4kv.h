@@ -159,10 +159,10 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
  * partials themselves (for example across devices) or time the stages apart.
  * nvfp4kv_decode_attn_splits takes the arguments of nvfp4kv_decode_attn
  * except `out` and writes only the workspace.  Work layout: the pages of
- * segment g = seq * num_kv_heads + kvh, segments in order, form one flat
- * list of TP pages; the plan's W ranges [w*TP/W, (w+1)*TP/W) split it, and
- * every (segment, range) pair that overlaps yields one partial in slot
- * g + w: per query head h of the group, a reference m (log2 units of
+ * segment g = seq * num_kv_heads + kvh, segments in order, each segment
+ * followed by 3 units of no work, form one flat list of TU units; the plan's
+ * W ranges [w*TU/W, (w+1)*TU/W) split it, and every (segment, range) pair
+ * whose pages overlap yields one partial in slot g + w: per query head h of the group, a reference m (log2 units of
  * sm_scale * score), the weight sum l and the weighted V sum acc[128], with
  * weights 2^(s - m + 8) for the pair's tokens.  Layout, each part starting
  * at a 256-byte boundary: acc at float offset (slot * group + h) * 128 for

@@ -171,8 +171,34 @@ __device__ inline int64_t seq_pages(const int32_t* __restrict__ seq_lens, int s)
   return (seq_lens[s] + kPageSize - 1) / kPageSize;
 }
 
-// The wave whose range [w*TP/W, (w+1)*TP/W) holds flattened page index x.
-__device__ inline int64_t wave_of(int64_t x, int64_t TP, int64_t W) { return ((x + 1) * W - 1) / TP; }
+// The wave whose range [w*TU/W, (w+1)*TU/W) holds work unit x.
+__device__ inline int64_t wave_of(int64_t x, int64_t TU, int64_t W) { return ((x + 1) * W - 1) / TU; }
+
+// Work units of the stream-K split: every segment counts its pages plus
+// kSegExtra units of no work after its last page.  The wavefront whose
+// range holds a segment's end (it quantizes the current token there and
+// switches segments) thereby gets that many fewer pages; measured, those
+// wavefronts otherwise finish 10-25 us after the median one.
+constexpr int kSegExtra = 3;
+
+// Flattened page index (pages of all segments in order) of the first page at
+// or after work unit u; u = total units gives the total page count.
+__device__ inline int64_t page_of_unit(int64_t u, const int32_t* __restrict__ seq_lens, int n_seq,
+                                       int hkv) {
+  int64_t P = 0, U = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int64_t pg = seq_pages(seq_lens, s);
+    const int64_t span = (int64_t)hkv * (pg + kSegExtra);
+    if (u < U + span) {
+      const int64_t k = (u - U) / (pg + kSegExtra);
+      const int64_t off = (u - U) - k * (pg + kSegExtra);
+      return P + k * pg + min(off, pg);
+    }
+    U += span;
+    P += (int64_t)hkv * pg;
+  }
+  return P;
+}
 
 // Inputs of one segment's query operands: the query rows of the group (up
 // to 4 heads per pass, one 16-lane group per head) and the lane's RoPE
@@ -443,12 +469,14 @@ __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (
 constexpr int kQSlots = 3;
 
 // Stream-K decode.  All (sequence, kv head, page) work is laid out flat:
-// segment g = seq * hkv + kvh holds that pair's pages, segments in order.
-// With TP pages in all and W = gridDim.x wavefronts, wave w takes the range
-// [w*TP/W, (w+1)*TP/W), so every wave gets the same number of pages (+-1)
-// whatever the sequence lengths.  A range may start or end inside a segment
-// and may cover several; the wave writes one partial per segment it
-// touches, to slot g + w (distinct for every (segment, wave) pair).
+// segment g = seq * hkv + kvh holds that pair's pages, segments in order,
+// each followed by kSegExtra units of no work.  With TU units in all and W =
+// gridDim.x wavefronts, wave w takes the pages of units [w*TU/W,
+// (w+1)*TU/W), so every wave gets the same amount of work (+-1 page), a
+// segment end counting as kSegExtra pages, whatever the sequence lengths.  A
+// range may start or end inside a segment and may cover several; the wave
+// writes one partial per segment it touches, to slot g + w (distinct for
+// every (segment, wave) pair).
 //
 // The wave walks its range as one stream of pages: two register sets, A for
 // the range's even pages and B for its odd pages, so every load is issued
@@ -485,8 +513,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   int64_t TP = 0;
   for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
   TP *= hkv;
-  const int64_t a = (w * TP) / W;
-  const int64_t b = ((w + 1) * TP) / W;
+  const int64_t TU = TP + (int64_t)kSegExtra * n_seq * hkv;
+  // this wave's pages: those of its work units [w*TU/W, (w+1)*TU/W)
+  const int64_t a = page_of_unit((w * TU) / W, seq_lens, n_seq, hkv);
+  const int64_t b = page_of_unit(((w + 1) * TU) / W, seq_lens, n_seq, hkv);
   if (a >= b) return;
 
   // segment holding page a: sequence, kv head, flat index of its first page
@@ -541,22 +571,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     return x < b && __builtin_amdgcn_readlane(w_j, (int)(x - win)) == 0;
   };
 
-  // query inputs of the range's first segment, loaded before any page
+  // query inputs of the range's first segment, and of the second when the
+  // range reaches it, loaded before any page: made later, at the switch,
+  // their loads would wait for the pages in flight (the wait counter is in
+  // order)
   constexpr int kPasses = PACKED ? 2 : 4;
-  QIn<kPasses> qin;
+  QIn<kPasses> qin, qin2;
   load_q_inputs<kPasses>(seg0, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos, rope_sin,
                          rotary_dim, qin);
+  const bool two_segs = b > seq_base + (int64_t)(kvh0 + 1) * pg;
+  if (two_segs)
+    load_q_inputs<kPasses>(seg0 + 1, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
+                           rope_sin, rotary_dim, qin2);
 
   // ---- the current token of every segment whose last page is in the range
-  // goes into the cache first (only this wavefront reads that page), and
-  // the stores land before any page load below is issued
-  if (k_new != nullptr) {
+  // goes into the cache here (only this wavefront reads that page), and its
+  // stores land before that page's loads are issued.  A token whose page is
+  // among the range's first two pages is written before any page load;
+  // the others after the first two pages' loads are on their way, so the
+  // wavefront does not start late.
+  auto append_tokens = [&](bool first_pages) {
+    bool any = false;
     int sq = seq, kv = kvh0;
     int64_t sstart = seq_base + (int64_t)kvh0 * pg, pgl = pg;
-    bool any = false;
     while (sstart < b) {
       const int64_t last = sstart + pgl - 1;
-      if (pgl > 0 && last >= a && last < b) {
+      if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
         append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
                          q_positions, rope_cos, rope_sin, rotary_dim, hadamard, page_table,
                          pt_stride, seq_lens);
@@ -569,10 +609,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         pgl = seq_pages(seq_lens, sq);
       }
     }
-    if (any) {
-      __builtin_amdgcn_s_waitcnt(0);
-      asm volatile("" ::: "memory");
-    }
+    return any;
+  };
+  if (k_new != nullptr && append_tokens(true)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
   }
 
   const int voff = 16 * lane;
@@ -592,7 +633,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   float m_ref = -INFINITY;
   float l_run = 0.0f;
   SegState st{(size_t)seg0 + (size_t)w};
-  int q_ready = seg0;   // last segment whose query operands are in LDS
+  int q_ready = two_segs ? seg0 + 1 : seg0;   // last segment whose query operands are in LDS
   // query operands of a segment from its LDS slot
   auto q_of = [&](int sg, h8 (&qb)[4]) {
     const int sl = (sg - seg0) % kQSlots;
@@ -627,8 +668,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     vB[1] = ld16(r1, voff, kVCodeOff + 1024);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // query operands of the first segment, while the first pages load
+  // query operands of the first segment, and the later-page tokens, while
+  // the first pages load
+  const bool late_appends = k_new != nullptr && append_tokens(false);
   make_q_operands<PACKED, kPasses>(qin, group, rotary_dim, hadamard, qrow, q_lds[0]);
+  if (two_segs) make_q_operands<PACKED, kPasses>(qin2, group, rotary_dim, hadamard, qrow, q_lds[1]);
+  if (late_appends) {
+    __builtin_amdgcn_s_waitcnt(0);   // before the next loads, which may read those pages
+    asm volatile("" ::: "memory");
+  }
   f4 S[2];
   h8 pw0, pw1, qb[4];
   {
@@ -787,17 +835,19 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int tid = (int)threadIdx.x;
   const int dd = tid & 31, j = tid >> 5;  // dim within the chunk, piece group
   const int kvh = hq_idx / group, h = hq_idx % group;
-  int64_t TP = 0, seq_base = 0;
+  // work units (pages plus kSegExtra per segment, as the decode kernel
+  // splits them) before this segment and in all
+  int64_t TU = 0, seq_base = 0;
   for (int s = 0; s < n_seq; ++s) {
-    const int64_t pg = seq_pages(seq_lens, s);
-    if (s == seq) seq_base = TP;
-    TP += pg;
+    const int64_t pg = seq_pages(seq_lens, s) + kSegExtra;
+    if (s == seq) seq_base = TU;
+    TU += pg;
   }
-  TP *= hkv;
+  TU *= hkv;
   seq_base *= hkv;
   const int64_t pg = seq_pages(seq_lens, seq);
-  const int64_t S = seq_base + kvh * pg, E = S + pg;
-  const int64_t w0 = wave_of(S, TP, W), w1 = wave_of(E - 1, TP, W);
+  const int64_t S = seq_base + kvh * (pg + kSegExtra), E = S + pg;   // the segment's page units
+  const int64_t w0 = wave_of(S, TU, W), w1 = wave_of(E - 1, TU, W);
   const size_t g = (size_t)seq * hkv + kvh;
 
   constexpr int kChunk = 1024;             // pieces whose weights are staged at once
@@ -808,7 +858,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   // ---- running max over all pieces
   float M = -INFINITY;
   for (int64_t w = w0 + tid; w <= w1; w += 256) {
-    if ((w * TP) / W == ((w + 1) * TP) / W) continue;
+    if ((w * TU) / W == ((w + 1) * TU) / W) continue;
     M = fmaxf(M, ws_ml[(g + w) * group + h].x);
   }
   for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
@@ -828,7 +878,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     for (int i = tid; i < n; i += 256) {
       const int64_t w = c0 + i;
       float wt = 0.0f;
-      if ((w * TP) / W != ((w + 1) * TP) / W) {
+      if ((w * TU) / W != ((w + 1) * TU) / W) {
         const float2 ml = ws_ml[(g + w) * group + h];
         wt = exp2f(ml.x - M);
         L += wt * ml.y;
