@@ -160,7 +160,7 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
  * nvfp4kv_decode_attn_splits takes the arguments of nvfp4kv_decode_attn
  * except `out` and writes only the workspace.  Work layout: the pages of
  * segment g = seq * num_kv_heads + kvh, segments in order, each segment
- * followed by 3 units of no work, form one flat list of TU units; the plan's
+ * followed by 5 units of no work, form one flat list of TU units; the plan's
  * W ranges [w*TU/W, (w+1)*TU/W) split it, and every (segment, range) pair
  * whose pages overlap yields one partial in slot g + w: per query head h of the group, a reference m (log2 units of
  * sm_scale * score), the weight sum l and the weighted V sum acc[128], with

@@ -179,7 +179,7 @@ __device__ inline int64_t wave_of(int64_t x, int64_t TU, int64_t W) { return ((x
 // range holds a segment's end (it quantizes the current token there and
 // switches segments) thereby gets that many fewer pages; measured, those
 // wavefronts otherwise finish 10-25 us after the median one.
-constexpr int kSegExtra = 3;
+constexpr int kSegExtra = 5;
 
 // Flattened page index (pages of all segments in order) of the first page at
 // or after work unit u; u = total units gives the total page count.
