@@ -10,10 +10,11 @@
 // in registers to fp16, which holds every E2M1 x E4M3 value exactly, and run
 // on v_mfma_f32_16x16x32_f16.
 //
-// A small kernel quantizes each (sequence, kv head) pair's queries once and
-// stores them as MFMA operands.  The decode kernel then splits the pages of
-// all pairs evenly over its wavefronts (one workgroup each, all resident)
-// and each wavefront streams its range page by page: per 64-token page it
+// The decode kernel splits the pages of all (sequence, kv head) pairs evenly
+// over its wavefronts (one workgroup each, all resident).  Each wavefront
+// quantizes the queries of the pairs it covers into MFMA operands in LDS
+// (and, when given, the step's new token into the cache), then streams its
+// range page by page: per 64-token page it
 // loads 9216 contiguous bytes with nine 16-byte loads per lane (the code
 // tiling of the pool makes each load land directly in the lane's matrix
 // operand), two pages ahead of use, and
