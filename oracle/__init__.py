@@ -182,6 +182,32 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
     return out
 
 
+def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
+                           page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None):
+    """fp64 attention of M new query tokens per sequence over the pool's bytes,
+    causal among the new tokens: the decode step of speculative verification
+    (ai-manual.ru article on "Ninfer 4080", section "Key features": the draft
+    model proposes K tokens, the main model checks them in one step).
+
+    q [n_seq][M][hq][128], q_pos [n_seq][M]; seq_lens[n] counts all M tokens,
+    which are the last M of the sequence.  Query token j of sequence n sees
+    tokens 0 .. seq_lens[n] - M + j, so its output is a one-token decode over
+    that prefix: this function is that definition, one decode_attention call
+    over the n_seq * M (sequence, token) pairs."""
+    q = _c(q, np.float32)
+    n_seq, m = q.shape[0], q.shape[1]
+    lens = np.asarray(seq_lens, np.int64)
+    if (lens < m).any():
+        raise ValueError("every sequence must hold its M new tokens")
+    rows = np.repeat(_c(page_table, np.int32), m, axis=0)
+    pref = (lens[:, None] - m + 1 + np.arange(m)[None, :]).reshape(-1).astype(np.int32)
+    out = decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard,
+                           q.reshape(n_seq * m, q.shape[2], HEAD_DIM),
+                           np.asarray(q_pos, np.int32).reshape(-1), rows, pref, sm_scale,
+                           cos_tab, sin_tab)
+    return out.reshape(n_seq, m, q.shape[2], HEAD_DIM)
+
+
 def reference_attention(q, q_pos, k, v, k_pos, rotary_dim, sm_scale, cos_tab=None, sin_tab=None):
     """fp64 attention on unquantized rows for one sequence: q [hq][128], k/v [T][hkv][128]."""
     q = _c(q, np.float32)

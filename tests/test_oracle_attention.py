@@ -217,3 +217,67 @@ def test_quantized_attention_close_to_unquantized_reference():
     ref = oracle.reference_attention(q[0], T - 1, k, v, np.arange(T), 0, 1 / np.sqrt(128))
     rel = np.linalg.norm(out[0] - ref) / np.linalg.norm(ref)
     assert rel < 0.25
+
+
+def _multi_case(seed, T, m, hkv, hq, rotary=32, hadamard=True):
+    """T cached tokens (the last m are the new ones) and m query tokens per sequence."""
+    rng = np.random.default_rng(seed)
+    n_pages = (T + 63) // 64 + 1
+    pool = _pool(n_pages, hkv)
+    table = rng.permutation(n_pages)[: (T + 63) // 64].astype(np.int32)[None, :]
+    k = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    pos = np.arange(T)
+    slots = table[0, pos // 64].astype(np.int64) * 64 + pos % 64
+    c = s = None
+    if rotary:
+        c, s = oracle.rope_table(1e7, rotary, 1.0, T + 1)
+    oracle.append(pool, n_pages, hkv, rotary, hadamard, 0, k, v, slots, pos, c, s)
+    q = rng.standard_normal((1, m, hq, D)).astype(np.float32)
+    q_pos = (T - m + np.arange(m))[None, :]
+    return dict(pool=pool, n_pages=n_pages, table=table, q=q, q_pos=q_pos, c=c, s=s, slots=slots,
+                k=k, v=v, T=T, m=m, hkv=hkv, hq=hq, rotary=rotary, hadamard=hadamard)
+
+
+def _multi(cs, pool=None, scale=1 / np.sqrt(128)):
+    return oracle.decode_attention_multi(cs["pool"] if pool is None else pool, cs["n_pages"], cs["hkv"], 0,
+                                         cs["rotary"], cs["hadamard"], cs["q"], cs["q_pos"], cs["table"],
+                                         [cs["T"]], scale, cs["c"], cs["s"])
+
+
+def test_multi_query_brute_force_causal():
+    """Query token j of m new tokens attends to tokens 0 .. T-m+j: 50-digit
+    softmax over exactly that prefix (ai-manual.ru "Ninfer 4080", section
+    "Key features": several drafted tokens checked in one step)."""
+    cs = _multi_case(40, 6, 3, 1, 2)
+    out = _multi(cs)
+    kh = np.stack([oracle.dequant_row(*oracle.pool_read_row(cs["pool"], cs["n_pages"], 1, 0, cs["slots"][t], 0, 0)) for t in range(6)])
+    vh = np.stack([oracle.dequant_row(*oracle.pool_read_row(cs["pool"], cs["n_pages"], 1, 0, cs["slots"][t], 0, 1)) for t in range(6)])
+    for j in range(3):
+        p = cs["q_pos"][0, j]
+        for h in range(2):
+            codes, scales = oracle.quant_row(cs["q"][0, j, h], 32, cs["c"][p], cs["s"][p], True)
+            ref = _mp_attention(oracle.dequant_row(codes, scales), kh[: 6 - 3 + j + 1], vh[: 6 - 3 + j + 1], 1 / np.sqrt(128))
+            assert np.abs(out[0, j, h] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max()), (j, h)
+
+
+def test_multi_query_one_token_is_decode():
+    cs = _multi_case(41, 200, 1, 2, 4)
+    single = oracle.decode_attention(cs["pool"], cs["n_pages"], 2, 0, 32, True, cs["q"][:, 0], [199],
+                                     cs["table"], [200], 1 / np.sqrt(128), cs["c"], cs["s"])
+    assert (_multi(cs)[:, 0] == single).all()
+
+
+def test_multi_query_is_causal():
+    """Rewriting the last token's K and V changes only the last query token's
+    output; rewriting token T-m changes all of them."""
+    cs = _multi_case(42, 130, 4, 1, 2)
+    base = _multi(cs)
+    for t, changed in ((129, [3]), (126, [0, 1, 2, 3])):
+        pool = cs["pool"].copy()
+        k2 = cs["k"][t:t + 1] * -2.0
+        v2 = cs["v"][t:t + 1] + 3.0
+        oracle.append(pool, cs["n_pages"], 1, 32, True, 0, k2, v2, cs["slots"][t:t + 1], [t], cs["c"], cs["s"])
+        out = _multi(cs, pool)
+        diff = [j for j in range(4) if not (out[0, j] == base[0, j]).all()]
+        assert diff == changed, (t, diff)
