@@ -186,6 +186,40 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
                           const void* workspace, size_t workspace_bytes, int32_t pages_per_split,
                           hipStream_t stream);
 
+/* Decode attention for n_qtok new query tokens per sequence at once, causal
+ * among them: the verification step of speculative decoding, where a draft
+ * model proposes several tokens and the main model checks them in one step
+ * (ai-manual.ru article on "Ninfer 4080", section "Key features": DFlash2
+ * with K = 7 drafted tokens), or the tail of a chunked prefill.  The n_qtok
+ * tokens are the last n_qtok of each sequence and must already be in the
+ * cache (nvfp4kv_append).  Query token j of sequence n attends to the
+ * sequence's tokens 0 .. seq_lens[n] - n_qtok + j; otherwise each query
+ * token is treated as in nvfp4kv_decode_attn (RoPE at its own position,
+ * Hadamard rotation, NVFP4 round trip).
+ *   q           [n_seq][n_qtok][n_q_heads][128], dtype q_dtype, before RoPE
+ *   q_positions [n_seq][n_qtok] int32 (read only when rotary_dim > 0)
+ *   seq_lens    [n_seq] int32, n_qtok <= seq_lens[n] <= max_seq_len,
+ *               counting the n_qtok tokens
+ *   out         [n_seq][n_qtok][n_q_heads][128] float
+ *   workspace   at least nvfp4kv_decode_multi_workspace_bytes(...) bytes,
+ *               256-byte aligned; its contents on entry do not matter
+ * Other arguments as in nvfp4kv_decode_attn.  The cache is read once per
+ * floor(16 / (n_q_heads / num_kv_heads)) query tokens (16 matrix columns
+ * hold that many tokens' query heads), each such launch followed by its
+ * reduce; 1 <= n_qtok <= 64.  n_qtok = 1 computes what
+ * nvfp4kv_decode_attn computes without k_new/v_new. */
+size_t nvfp4kv_decode_multi_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok,
+                                            int32_t n_q_heads, int64_t max_seq_len,
+                                            int32_t pages_per_split);
+
+int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_qtok,
+                              int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                              const int32_t* q_positions, const float* rope_cos,
+                              const float* rope_sin, int32_t max_pos, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* seq_lens,
+                              int64_t max_seq_len, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
+
 /* Dequantize cached rows (element = E2M1 value * E4M3 scale, exact in f32 and
  * bf16).  K comes back in the rotated domain unless `unrotate` is 1, which
  * applies the Hadamard transform once more (it is its own inverse; the

@@ -63,6 +63,11 @@ def _load():
     L.nvfp4kv_decode_attn_splits.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32,
                                              P, i32, P, i64, ctypes.c_float, P, sz, i32, P]
     L.nvfp4kv_decode_attn_splits.restype = ctypes.c_int
+    L.nvfp4kv_decode_multi_workspace_bytes.argtypes = [PD, i32, i32, i32, i64, i32]
+    L.nvfp4kv_decode_multi_workspace_bytes.restype = sz
+    L.nvfp4kv_decode_attn_multi.argtypes = [PD, i32, i32, i32, i32, P, ctypes.c_int, P, P, P, i32, P, i32,
+                                            P, i64, ctypes.c_float, P, P, sz, i32, P]
+    L.nvfp4kv_decode_attn_multi.restype = ctypes.c_int
     L.nvfp4kv_decode_reduce.argtypes = [PD, i32, i32, P, i64, P, P, sz, i32, P]
     L.nvfp4kv_decode_reduce.restype = ctypes.c_int
     L.nvfp4kv_dequant.argtypes = [PD, i32, i32, P, P, P, ctypes.c_int, i32, P]
@@ -78,7 +83,8 @@ _lib = _load()
 
 EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
             "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_splits",
-            "nvfp4kv_decode_reduce", "nvfp4kv_dequant",
+            "nvfp4kv_decode_reduce", "nvfp4kv_decode_multi_workspace_bytes", "nvfp4kv_decode_attn_multi",
+            "nvfp4kv_dequant",
             "nvfp4kv_last_error", "nvfp4kv_version"]
 
 
@@ -260,6 +266,43 @@ def nvfp4kv_decode_reduce(pool: Pool, n_seq: int, n_q_heads: int, seq_lens: torc
                                       int(max_seq_len), _ptr(out), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), pages_per_split,
                                       _stream(stream)))
+    return out
+
+
+def nvfp4kv_decode_multi_workspace_bytes(pool: Pool, n_seq: int, n_qtok: int, n_q_heads: int,
+                                         max_seq_len: int, pages_per_split: int = 0) -> int:
+    d = pool.desc()
+    return _lib.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), n_seq, n_qtok, n_q_heads,
+                                                     max_seq_len, pages_per_split)
+
+
+def nvfp4kv_decode_attn_multi(pool: Pool, layer: int, q: torch.Tensor, q_positions: torch.Tensor | None,
+                              page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                              sm_scale: float, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None,
+                              rope_cos: torch.Tensor | None = None, rope_sin: torch.Tensor | None = None,
+                              pages_per_split: int = 0, stream=None) -> torch.Tensor:
+    """Decode attention for several new query tokens per sequence, causal among
+    them: q [n_seq][n_qtok][Hq][128] -> out [n_seq][n_qtok][Hq][128] float32.
+    The n_qtok tokens must already be in the cache."""
+    assert q.dim() == 4 and q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    n_seq, n_qtok, n_q_heads, _ = q.shape
+    if out is None:
+        out = torch.empty((n_seq, n_qtok, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = nvfp4kv_decode_multi_workspace_bytes(pool, n_seq, n_qtok, n_q_heads, max_seq_len,
+                                                    pages_per_split)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    d = pool.desc()
+    _check("nvfp4kv_decode_attn_multi",
+           _lib.nvfp4kv_decode_attn_multi(ctypes.byref(d), layer, n_seq, n_qtok, n_q_heads, _ptr(q),
+                                          _dtype_code(q), _ptr(q_positions), _ptr(rope_cos),
+                                          _ptr(rope_sin), max_pos, _ptr(page_table), page_table.shape[1],
+                                          _ptr(seq_lens), int(max_seq_len), float(sm_scale), _ptr(out),
+                                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                          pages_per_split, _stream(stream)))
     return out
 
 

@@ -201,38 +201,59 @@ __device__ inline int64_t page_of_unit(int64_t u, const int32_t* __restrict__ se
   return P;
 }
 
-// Inputs of one segment's query operands: the query rows of the group (up
-// to 4 heads per pass, one 16-lane group per head) and the lane's RoPE
-// coefficients at the segment's position (the same for every head).
-template <int kPasses>
+// Query columns.  A kernel pass works on `group` columns per kv head: the
+// query heads of the kv head (`heads` of them) for `group / heads`
+// consecutive query tokens starting at token qtok0 of the n_qtok new tokens
+// of each sequence (one token, qtok0 0 and group == heads for a plain
+// decode).  Column c is head c % heads of token qtok0 + c / heads; q and out
+// are laid out [seq][token][query head][128].
+struct QCols {
+  int group, heads, n_qtok, qtok0;
+};
+
+// Inputs of one segment's query operands: the query rows of the columns (up
+// to 4 per pass, one 16-lane group per column) and the lane's RoPE
+// coefficients at the segment's one position; with several query tokens
+// (MQ) the rows' positions instead, their coefficients being loaded per pass
+// when the operands are made (one set per pass would hold 16 more registers
+// per pass through the page loads).
+template <int kPasses, bool MQ>
 struct QIn {
   float x[kPasses][8];
   float cv[8], sv[8];
+  int pos[MQ ? kPasses : 1];
 };
 
-template <int kPasses>
-__device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, int group,
+template <int kPasses, bool MQ>
+__device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, const QCols& qc,
                                               const void* __restrict__ q, int q_dtype,
                                               const int32_t* __restrict__ q_positions,
                                               const float* __restrict__ rope_cos,
                                               const float* __restrict__ rope_sin, int rotary_dim,
-                                              QIn<kPasses>& in) {
+                                              QIn<kPasses, MQ>& in) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int seq = sg / hkv, kvh = sg % hkv;
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
-    const int h = min(pass * 4 + g4, group - 1);
-    load8(q, q_dtype, ((size_t)seq * n_q_heads + (size_t)kvh * group + h) * kHeadDim + 8 * c16,
+    const int col = min(pass * 4 + g4, qc.group - 1);
+    const int tok = MQ ? qc.qtok0 + col / qc.heads : 0;
+    const int h = MQ ? col % qc.heads : col;
+    load8(q, q_dtype,
+          (((size_t)seq * (MQ ? qc.n_qtok : 1) + tok) * n_q_heads + (size_t)kvh * qc.heads + h) * kHeadDim +
+              8 * c16,
           in.x[pass]);
+    if (MQ) in.pos[pass] = rotary_dim > 0 ? q_positions[(size_t)seq * qc.n_qtok + tok] : 0;
   }
-  if (rotary_dim > 0) {
-    const int pos = q_positions[seq];
-    rope_coeffs(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
-                rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
-  } else {
+  if (!MQ) {
+    if (rotary_dim > 0) {
+      const int pos = q_positions[seq];
+      rope_coeffs(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
+                  rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
+      for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
+    }
   }
 }
 
@@ -242,9 +263,11 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, in
 // 32*g4 + 8c .. +7 of the query head of column c16.  PACKED: columns 8-15
 // repeat heads 0-7.  Columns past the group are zero.  `qrow` is an LDS
 // scratch of 16 x 128 halves.
-template <bool PACKED, int kPasses>
-__device__ __forceinline__ void make_q_operands(QIn<kPasses>& in, int group, int rotary_dim,
-                                                int hadamard, _Float16* qrow, h8 (*slot)[64]) {
+template <bool PACKED, int kPasses, bool MQ>
+__device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group, int rotary_dim,
+                                                const float* __restrict__ rope_cos,
+                                                const float* __restrict__ rope_sin, int hadamard,
+                                                _Float16* qrow, h8 (*slot)[64]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
@@ -252,6 +275,14 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses>& in, int group, int
     if (pass * 4 >= group) break;
     const int h = pass * 4 + g4;
     uint32_t codes, scode;
+    if (MQ) {
+      if (rotary_dim > 0)
+        rope_coeffs(c16, rotary_dim, rope_cos + (size_t)in.pos[pass] * (rotary_dim / 2),
+                    rope_sin + (size_t)in.pos[pass] * (rotary_dim / 2), in.cv, in.sv);
+      else
+#pragma unroll
+        for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
+    }
     quant_row16_v(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0, codes, scode);
     const float s = e4m3_value(scode);
     h8 qv;
@@ -351,7 +382,10 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
                                            float c_log2, float lo_mask, f4 (&acc)[8], float& m_ref,
                                            float& l_run, h8& p0, h8& p1, bool sw, int group,
                                            float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
-                                           SegState& st) {
+                                           SegState& st, int cut) {
+  // the lane's column sees the unit's first nvalid - cut tokens (cut > 0
+  // only for the earlier of several new query tokens)
+  if (MASKED) nvalid -= cut;
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -367,7 +401,9 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
       l_run = 0.0f;
     }
     const float m_new = fmaxf(m_ref, max4lanes(mx));
-    const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+    // (a column with no valid score yet keeps -inf: its sums are zero, and
+    // 2^(-inf - -inf) would make them NaN)
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
@@ -450,18 +486,20 @@ __device__ __forceinline__ bool softmax_fast(const f4 (&S)[2], float c_log2, flo
   return false;
 }
 
+// Unmasked softmax when the unit's nvalid tokens cover the whole unit for
+// every column (full_at = 32 + the largest cut), else the masked one.
 template <bool MASKED_FULL, bool PACKED>
 __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (&S)[2], int g4,
                                              int c16, float c_log2, float lo_mask, f4 (&acc)[8],
                                              float& m_ref, float& l_run, h8& p0, h8& p1, bool sw,
                                              int group, float* __restrict__ ws_acc,
-                                             float2* __restrict__ ws_ml, SegState& st) {
+                                             float2* __restrict__ ws_ml, SegState& st, int cut) {
   if (nvalid >= full_at)
     softmax_sw<false, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
-                              group, ws_acc, ws_ml, st);
+                              group, ws_acc, ws_ml, st, cut);
   else
     softmax_sw<true, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
-                             group, ws_acc, ws_ml, st);
+                             group, ws_acc, ws_ml, st, cut);
 }
 
 // Query-operand slots in LDS per wave: segment s of the range uses slot
@@ -493,10 +531,10 @@ constexpr int kQSlots = 3;
 // range: its pool block (page * hkv + kv head), its valid tokens, its page
 // index inside its segment and its segment; the loop reads these with
 // readlane, so no scalar loads sit on its path.
-template <bool PACKED>
+template <bool PACKED, bool MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_splitk_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int n_q_heads,
-    int group, const void* __restrict__ q, const void* __restrict__ k_new,
+    QCols qc, const void* __restrict__ q, const void* __restrict__ k_new,
     const void* __restrict__ v_new, int in_dtype, const int32_t* __restrict__ q_positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, const int32_t* __restrict__ page_table, int pt_stride,
@@ -509,6 +547,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4;     // lane group
   const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
+  const int group = qc.group;
+  // Several new query tokens: the lane's column (its query token j) sees the
+  // sequence up to token seq_len - n_qtok + j, i.e. `cut` tokens less than
+  // the last one; a unit is full for every column only from `mcut` tokens
+  // past its end on.
+  const int col = PACKED ? (c16 & 7) : c16;
+  const int cut = MQ ? max(qc.n_qtok - 1 - (qc.qtok0 + min(col, group - 1) / qc.heads), 0) : 0;
+  const int mcut = MQ ? qc.n_qtok - 1 - qc.qtok0 : 0;
   __builtin_amdgcn_s_setprio(3);
   const int64_t W = gridDim.x, w = blockIdx.x;
   int64_t TP = 0;
@@ -577,12 +623,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // their loads would wait for the pages in flight (the wait counter is in
   // order)
   constexpr int kPasses = PACKED ? 2 : 4;
-  QIn<kPasses> qin, qin2;
-  load_q_inputs<kPasses>(seg0, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos, rope_sin,
+  QIn<kPasses, MQ> qin, qin2;
+  load_q_inputs<kPasses, MQ>(seg0, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos, rope_sin,
                          rotary_dim, qin);
   const bool two_segs = b > seq_base + (int64_t)(kvh0 + 1) * pg;
   if (two_segs)
-    load_q_inputs<kPasses>(seg0 + 1, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
+    load_q_inputs<kPasses, MQ>(seg0 + 1, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                            rope_sin, rotary_dim, qin2);
 
   // ---- the current token of every segment whose last page is in the range
@@ -672,8 +718,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // query operands of the first segment, and the later-page tokens, while
   // the first pages load
   const bool late_appends = k_new != nullptr && append_tokens(false);
-  make_q_operands<PACKED, kPasses>(qin, group, rotary_dim, hadamard, qrow, q_lds[0]);
-  if (two_segs) make_q_operands<PACKED, kPasses>(qin2, group, rotary_dim, hadamard, qrow, q_lds[1]);
+  make_q_operands<PACKED, kPasses, MQ>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+                                       q_lds[0]);
+  if (two_segs)
+    make_q_operands<PACKED, kPasses, MQ>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+                                         q_lds[1]);
   if (late_appends) {
     __builtin_amdgcn_s_waitcnt(0);   // before the next loads, which may read those pages
     asm volatile("" ::: "memory");
@@ -691,8 +740,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     vB[2] = ld16(r1, voff, kVCodeOff + 2048);
     vB[3] = ld16(r1, voff, kVCodeOff + 3072);
     __builtin_amdgcn_sched_barrier(0);
-    softmax_pick<false, PACKED>(nvalid_of(a), 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
-                                pw0, pw1, false, group, ws_acc, ws_ml, st);
+    softmax_pick<false, PACKED>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref,
+                                l_run, pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
   }
 
   // ---- main loop, two pages (p in set A, p+1 in set B) per trip.  Page p
@@ -732,10 +781,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // crosses few segment boundaries)
     while (q_ready < sg2) {
       ++q_ready;
-      QIn<kPasses> in;
-      load_q_inputs<kPasses>(q_ready, hkv, n_q_heads, group, q, in_dtype, q_positions, rope_cos,
+      QIn<kPasses, MQ> in;
+      load_q_inputs<kPasses, MQ>(q_ready, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                              rope_sin, rotary_dim, in);
-      make_q_operands<PACKED, kPasses>(in, group, rotary_dim, hadamard, qrow,
+      make_q_operands<PACKED, kPasses, MQ>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
                                        q_lds[(q_ready - seg0) % kQSlots]);
     }
 
@@ -787,7 +836,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // softmax has no rescale branch; the first unit that needs one sends
     // the rest of the trip to the general path below, which picks up at
     // that unit.  Either way the loads go out in the same order.
-    const bool regular = !sw1 && !sw2 && nv0 >= 64 && nv1 >= 64 && nv2 >= 32 && p + 1 < b;
+    const bool regular =
+        !sw1 && !sw2 && nv0 >= 64 + mcut && nv1 >= 64 + mcut && nv2 >= 32 + mcut && p + 1 < b;
     int bail = 0;
     if (__builtin_expect(regular, 1)) {
       blk1();
@@ -803,20 +853,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   general:
     if (bail < 1) blk1();
     if (bail <= 1)
-      softmax_pick<false, PACKED>(nv0 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
-                                  pw1, false, group, ws_acc, ws_ml, st);
+      softmax_pick<false, PACKED>(nv0 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+                                  pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
     if (bail < 2) blk2();
     if (bail <= 2)
-      softmax_pick<false, PACKED>(nv1, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
-                                  sw1, group, ws_acc, ws_ml, st);
+      softmax_pick<false, PACKED>(nv1, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                  pw1, sw1, group, ws_acc, ws_ml, st, cut);
     if (p + 1 >= b) break;
     if (bail < 3) blk3();
     if (bail <= 3)
-      softmax_pick<false, PACKED>(nv1 - 32, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
-                                  pw1, false, group, ws_acc, ws_ml, st);
+      softmax_pick<false, PACKED>(nv1 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+                                  pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
     if (bail < 4) blk4();
-    softmax_pick<false, PACKED>(nv2, 32, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0, pw1,
-                                sw2, group, ws_acc, ws_ml, st);
+    softmax_pick<false, PACKED>(nv2, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+                                pw1, sw2, group, ws_acc, ws_ml, st, cut);
   }
   write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
 }
@@ -828,9 +878,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // pages) wrote nothing and are skipped.
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
-    const int32_t* __restrict__ seq_lens, int n_seq, int hkv, int group, int64_t W,
+    const int32_t* __restrict__ seq_lens, int n_seq, int hkv, QCols qc, int n_q_heads, int64_t W,
     float* __restrict__ out) {
-  const int hq_idx = (int)blockIdx.x;     // query head
+  const int group = qc.group;
+  const int hq_idx = (int)blockIdx.x;     // column over all kv heads: kvh * group + c
   const int seq = (int)blockIdx.y;
   const int d0 = 32 * (int)blockIdx.z;    // first output dim of this block
   const int tid = (int)threadIdx.x;
@@ -911,7 +962,10 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
       o += red_o[i][dd];
       l += red_l[i];
     }
-    out[((size_t)seq * hkv * group + hq_idx) * kHeadDim + d0 + dd] = o / l;
+    // column h of kv head kvh: head h % heads of query token qtok0 + h / heads
+    const int tok = qc.qtok0 + h / qc.heads;
+    out[(((size_t)seq * qc.n_qtok + tok) * n_q_heads + (size_t)kvh * qc.heads + h % qc.heads) * kHeadDim +
+        d0 + dd] = o / l;
   }
 }
 
@@ -922,14 +976,18 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
                                 const int32_t* q_positions, const float* rope_cos,
                                 const float* rope_sin, const int32_t* page_table,
                                 int page_table_stride, const int32_t* seq_lens, float sm_scale,
-                                void* workspace, const DecodePlan& plan, hipStream_t stream) {
+                                void* workspace, const DecodePlan& plan, const QTokens& qt,
+                                hipStream_t stream) {
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   float* ws_acc = reinterpret_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(ws + ws_ml_offset(n_seq, P.hkv, plan));
   const float c_log2 = sm_scale * 1.4426950408889634f;
-  auto kern = plan.group <= 8 ? decode_attn_splitk_kernel<true> : decode_attn_splitk_kernel<false>;
+  const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
+  const bool packed = plan.group <= 8, mq = qt.n_qtok > 1;
+  auto kern = packed ? (mq ? decode_attn_splitk_kernel<true, true> : decode_attn_splitk_kernel<true, false>)
+                     : (mq ? decode_attn_splitk_kernel<false, true> : decode_attn_splitk_kernel<false, false>);
   hipLaunchKernelGGL(kern, dim3(plan.n_waves), dim3(64), 0, stream, P.base, P.num_pages, P.hkv,
-                     layer, n_seq, n_q_heads, plan.group, q, k_new, v_new, in_dtype, q_positions,
+                     layer, n_seq, n_q_heads, qc, q, k_new, v_new, in_dtype, q_positions,
                      rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table, page_table_stride,
                      seq_lens, c_log2, ws_acc, ws_ml);
   return hipGetLastError();
@@ -937,22 +995,29 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
 
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
-                                hipStream_t stream) {
+                                const QTokens& qt, hipStream_t stream) {
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float2* ws_ml = reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) +
                                                         ws_ml_offset(n_seq, hkv, plan));
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(n_q_heads, n_seq, kHeadDim / 32), dim3(256), 0, stream, ws_acc,
-                     ws_ml, seq_lens, n_seq, hkv, plan.group, (int64_t)plan.n_waves, out);
+  const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3(hkv * plan.group, n_seq, kHeadDim / 32), dim3(256), 0,
+                     stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
+                     (int64_t)plan.n_waves, out);
   return hipGetLastError();
 }
 
 int decode_waves_per_cu() {
-  int blocks = 0;
-  int other = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_attn_splitk_kernel<true>, 64, 0) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&other, decode_attn_splitk_kernel<false>, 64, 0) != hipSuccess)
-    return 0;
-  return blocks < other ? blocks : other;
+  int lo = 1 << 30;
+  const void* kernels[4] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false>),
+                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false>),
+                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true>),
+                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true>)};
+  for (const void* k : kernels) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 64, 0) != hipSuccess) return 0;
+    lo = blocks < lo ? blocks : lo;
+  }
+  return lo;
 }
 
 }  // namespace nvfp4kv

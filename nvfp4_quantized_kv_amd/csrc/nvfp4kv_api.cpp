@@ -205,6 +205,17 @@ size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int3
   return nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
 }
 
+// The one new query token of a plain decode call.
+static nvfp4kv::QTokens one_token(const nvfp4kv::DecodePlan& plan) {
+  return nvfp4kv::QTokens{1, 0, plan.group};
+}
+
+// Query tokens per launch of a multi-token decode: as many as fit 16 MFMA
+// columns with every query head of a kv head (at least 1).
+static int tokens_per_launch(int heads, int n_qtok) {
+  return std::max(1, std::min(n_qtok, 16 / heads));
+}
+
 // Checks shared by the decode entry points; fills `plan`.
 static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
                         const void* q, const void* k_new, const void* v_new,
@@ -252,7 +263,7 @@ int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_s
   hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
-                                               workspace, plan, stream);
+                                               workspace, plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
   return NVFP4KV_OK;
 }
@@ -270,7 +281,7 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if ((rc = check_workspace(p, n_seq, plan, workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
   hipError_t e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out,
-                                               workspace, plan, stream);
+                                               workspace, plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
   return NVFP4KV_OK;
 }
@@ -294,11 +305,75 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
-                                               workspace, plan, stream);
+                                               workspace, plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
   e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out, workspace,
-                                    plan, stream);
+                                    plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
+  return NVFP4KV_OK;
+}
+
+// Shape checks of a multi-token decode; `cols` = query columns per launch.
+static int check_multi_shape(const nvfp4kv_pool* p, int32_t n_qtok, int32_t n_q_heads, int* cols,
+                             int* per_launch) {
+  if (n_qtok < 1 || n_qtok > 64)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "n_qtok %d out of range (1..64)", n_qtok);
+  if (n_q_heads <= 0 || n_q_heads % p->num_kv_heads != 0)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of num_kv_heads %d", n_q_heads, p->num_kv_heads);
+  const int heads = n_q_heads / p->num_kv_heads;
+  if (heads > 16) return fail(NVFP4KV_ERR_UNSUPPORTED, "%d query heads per kv head unsupported (at most 16)", heads);
+  *per_launch = tokens_per_launch(heads, n_qtok);
+  *cols = *per_launch * heads;
+  return NVFP4KV_OK;
+}
+
+size_t nvfp4kv_decode_multi_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok,
+                                            int32_t n_q_heads, int64_t max_seq_len,
+                                            int32_t pages_per_split) {
+  g_last_error.clear();
+  if (check_pool_shape(p) != NVFP4KV_OK) return 0;
+  int cols = 0, per = 0;
+  if (check_multi_shape(p, n_qtok, n_q_heads, &cols, &per) != NVFP4KV_OK) return 0;
+  nvfp4kv::DecodePlan plan;
+  if (make_plan(p, n_seq, p->num_kv_heads * cols, max_seq_len, pages_per_split, &plan) != NVFP4KV_OK) return 0;
+  return nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+}
+
+int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_qtok,
+                              int32_t n_q_heads, const void* q, nvfp4kv_dtype q_dtype,
+                              const int32_t* q_positions, const float* rope_cos,
+                              const float* rope_sin, int32_t max_pos, const int32_t* page_table,
+                              int32_t page_table_stride, const int32_t* seq_lens,
+                              int64_t max_seq_len, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  int cols = 0, per = 0;
+  if ((rc = check_multi_shape(p, n_qtok, n_q_heads, &cols, &per)) != NVFP4KV_OK) return rc;
+  nvfp4kv::DecodePlan plan;
+  rc = check_decode(p, layer, n_seq, p->num_kv_heads * cols, q, nullptr, nullptr, q_dtype, q_positions,
+                    rope_cos, rope_sin, max_pos, page_table, page_table_stride, seq_lens, max_seq_len,
+                    sm_scale, workspace, workspace_bytes, pages_per_split, &plan);
+  if (rc != NVFP4KV_OK) return rc;
+  if (out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null out");
+  if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+  const int heads = n_q_heads / p->num_kv_heads;
+  // one split + reduce pair per launch's tokens; the workspace is reused in
+  // stream order
+  for (int t0 = 0; t0 < n_qtok; t0 += per) {
+    nvfp4kv::DecodePlan pl = plan;
+    pl.group = std::min(per, n_qtok - t0) * heads;
+    const nvfp4kv::QTokens qt{n_qtok, t0, heads};
+    hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, nullptr, nullptr,
+                                                 (int)q_dtype, q_positions, rope_cos, rope_sin, page_table,
+                                                 page_table_stride, seq_lens, sm_scale, workspace, pl, qt,
+                                                 stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
+    e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out, workspace, pl,
+                                      qt, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
+  }
   return NVFP4KV_OK;
 }
 

@@ -54,15 +54,25 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
 hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64_t* slots,
                           void* k_out, void* v_out, int dtype, int unrotate, hipStream_t stream);
 
+// New query tokens of a decode call: n_qtok per sequence (1 for a plain
+// decode step), this launch's columns start at token qtok0, and `heads`
+// query heads share each kv head.
+struct QTokens {
+  int n_qtok;
+  int qtok0;
+  int heads;
+};
+
 hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
                                 const void* q, const void* k_new, const void* v_new, int in_dtype,
                                 const int32_t* q_positions, const float* rope_cos,
                                 const float* rope_sin, const int32_t* page_table,
                                 int page_table_stride, const int32_t* seq_lens, float sm_scale,
-                                void* workspace, const DecodePlan& plan, hipStream_t stream);
+                                void* workspace, const DecodePlan& plan, const QTokens& qt,
+                                hipStream_t stream);
 
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
-                                hipStream_t stream);
+                                const QTokens& qt, hipStream_t stream);
 
 }  // namespace nvfp4kv

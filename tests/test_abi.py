@@ -29,7 +29,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for must in ("nvfp4kv_append", "nvfp4kv_decode_attn", "nvfp4kv_dequant", "nvfp4kv_pool_bytes",
-                 "nvfp4kv_decode_workspace_bytes", "nvfp4kv_last_error"):
+                 "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn_multi", "nvfp4kv_last_error"):
         assert must in names
 
 
@@ -144,3 +144,37 @@ def test_dequant_rejects_bad_arguments(kv):
     assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 4, 4096, 4096, 4096, 0, 3, None) == -1
     assert L.nvfp4kv_dequant(ctypes.byref(d), 5, 4, 4096, 4096, 4096, 0, 0, None) == -1
     assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 0, 4096, 4096, 4096, 0, 0, None) == 0
+
+
+def _multi(kv, d, n_seq=2, n_qtok=3, hq=24, q=4096, pt=4096, stride=16, lens=4096, max_len=1000,
+           scale=0.1, out=4096, ws=4096, ws_bytes=1 << 30, pps=0, qpos=4096):
+    return kv.lib().nvfp4kv_decode_attn_multi(ctypes.byref(d), 0, n_seq, n_qtok, hq, q, 1, qpos, 4096, 4096,
+                                              10, pt, stride, lens, max_len, scale, out, ws, ws_bytes, pps,
+                                              None)
+
+
+def test_decode_multi_rejects_bad_arguments(kv):
+    d = _desc(kv)
+    assert _multi(kv, d, n_qtok=0) == -1
+    assert _multi(kv, d, n_qtok=65) == -1
+    assert "n_qtok" in kv.nvfp4kv_last_error()
+    assert _multi(kv, d, hq=25) == -1
+    assert _multi(kv, d, hq=4 * 17) == -2
+    assert _multi(kv, d, q=None) == -1
+    assert _multi(kv, d, qpos=None) == -1
+    assert _multi(kv, d, out=None) == -1
+    assert _multi(kv, d, out=4100) == -1
+    assert _multi(kv, d, ws_bytes=16) == -3
+
+
+def test_decode_multi_workspace_query(kv):
+    """One launch's partials: floor(16 / 6) = 2 tokens x 6 heads = 12 columns
+    per kv head for 24 query heads over 4 kv heads, so 2x the one-token need."""
+    d = _desc(kv)
+    L = kv.lib()
+    one = L.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 3, 24, 470001, 64)
+    m1 = L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 1, 24, 470001, 64)
+    m7 = L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 7, 24, 470001, 64)
+    assert m1 == one
+    assert 2 * one - 1024 <= m7 <= 2 * one + 1024
+    assert L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 0, 24, 1000, 0) == 0
