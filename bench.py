@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM copy-ceiling measurement")
+    ap.add_argument("--multi", type=int, default=0,
+                    help="time multi-query decode instead: this many new query tokens per sequence")
     return ap.parse_args()
 
 
@@ -152,6 +154,8 @@ def main():
         step.run()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
+    if args.multi:
+        return bench_multi(args, step, wl, torch, kv, W, ceiling)
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -227,6 +231,81 @@ def main():
         "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity_err,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_multi(args, step, wl, torch, kv, W, ceiling):
+    """Multi-query decode: every layer, n_qtok = args.multi new query tokens per
+    sequence (already in the cache) attend causally over the cache, one call
+    (a decode launch and its reduce per 16 // heads tokens)."""
+    m = args.multi
+    step.prepare_multi(m)
+    for layer in range(wl.layers):
+        step.append(layer)          # the newest token; the m query tokens are the last m cached ones
+        step.decode_multi(layer)
+    torch.cuda.synchronize()
+    heads = wl.hq // wl.hkv
+    per_launch = max(1, min(m, 16 // heads))
+    launches = -(-m // per_launch)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * wl.layers)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    i = 0
+    for _ in range(args.steps):
+        for layer in range(wl.layers):
+            ev[i][0].record(stream)
+            step.decode_multi(layer)
+            ev[i][1].record(stream)
+            i += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    bytes_per_layer = wl.decode_bytes_per_layer()
+    qrows = wl.n_seq * m * wl.hq * wl.layers
+    log(f"multi-query n_qtok {m}: {launches} decode launches per layer, {ms_per_step:.3f} ms/step, "
+        f"{call_ms * 1e3:.1f} us per layer call")
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("timing the CPU oracle (multi-query) on layer 0")
+        gpu = step.decode_multi(0).cpu().numpy()
+        pool = step.pool.data[:step.pool.data.numel() // wl.layers].cpu().numpy()   # layer 0 blocks
+        oc, os_ = (oracle.rope_table(wl.theta, wl.rotary_dim, wl.pos_scale, step.max_pos)
+                   if wl.rotary_dim else (None, None))
+        t0 = time.perf_counter()
+        ref = oracle.decode_attention_multi(pool, step.pool.num_pages, wl.hkv, 0, wl.rotary_dim, wl.hadamard,
+                                            step.mq[0].float().cpu().numpy(), step.mq_pos.cpu().numpy(),
+                                            step.table_np, wl.seq_lens, W.sm_scale(), oc, os_)
+        secs = time.perf_counter() - t0
+        parity = float(abs(gpu - ref).max())
+        cpu = {"value": round(m * wl.n_seq * wl.hq / secs, 1), "unit": "query token·heads/s", "cores": int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0)))),
+               "kind": "oracle", "sample": f"layer 0 of {wl.layers}: fp64 attention of {wl.n_seq} x {m} query tokens "
+                                             f"x {wl.hq} heads ({secs:.1f} s)"}
+        log(f"oracle {secs:.1f} s; max |gpu - oracle| = {parity:.2e}")
+    rec = {
+        "metric": "NVFP4 multi-query decode-attn query token·heads/s (speculative verification)",
+        "value": round(qrows / (ms_per_step * 1e-3), 1),
+        "unit": "query token·heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} with {m} new query tokens per sequence (causal among them)",
+                   "n_seq": wl.n_seq, "layers": wl.layers, "q_heads": wl.hq, "kv_heads": wl.hkv, "n_qtok": m,
+                   "decode_launches_per_layer": launches,
+                   "step": "per layer: nvfp4kv_decode_attn_multi (decode launch + reduce per "
+                           f"{per_launch} tokens)"},
+        "cache_gbps_per_call": round(bytes_per_layer / (call_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_attn_splitk_kernel (multi-query columns)",
+                     "achieved": round(launches * bytes_per_layer / (call_ms * 1e-3) / 1e9, 2),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(launches * bytes_per_layer / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "note": "per call: the cache read once per decode launch, reduces included"},
+        "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_layer0": parity,
     }
     print(json.dumps(rec), flush=True)
 

@@ -11,7 +11,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (Pool, nvfp4kv_append, nvfp4kv_decode_attn, nvfp4kv_decode_attn_splits,
+from . import (Pool, nvfp4kv_append, nvfp4kv_decode_attn, nvfp4kv_decode_attn_multi,
+               nvfp4kv_decode_attn_splits, nvfp4kv_decode_multi_workspace_bytes,
                nvfp4kv_decode_reduce, nvfp4kv_decode_workspace_bytes, nvfp4kv_rope_table)
 from . import workloads as W
 
@@ -101,6 +102,26 @@ class DecodeStep:
         return nvfp4kv_decode_reduce(self.pool, self.wl.n_seq, self.wl.hq, self.seq_lens,
                                      self.wl.max_seq_len, self.out if out is None else out,
                                      self.workspace, pages_per_split=self.pages_per_split)
+
+    # -- several new query tokens per sequence (speculative verification) ----
+    def prepare_multi(self, m: int) -> None:
+        """Queries of the last m tokens of every sequence, per layer, and a
+        workspace for them; the m tokens must be in the cache (fill + append)."""
+        wl, n = self.wl, self.wl.n_seq
+        self.m = m
+        self.mq = [torch.stack([W.rows(wl, "q", layer, 1000 + i, m, wl.hq, self.device) for i in range(n)])
+                   .contiguous() for layer in range(wl.layers)]
+        self.mq_pos = torch.tensor([[T - m + j for j in range(m)] for T in wl.seq_lens], dtype=torch.int32,
+                                   device=self.device)
+        self.mq_out = torch.empty((n, m, wl.hq, 128), dtype=torch.float32, device=self.device)
+        need = nvfp4kv_decode_multi_workspace_bytes(self.pool, n, m, wl.hq, wl.max_seq_len, self.pages_per_split)
+        self.mq_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+
+    def decode_multi(self, layer: int) -> torch.Tensor:
+        return nvfp4kv_decode_attn_multi(self.pool, layer, self.mq[layer], self.mq_pos, self.table,
+                                         self.seq_lens, self.wl.max_seq_len, W.sm_scale(), out=self.mq_out,
+                                         workspace=self.mq_ws, rope_cos=self.rope_cos, rope_sin=self.rope_sin,
+                                         pages_per_split=self.pages_per_split)
 
     def run(self, fused: bool = True) -> None:
         for layer in range(self.wl.layers):
