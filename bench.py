@@ -238,7 +238,7 @@ def main():
 def bench_multi(args, step, wl, torch, kv, W, ceiling):
     """Multi-query decode: every layer, n_qtok = args.multi new query tokens per
     sequence (already in the cache) attend causally over the cache, one call
-    (a decode launch and its reduce per 16 // heads tokens)."""
+    (a decode launch and its reduce per 48 // heads tokens)."""
     m = args.multi
     step.prepare_multi(m)
     for layer in range(wl.layers):
@@ -246,7 +246,7 @@ def bench_multi(args, step, wl, torch, kv, W, ceiling):
         step.decode_multi(layer)
     torch.cuda.synchronize()
     heads = wl.hq // wl.hkv
-    per_launch = max(1, min(m, 16 // heads))
+    per_launch = max(1, min(m, 48 // heads))      # a launch takes up to 48 query columns per kv head
     launches = -(-m // per_launch)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))

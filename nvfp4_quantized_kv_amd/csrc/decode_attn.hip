@@ -91,13 +91,15 @@ __device__ inline float sum4lanes(float v) {
 constexpr float kOff = 8.0f;
 constexpr float kMargin = 7.0f;
 
-// QK^T of one 32-token unit (K tiles i = 0, 1 of the unit): S[i] holds
-// tokens 16i + 4*g4 + r of the unit for query column c16.  `k0`/`k1` hold
-// the lane's 32 codes of token c16 (+16) for dims 32*g4 .. +31; `sk` points
-// at the lane's K scale pair (blocks 2*g4, 2*g4+1) of the unit's first token
-// row in the staged page (tile stride 128 bytes).
+// QK^T of one 32-token unit (K tiles i = 0, 1 of the unit): S[t][i] holds
+// tokens 16i + 4*g4 + r of the unit for query column 16t + c16 (t < NT
+// column tiles, each dequantized K operand feeding NT MFMAs).  `k0`/`k1`
+// hold the lane's 32 codes of token c16 (+16) for dims 32*g4 .. +31; `sk`
+// points at the lane's K scale pair (blocks 2*g4, 2*g4+1) of the unit's
+// first token row in the staged page (tile stride 128 bytes).
+template <int NT>
 __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_t* __restrict__ sk,
-                                        const h8 (&qb)[4], f4 (&S)[2]) {
+                                        const h8 (&qb)[NT][4], f4 (&S)[NT][2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t ku = *reinterpret_cast<const uint16_t*>(sk + 128 * i);
@@ -106,7 +108,8 @@ __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_
     const h2 sc = bits_h2(__builtin_amdgcn_perm(0u, ku, 0x0c010c00u) << 7);
     const h2 sc0 = __builtin_shufflevector(sc, sc, 0, 0), sc1 = __builtin_shufflevector(sc, sc, 1, 1);
     const u4& kc = i ? k1 : k0;
-    S[i] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S[t][i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w = kc[c];
@@ -118,7 +121,8 @@ __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_
         a[2 * b] = x[0];
         a[2 * b + 1] = x[1];
       }
-      S[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], S[i], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) S[t][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[t][c], S[t][i], 0, 0, 0);
     }
   }
 }
@@ -129,9 +133,10 @@ __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_
 // block c16/2, in the staged page.  PACKED: `p0` carries the fp16 high part
 // of the weights in columns 0-7 and the low part in columns 8-15, one MFMA
 // per tile; otherwise `p0`/`p1` are the high/low parts, two MFMAs per tile.
-template <bool PACKED>
+// With NT column tiles every dequantized V operand feeds all of them.
+template <bool PACKED, int NT>
 __device__ __forceinline__ void pv_unit(const u4& va, const u4& vb, const uint8_t* __restrict__ sv,
-                                        const h8& p0, const h8& p1, f4 (&acc)[8]) {
+                                        const h8 (&p0)[NT], const h8 (&p1)[NT], f4 (&acc)[NT][8]) {
   // V words of the 8 tokens of this lane group; token of k-slot s:
   // s < 4: 4*g4 + s, s >= 4: 16 + 4*g4 + (s-4)
   const uint32_t w[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
@@ -158,11 +163,14 @@ __device__ __forceinline__ void pv_unit(const u4& va, const u4& vb, const uint8_
       ao[2 * pr] = o[0];
       ao[2 * pr + 1] = o[1];
     }
-    acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p0, acc[2 * b], 0, 0, 0);
-    acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p0, acc[2 * b + 1], 0, 0, 0);
-    if (!PACKED) {
-      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p1, acc[2 * b], 0, 0, 0);
-      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p1, acc[2 * b + 1], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p0[t], acc[t][2 * b], 0, 0, 0);
+      acc[t][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p0[t], acc[t][2 * b + 1], 0, 0, 0);
+      if (!PACKED) {
+        acc[t][2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ae, p1[t], acc[t][2 * b], 0, 0, 0);
+        acc[t][2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ao, p1[t], acc[t][2 * b + 1], 0, 0, 0);
+      }
     }
   }
 }
@@ -258,20 +266,26 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, co
 }
 
 // Query operands of one segment into an LDS slot: RoPE, Hadamard and the
-// NVFP4 round trip of the group's query heads (exact in fp16), laid out as
-// the B operands of QK^T: slot[c][lane] holds, for lane (c16, g4), dims
-// 32*g4 + 8c .. +7 of the query head of column c16.  PACKED: columns 8-15
-// repeat heads 0-7.  Columns past the group are zero.  `qrow` is an LDS
-// scratch of 16 x 128 halves.
-template <bool PACKED, int kPasses, bool MQ>
+// NVFP4 round trip of the group's query columns (exact in fp16), laid out as
+// the B operands of QK^T: slot[t][c][lane] holds, for lane (c16, g4), dims
+// 32*g4 + 8c .. +7 of column 16t + c16.  PACKED: columns 8-15 repeat
+// columns 0-7.  Columns past the group are zero.  The rows of a tile are
+// first written row-major to `qrow` (16 x 128 halves of LDS scratch), or,
+// with several tiles, to the tile's own slot memory, which is then
+// rewritten in operand order.
+template <bool PACKED, int kPasses, bool MQ, int NT>
 __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group, int rotary_dim,
                                                 const float* __restrict__ rope_cos,
                                                 const float* __restrict__ rope_sin, int hadamard,
-                                                _Float16* qrow, h8 (*slot)[64]) {
+                                                _Float16* qrow, h8 (*slot)[4][64]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
+  constexpr int kTilePasses = kPasses / NT;
 #pragma unroll
-  for (int pass = 0; pass < kPasses; ++pass) {
+  for (int t = 0; t < NT; ++t) {
+  _Float16* rows = NT > 1 ? reinterpret_cast<_Float16*>(&slot[t][0][0]) : qrow;
+#pragma unroll
+  for (int pass = kTilePasses * t; pass < kTilePasses * (t + 1); ++pass) {
     if (pass * 4 >= group) break;
     const int h = pass * 4 + g4;
     uint32_t codes, scode;
@@ -288,16 +302,21 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
     h8 qv;
 #pragma unroll
     for (int k = 0; k < 8; ++k) qv[k] = (_Float16)(e2m1_value((codes >> (4 * k)) & 15u) * s);
-    if (h < group) *reinterpret_cast<h8*>(&qrow[h * kHeadDim + 8 * c16]) = qv;
+    if (h < group) *reinterpret_cast<h8*>(&rows[(h - 16 * t) * kHeadDim + 8 * c16]) = qv;
   }
   __syncthreads();
   const int qcol = PACKED ? (c16 & 7) : c16;
+  h8 v[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    slot[c][lane] = (qcol < group) ? *reinterpret_cast<const h8*>(&qrow[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
+    v[c] = (16 * t + qcol < group) ? *reinterpret_cast<const h8*>(&rows[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
   }
+  if (NT > 1) __syncthreads();   // every row read before the slot is rewritten
+#pragma unroll
+  for (int c = 0; c < 4; ++c) slot[t][c][lane] = v[c];
   __syncthreads();
+  }
 }
 
 // The current token of segment sg (token seq_lens[seq] - 1) quantized into
@@ -339,11 +358,12 @@ __device__ __forceinline__ void append_new_token(
   }
 }
 
-// Partial (m, l, acc) of the group's query heads to slot `slot`.
+// Partial (m, l, acc) of the columns col0 .. col0 + 15 (those below
+// `group`) to slot `slot`.
 template <bool PACKED>
 __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, float l_run, int c16,
                                               int g4, int group, float* __restrict__ ws_acc,
-                                              float2* __restrict__ ws_ml, size_t slot) {
+                                              float2* __restrict__ ws_ml, size_t slot, int col0) {
   f4 o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -356,15 +376,16 @@ __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, f
     }
   }
   const float l_tot = sum4lanes(l_run);
-  if (c16 < group) {
+  const int col = col0 + c16;
+  if (col < group) {
     // lane holds dims 32*g4 + 8i + j in o[j][i]
-    float* dst = ws_acc + (slot * group + c16) * kHeadDim + 32 * g4;
+    float* dst = ws_acc + (slot * group + col) * kHeadDim + 32 * g4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       reinterpret_cast<float4*>(dst + 8 * i)[0] = make_float4(o[0][i], o[1][i], o[2][i], o[3][i]);
       reinterpret_cast<float4*>(dst + 8 * i)[1] = make_float4(o[4][i], o[5][i], o[6][i], o[7][i]);
     }
-    if (g4 == 0) ws_ml[slot * group + c16] = make_float2(m_ref, l_tot);
+    if (g4 == 0) ws_ml[slot * group + col] = make_float2(m_ref, l_tot);
   }
 }
 
@@ -373,16 +394,16 @@ struct SegState {
   size_t slot;        // partial slot of the current segment (segment + wave)
 };
 
-// Online softmax of one unit with the segment switch folded into its rare
-// branch: when `sw` is set, the unit is the first of a new segment, so the
-// finished segment's partial is written and the running state restarts
-// (reference -inf, so the rescale factor is 0).
+// Online softmax of one unit for one column tile with the segment switch
+// folded into its rare branch: when `sw` is set, the unit is the first of a
+// new segment, so the finished segment's partial goes to slot `slot` and the
+// running state restarts (reference -inf, so the rescale factor is 0).
 template <bool MASKED, bool PACKED>
 __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, int nvalid,
                                            float c_log2, float lo_mask, f4 (&acc)[8], float& m_ref,
                                            float& l_run, h8& p0, h8& p1, bool sw, int group,
                                            float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
-                                           SegState& st, int cut) {
+                                           size_t slot, int cut, int col0) {
   // the lane's column sees the unit's first nvalid - cut tokens (cut > 0
   // only for the earlier of several new query tokens)
   if (MASKED) nvalid -= cut;
@@ -395,15 +416,14 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
   mx *= c_log2;
   if (sw || __builtin_amdgcn_ballot_w64(mx > m_ref + kMargin)) {
     if (sw) {
-      write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
-      st.slot += 1;
+      write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, slot, col0);
       m_ref = -INFINITY;
       l_run = 0.0f;
     }
     const float m_new = fmaxf(m_ref, max4lanes(mx));
-    // (a column with no valid score yet keeps -inf: its sums are zero, and
-    // 2^(-inf - -inf) would make them NaN)
-    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    // (a column with no valid score yet keeps -inf and zero sums, also right
+    // after a segment switch; 2^(-inf - -inf) would make them NaN)
+    const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
     l_run *= alpha;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= alpha;
@@ -448,58 +468,74 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
 // which moves the reference and rescales); else turns the scores into the
 // weight operands.  Having no rescale here keeps the accumulators free of
 // any conditional update on the common path.
-template <bool PACKED>
-__device__ __forceinline__ bool softmax_fast(const f4 (&S)[2], float c_log2, float lo_mask,
-                                             float m_ref, float& l_run, h8& p0, h8& p1) {
-  float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                   fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-  mx *= c_log2;
-  if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_ref + kMargin) != 0, 0)) return true;
-  const float off = kOff - m_ref;
-  float P[8];
+template <bool PACKED, int NT>
+__device__ __forceinline__ bool softmax_fast(const f4 (&S)[NT][2], float c_log2, float lo_mask,
+                                             const float (&m_ref)[NT], float (&l_run)[NT], h8 (&p0)[NT],
+                                             h8 (&p1)[NT]) {
+  bool over = false;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < NT; ++t) {
+    float mx = fmaxf(fmaxf(fmaxf(S[t][0][0], S[t][0][1]), fmaxf(S[t][0][2], S[t][0][3])),
+                     fmaxf(fmaxf(S[t][1][0], S[t][1][1]), fmaxf(S[t][1][2], S[t][1][3])));
+    mx *= c_log2;
+    over = over || mx > m_ref[t] + kMargin;
+  }
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(over) != 0, 0)) return true;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = __builtin_amdgcn_exp2f(fmaf(S[i][r], c_log2, off));
-      P[4 * i + r] = e;
-      l_run += e;
-    }
+  for (int t = 0; t < NT; ++t) {
+    const float off = kOff - m_ref[t];
+    float P[8];
 #pragma unroll
-  for (int s2 = 0; s2 < 4; ++s2) {
-    const float pa = P[2 * s2], pb = P[2 * s2 + 1];
-    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
-    h2 lo;
-    if (PACKED) {
-      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-lo_mask, (float)hi[0], pa),
-                                                             fmaf(-lo_mask, (float)hi[1], pb)));
-      p0[2 * s2] = lo[0];
-      p0[2 * s2 + 1] = lo[1];
-    } else {
-      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
-      p0[2 * s2] = hi[0];
-      p0[2 * s2 + 1] = hi[1];
-      p1[2 * s2] = lo[0];
-      p1[2 * s2 + 1] = lo[1];
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(S[t][i][r], c_log2, off));
+        P[4 * i + r] = e;
+        l_run[t] += e;
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float pa = P[2 * s2], pb = P[2 * s2 + 1];
+      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa, pb));
+      h2 lo;
+      if (PACKED) {
+        lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-lo_mask, (float)hi[0], pa),
+                                                               fmaf(-lo_mask, (float)hi[1], pb)));
+        p0[t][2 * s2] = lo[0];
+        p0[t][2 * s2 + 1] = lo[1];
+      } else {
+        lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
+        p0[t][2 * s2] = hi[0];
+        p0[t][2 * s2 + 1] = hi[1];
+        p1[t][2 * s2] = lo[0];
+        p1[t][2 * s2 + 1] = lo[1];
+      }
     }
   }
   return false;
 }
 
-// Unmasked softmax when the unit's nvalid tokens cover the whole unit for
-// every column (full_at = 32 + the largest cut), else the masked one.
-template <bool MASKED_FULL, bool PACKED>
-__device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (&S)[2], int g4,
-                                             int c16, float c_log2, float lo_mask, f4 (&acc)[8],
-                                             float& m_ref, float& l_run, h8& p0, h8& p1, bool sw,
-                                             int group, float* __restrict__ ws_acc,
-                                             float2* __restrict__ ws_ml, SegState& st, int cut) {
-  if (nvalid >= full_at)
-    softmax_sw<false, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
-                              group, ws_acc, ws_ml, st, cut);
-  else
-    softmax_sw<true, PACKED>(S, g4, c16, nvalid, c_log2, lo_mask, acc, m_ref, l_run, p0, p1, sw,
-                             group, ws_acc, ws_ml, st, cut);
+// Softmax of one unit for every column tile: unmasked when the unit's
+// nvalid tokens cover the whole unit for every column (full_at = 32 + the
+// largest cut), else masked.  A segment switch moves to the next slot once
+// every tile's partial is written.
+template <bool PACKED, int NT>
+__device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (&S)[NT][2], int g4,
+                                             int c16, float c_log2, float lo_mask, f4 (&acc)[NT][8],
+                                             float (&m_ref)[NT], float (&l_run)[NT], h8 (&p0)[NT],
+                                             h8 (&p1)[NT], bool sw, int group,
+                                             float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+                                             SegState& st, const int (&cut)[NT]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (nvalid >= full_at)
+      softmax_sw<false, PACKED>(S[t], g4, c16, nvalid, c_log2, lo_mask, acc[t], m_ref[t], l_run[t], p0[t],
+                                p1[t], sw, group, ws_acc, ws_ml, st.slot, cut[t], 16 * t);
+    else
+      softmax_sw<true, PACKED>(S[t], g4, c16, nvalid, c_log2, lo_mask, acc[t], m_ref[t], l_run[t], p0[t],
+                               p1[t], sw, group, ws_acc, ws_ml, st.slot, cut[t], 16 * t);
+  }
+  if (sw) st.slot += 1;
 }
 
 // Query-operand slots in LDS per wave: segment s of the range uses slot
@@ -531,8 +567,14 @@ constexpr int kQSlots = 3;
 // range: its pool block (page * hkv + kv head), its valid tokens, its page
 // index inside its segment and its segment; the loop reads these with
 // readlane, so no scalar loads sit on its path.
-template <bool PACKED, bool MQ>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_splitk_kernel(
+//
+// NT column tiles of 16 (several new query tokens per sequence, up to 48
+// columns) share every dequantized K and V operand: the page is read and
+// dequantized once and feeds NT times the MFMAs and softmax work.  Those
+// kernels hold NT sets of scores, weights and accumulators and run one
+// wavefront per SIMD.
+template <bool PACKED, bool MQ, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 : 2, NT > 1 ? 1 : 2))) void decode_attn_splitk_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int n_q_heads,
     QCols qc, const void* __restrict__ q, const void* __restrict__ k_new,
     const void* __restrict__ v_new, int in_dtype, const int32_t* __restrict__ q_positions,
@@ -541,8 +583,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
-  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][4][64];
-  __shared__ __attribute__((aligned(16))) _Float16 qrow[16 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][64];
+  __shared__ __attribute__((aligned(16))) _Float16 qrow[NT > 1 ? 8 : 16 * kHeadDim];
 
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4;     // lane group
@@ -552,8 +594,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // sequence up to token seq_len - n_qtok + j, i.e. `cut` tokens less than
   // the last one; a unit is full for every column only from `mcut` tokens
   // past its end on.
-  const int col = PACKED ? (c16 & 7) : c16;
-  const int cut = MQ ? max(qc.n_qtok - 1 - (qc.qtok0 + min(col, group - 1) / qc.heads), 0) : 0;
+  int cut[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * t + (PACKED ? (c16 & 7) : c16);
+    cut[t] = MQ ? max(qc.n_qtok - 1 - (qc.qtok0 + min(col, group - 1) / qc.heads), 0) : 0;
+  }
   const int mcut = MQ ? qc.n_qtok - 1 - qc.qtok0 : 0;
   __builtin_amdgcn_s_setprio(3);
   const int64_t W = gridDim.x, w = blockIdx.x;
@@ -621,15 +667,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // query inputs of the range's first segment, and of the second when the
   // range reaches it, loaded before any page: made later, at the switch,
   // their loads would wait for the pages in flight (the wait counter is in
-  // order)
-  constexpr int kPasses = PACKED ? 2 : 4;
+  // order).  With several column tiles the inputs are too many registers to
+  // hold through the first page loads: their operands are made here.
+  constexpr int kPasses = PACKED ? 2 : 4 * NT;
   QIn<kPasses, MQ> qin, qin2;
   load_q_inputs<kPasses, MQ>(seg0, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos, rope_sin,
                          rotary_dim, qin);
   const bool two_segs = b > seq_base + (int64_t)(kvh0 + 1) * pg;
-  if (two_segs)
+  if (NT > 1) {
+    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+                                             q_lds[0]);
+    if (two_segs) {
+      load_q_inputs<kPasses, MQ>(seg0 + 1, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
+                                 rope_sin, rotary_dim, qin2);
+      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard,
+                                               qrow, q_lds[1]);
+    }
+  } else if (two_segs) {
     load_q_inputs<kPasses, MQ>(seg0 + 1, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                            rope_sin, rotary_dim, qin2);
+  }
 
   // ---- the current token of every segment whose last page is in the range
   // goes into the cache here (only this wavefront reads that page), and its
@@ -674,18 +731,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int sv_off = 512 + 32 * g4 + (c16 >> 1);  // V scales of token 4*g4, block c16/2
   const float lo_mask = (PACKED && c16 >= 8) ? 1.0f : 0.0f;
 
-  f4 acc[8];
+  f4 acc[NT][8];
+  float m_ref[NT], l_run[NT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;
-  float l_run = 0.0f;
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[t][j] = f4{0.f, 0.f, 0.f, 0.f};
+    m_ref[t] = -INFINITY;
+    l_run[t] = 0.0f;
+  }
   SegState st{(size_t)seg0 + (size_t)w};
   int q_ready = two_segs ? seg0 + 1 : seg0;   // last segment whose query operands are in LDS
   // query operands of a segment from its LDS slot
-  auto q_of = [&](int sg, h8 (&qb)[4]) {
+  auto q_of = [&](int sg, h8 (&qb)[NT][4]) {
+    if (NT > 1) asm volatile("" ::: "memory");
     const int sl = (sg - seg0) % kQSlots;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qb[c] = q_lds[sl][c][lane];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qb[t][c] = q_lds[sl][t][c][lane];
   };
   auto seg_of = [&](int64_t x) { return __builtin_amdgcn_readlane(w_sg, (int)(min(x, b - 1) - win)); };
 
@@ -718,30 +782,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // query operands of the first segment, and the later-page tokens, while
   // the first pages load
   const bool late_appends = k_new != nullptr && append_tokens(false);
-  make_q_operands<PACKED, kPasses, MQ>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
-                                       q_lds[0]);
-  if (two_segs)
-    make_q_operands<PACKED, kPasses, MQ>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
-                                         q_lds[1]);
+  if (NT == 1) {
+    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+                                             q_lds[0]);
+    if (two_segs)
+      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard,
+                                               qrow, q_lds[1]);
+  }
   if (late_appends) {
     __builtin_amdgcn_s_waitcnt(0);   // before the next loads, which may read those pages
     asm volatile("" ::: "memory");
   }
-  f4 S[2];
-  h8 pw0, pw1, qb[4];
+  f4 S[NT][2];
+  h8 pw0[NT], pw1[NT], qb[NT][4];
   {
     const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r2, voff, kKScaleOff);
     q_of(seg0, qb);
-    qk_unit(kA[0], kA[1], reinterpret_cast<const uint8_t*>(&sc_lds[0][0]) + sk_off, qb, S);
+    qk_unit<NT>(kA[0], kA[1], reinterpret_cast<const uint8_t*>(&sc_lds[0][0]) + sk_off, qb, S);
     kA[0] = ld16(r2, voff, 0);
     kA[1] = ld16(r2, voff, 1024);
     vB[2] = ld16(r1, voff, kVCodeOff + 2048);
     vB[3] = ld16(r1, voff, kVCodeOff + 3072);
     __builtin_amdgcn_sched_barrier(0);
-    softmax_pick<false, PACKED>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref,
-                                l_run, pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
+    softmax_pick<PACKED, NT>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+                             pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
   }
 
   // ---- main loop, two pages (p in set A, p+1 in set B) per trip.  Page p
@@ -784,8 +850,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       QIn<kPasses, MQ> in;
       load_q_inputs<kPasses, MQ>(q_ready, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                              rope_sin, rotary_dim, in);
-      make_q_operands<PACKED, kPasses, MQ>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
-                                       q_lds[(q_ready - seg0) % kQSlots]);
+      make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+                                               q_lds[(q_ready - seg0) % kQSlots]);
     }
 
     // The four blocks of a trip: each does QK^T of one unit and PV of the
@@ -793,10 +859,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // two ahead.
     auto blk1 = [&]() {   // page p: tokens 32..63 scored, 0..31 accumulated
       q_of(sg0, qb);
-      qk_unit(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
+      qk_unit<NT>(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
       kA[2] = ld16(r2, voff, 2048);
       kA[3] = ld16(r2, voff, 3072);
-      pv_unit<PACKED>(vA[0], vA[1], sb0 + sv_off, pw0, pw1, acc);
+      pv_unit<PACKED, NT>(vA[0], vA[1], sb0 + sv_off, pw0, pw1, acc);
       vA[0] = ld16(r2, voff, kVCodeOff);
       vA[1] = ld16(r2, voff, kVCodeOff + 1024);
     };
@@ -804,19 +870,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
       sB = ld16(r3, voff, kKScaleOff);
       q_of(sg1, qb);
-      qk_unit(kB[0], kB[1], sb1 + sk_off, qb, S);
+      qk_unit<NT>(kB[0], kB[1], sb1 + sk_off, qb, S);
       kB[0] = ld16(r3, voff, 0);
       kB[1] = ld16(r3, voff, 1024);
-      pv_unit<PACKED>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
+      pv_unit<PACKED, NT>(vA[2], vA[3], sb0 + sv_off + 256, pw0, pw1, acc);
       vA[2] = ld16(r2, voff, kVCodeOff + 2048);
       vA[3] = ld16(r2, voff, kVCodeOff + 3072);
     };
     auto blk3 = [&]() {   // page p+1: tokens 32..63 scored, 0..31 accumulated
       q_of(sg1, qb);
-      qk_unit(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
+      qk_unit<NT>(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
       kB[2] = ld16(r3, voff, 2048);
       kB[3] = ld16(r3, voff, 3072);
-      pv_unit<PACKED>(vB[0], vB[1], sb1 + sv_off, pw0, pw1, acc);
+      pv_unit<PACKED, NT>(vB[0], vB[1], sb1 + sv_off, pw0, pw1, acc);
       vB[0] = ld16(r3, voff, kVCodeOff);
       vB[1] = ld16(r3, voff, kVCodeOff + 1024);
     };
@@ -824,10 +890,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
       sA = ld16(r4, voff, kKScaleOff);
       q_of(sg2, qb);
-      qk_unit(kA[0], kA[1], sb0 + sk_off, qb, S);
+      qk_unit<NT>(kA[0], kA[1], sb0 + sk_off, qb, S);
       kA[0] = ld16(r4, voff, 0);
       kA[1] = ld16(r4, voff, 1024);
-      pv_unit<PACKED>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
+      pv_unit<PACKED, NT>(vB[2], vB[3], sb1 + sv_off + 256, pw0, pw1, acc);
       vB[2] = ld16(r3, voff, kVCodeOff + 2048);
       vB[3] = ld16(r3, voff, kVCodeOff + 3072);
     };
@@ -841,34 +907,36 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     int bail = 0;
     if (__builtin_expect(regular, 1)) {
       blk1();
-      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 1; goto general; }
+      if (softmax_fast<PACKED, NT>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 1; goto general; }
       blk2();
-      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 2; goto general; }
+      if (softmax_fast<PACKED, NT>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 2; goto general; }
       blk3();
-      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 3; goto general; }
+      if (softmax_fast<PACKED, NT>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 3; goto general; }
       blk4();
-      if (softmax_fast<PACKED>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 4; goto general; }
+      if (softmax_fast<PACKED, NT>(S, c_log2, lo_mask, m_ref, l_run, pw0, pw1)) { bail = 4; goto general; }
       continue;
     }
   general:
     if (bail < 1) blk1();
     if (bail <= 1)
-      softmax_pick<false, PACKED>(nv0 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+      softmax_pick<PACKED, NT>(nv0 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
                                   pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
     if (bail < 2) blk2();
     if (bail <= 2)
-      softmax_pick<false, PACKED>(nv1, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+      softmax_pick<PACKED, NT>(nv1, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
                                   pw1, sw1, group, ws_acc, ws_ml, st, cut);
     if (p + 1 >= b) break;
     if (bail < 3) blk3();
     if (bail <= 3)
-      softmax_pick<false, PACKED>(nv1 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+      softmax_pick<PACKED, NT>(nv1 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
                                   pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
     if (bail < 4) blk4();
-    softmax_pick<false, PACKED>(nv2, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
+    softmax_pick<PACKED, NT>(nv2, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
                                 pw1, sw2, group, ws_acc, ws_ml, st, cut);
   }
-  write_partial<PACKED>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, st.slot);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    write_partial<PACKED>(acc[t], m_ref[t], l_run[t], c16, g4, group, ws_acc, ws_ml, st.slot, 16 * t);
 }
 
 // Combine the partials of one (sequence, query head) for 32 output dims:
@@ -945,9 +1013,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
         const int iu = i + 8 * u < n ? i + 8 * u : i;
         a[u] = ws_acc[((g + c0 + iu) * group + h) * kHeadDim + d0 + dd];
       }
+      // a piece of weight 0 adds nothing; its slot may never have been
+      // written (a wavefront with an empty range), so it is not multiplied
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (i + 8 * u < n) acc += wts[i + 8 * u] * a[u];
+        if (i + 8 * u < n && wts[i + 8 * u] != 0.0f) acc += wts[i + 8 * u] * a[u];
     }
   }
   // L was summed per thread over its pieces; combine across the block
@@ -984,8 +1054,11 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
   const float c_log2 = sm_scale * 1.4426950408889634f;
   const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
   const bool packed = plan.group <= 8, mq = qt.n_qtok > 1;
-  auto kern = packed ? (mq ? decode_attn_splitk_kernel<true, true> : decode_attn_splitk_kernel<true, false>)
-                     : (mq ? decode_attn_splitk_kernel<false, true> : decode_attn_splitk_kernel<false, false>);
+  const int nt = decode_column_tiles(plan.group);
+  auto kern = nt == 3   ? decode_attn_splitk_kernel<false, true, 3>
+              : nt == 2 ? decode_attn_splitk_kernel<false, true, 2>
+              : packed  ? (mq ? decode_attn_splitk_kernel<true, true, 1> : decode_attn_splitk_kernel<true, false, 1>)
+                        : (mq ? decode_attn_splitk_kernel<false, true, 1> : decode_attn_splitk_kernel<false, false, 1>);
   hipLaunchKernelGGL(kern, dim3(plan.n_waves), dim3(64), 0, stream, P.base, P.num_pages, P.hkv,
                      layer, n_seq, n_q_heads, qc, q, k_new, v_new, in_dtype, q_positions,
                      rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table, page_table_stride,
@@ -1006,13 +1079,18 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
   return hipGetLastError();
 }
 
-int decode_waves_per_cu() {
+int decode_waves_per_cu(int nt) {
   int lo = 1 << 30;
-  const void* kernels[4] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false>),
-                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false>),
-                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true>),
-                            reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true>)};
-  for (const void* k : kernels) {
+  const void* one[4] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false, 1>),
+                        reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false, 1>),
+                        reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true, 1>),
+                        reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 1>)};
+  const void* two[1] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 2>)};
+  const void* three[1] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 3>)};
+  const int n = nt == 3 || nt == 2 ? 1 : 4;
+  const void* const* kernels = nt == 3 ? three : nt == 2 ? two : one;
+  for (int i = 0; i < n; ++i) {
+    const void* k = kernels[i];
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k, 64, 0) != hipSuccess) return 0;
     lo = blocks < lo ? blocks : lo;

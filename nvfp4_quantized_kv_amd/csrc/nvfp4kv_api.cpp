@@ -83,41 +83,45 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   return L;
 }
 
-// Resident wavefronts of the decode kernel on the current device: CUs times
-// one-wavefront workgroups per CU.  Cached per device; if the device cannot be
-// queried (no GPU), 256 CUs x 8 is assumed so that size queries still work.
-int resident_decode_waves() {
-  static int cached[64] = {0};
+// Resident wavefronts of the decode kernels with `nt` column tiles on the
+// current device: CUs times one-wavefront workgroups per CU.  Cached per
+// device; if the device cannot be queried (no GPU), 256 CUs x 8 (x 4 for
+// several tiles) is assumed so that size queries still work.
+int resident_decode_waves(int nt) {
+  static int cached[64][4] = {};
+  const int fallback = nt > 1 ? 256 * 4 : 256 * 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
-    return 256 * 8;
+    return fallback;
   }
-  if (cached[dev] == 0) {
+  if (cached[dev][nt] == 0) {
     int cus = 0;
-    const int per_cu = nvfp4kv::decode_waves_per_cu();
+    const int per_cu = nvfp4kv::decode_waves_per_cu(nt);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
       (void)hipGetLastError();
-      return 256 * 8;
+      return fallback;
     }
-    cached[dev] = cus * per_cu;
+    cached[dev][nt] = cus * per_cu;
   }
-  return cached[dev];
+  return cached[dev][nt];
 }
 
 // Split-K plan.  The flattened (sequence, kv head, page) work is shared
 // equally by n_waves one-wavefront workgroups.  pages_per_split 0 launches
 // one wavefront per resident slot of the device; a positive value asks for
-// about that many pages per wavefront at max_seq_len.
+// about that many pages per wavefront at max_seq_len.  n_q_heads counts the
+// query columns of the launch (query heads x new tokens), at most
+// max_group per kv head.
 int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t max_seq_len,
-              int32_t pages_per_split, nvfp4kv::DecodePlan* out) {
+              int32_t pages_per_split, nvfp4kv::DecodePlan* out, int max_group = 16) {
   if (n_seq <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
   if (n_seq > 65535) return fail(NVFP4KV_ERR_UNSUPPORTED, "n_seq %d too large (at most 65535)", n_seq);
   if (n_q_heads <= 0 || n_q_heads % p->num_kv_heads != 0)
     return fail(NVFP4KV_ERR_INVALID_ARG, "n_q_heads %d must be a positive multiple of num_kv_heads %d", n_q_heads, p->num_kv_heads);
   const int group = n_q_heads / p->num_kv_heads;
-  if (group > 16) return fail(NVFP4KV_ERR_UNSUPPORTED, "%d query heads per kv head unsupported (at most 16)", group);
+  if (group > max_group) return fail(NVFP4KV_ERR_UNSUPPORTED, "%d query heads per kv head unsupported (at most %d)", group, max_group);
   if (max_seq_len <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "max_seq_len must be positive");
   const int64_t max_pages = (max_seq_len + 63) / 64;
   if (max_pages > ((int64_t)1 << 30)) return fail(NVFP4KV_ERR_INVALID_ARG, "max_seq_len too large");
@@ -126,7 +130,7 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   const int64_t max_total = (int64_t)n_seq * p->num_kv_heads * max_pages;
   int64_t waves;
   if (pages_per_split == 0)
-    waves = resident_decode_waves();
+    waves = resident_decode_waves(nvfp4kv::decode_column_tiles(group));
   else
     waves = (max_total + pages_per_split - 1) / pages_per_split;
   waves = std::max<int64_t>(1, std::min<int64_t>(waves, std::min<int64_t>(max_total, (int64_t)1 << 24)));
@@ -135,9 +139,7 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   return NVFP4KV_OK;
 }
 
-int check_workspace(const nvfp4kv_pool* p, int32_t n_seq, const nvfp4kv::DecodePlan& plan,
-                    const void* workspace, size_t workspace_bytes) {
-  const size_t need = nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+int check_workspace(size_t need, const void* workspace, size_t workspace_bytes) {
   if (workspace == nullptr || workspace_bytes < need)
     return fail(NVFP4KV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(NVFP4KV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -210,10 +212,10 @@ static nvfp4kv::QTokens one_token(const nvfp4kv::DecodePlan& plan) {
   return nvfp4kv::QTokens{1, 0, plan.group};
 }
 
-// Query tokens per launch of a multi-token decode: as many as fit 16 MFMA
-// columns with every query head of a kv head (at least 1).
+// Query tokens per launch of a multi-token decode: as many as fit the
+// kernel's 48 columns with every query head of a kv head (at least 1).
 static int tokens_per_launch(int heads, int n_qtok) {
-  return std::max(1, std::min(n_qtok, 16 / heads));
+  return std::max(1, std::min(n_qtok, nvfp4kv::kMaxDecodeColumns / heads));
 }
 
 // Checks shared by the decode entry points; fills `plan`.
@@ -224,12 +226,12 @@ static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                         const int32_t* page_table, int32_t page_table_stride,
                         const int32_t* seq_lens, int64_t max_seq_len, float sm_scale,
                         const void* workspace, size_t workspace_bytes, int32_t pages_per_split,
-                        nvfp4kv::DecodePlan* plan) {
+                        nvfp4kv::DecodePlan* plan, int max_group = 16) {
   int rc;
   if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
   if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
   if ((rc = check_dtype(q_dtype, "query")) != NVFP4KV_OK) return rc;
-  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, plan)) != NVFP4KV_OK) return rc;
+  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, plan, max_group)) != NVFP4KV_OK) return rc;
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr)
     return fail(NVFP4KV_ERR_INVALID_ARG, "null q, page_table or seq_lens");
   if (!aligned(q, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q must be 16-byte aligned");
@@ -243,7 +245,7 @@ static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   if (page_table_stride < max_pages)
     return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride %d smaller than the %lld pages of max_seq_len", page_table_stride, (long long)max_pages);
   if (!(sm_scale >= 0.0f) || !isfinite(sm_scale)) return fail(NVFP4KV_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
-  return check_workspace(p, n_seq, *plan, workspace, workspace_bytes);
+  return check_workspace(nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, *plan), workspace, workspace_bytes);
 }
 
 int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
@@ -279,7 +281,7 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
   if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan)) != NVFP4KV_OK) return rc;
   if (seq_lens == nullptr || out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null seq_lens or out");
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
-  if ((rc = check_workspace(p, n_seq, plan, workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
+  if ((rc = check_workspace(nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan), workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
   hipError_t e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out,
                                                workspace, plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
@@ -327,6 +329,23 @@ static int check_multi_shape(const nvfp4kv_pool* p, int32_t n_qtok, int32_t n_q_
   return NVFP4KV_OK;
 }
 
+// Plans of the launches of a multi-token decode: every launch takes `per`
+// tokens but the last, which takes the rest; the workspace is reused in
+// stream order, so it must hold the larger of the two plans' partials.
+static int multi_plans(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok, int heads, int per,
+                       int64_t max_seq_len, int32_t pages_per_split, nvfp4kv::DecodePlan* full,
+                       nvfp4kv::DecodePlan* last, size_t* need) {
+  const int hkv = p->num_kv_heads;
+  int rc = make_plan(p, n_seq, hkv * per * heads, max_seq_len, pages_per_split, full,
+                     nvfp4kv::kMaxDecodeColumns);
+  if (rc != NVFP4KV_OK) return rc;
+  const int rest = n_qtok % per == 0 ? per : n_qtok % per;
+  rc = make_plan(p, n_seq, hkv * rest * heads, max_seq_len, pages_per_split, last, nvfp4kv::kMaxDecodeColumns);
+  if (rc != NVFP4KV_OK) return rc;
+  *need = std::max(nvfp4kv::ws_bytes(n_seq, hkv, *full), nvfp4kv::ws_bytes(n_seq, hkv, *last));
+  return NVFP4KV_OK;
+}
+
 size_t nvfp4kv_decode_multi_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok,
                                             int32_t n_q_heads, int64_t max_seq_len,
                                             int32_t pages_per_split) {
@@ -334,9 +353,12 @@ size_t nvfp4kv_decode_multi_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq
   if (check_pool_shape(p) != NVFP4KV_OK) return 0;
   int cols = 0, per = 0;
   if (check_multi_shape(p, n_qtok, n_q_heads, &cols, &per) != NVFP4KV_OK) return 0;
-  nvfp4kv::DecodePlan plan;
-  if (make_plan(p, n_seq, p->num_kv_heads * cols, max_seq_len, pages_per_split, &plan) != NVFP4KV_OK) return 0;
-  return nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+  nvfp4kv::DecodePlan full, last;
+  size_t need = 0;
+  if (multi_plans(p, n_seq, n_qtok, n_q_heads / p->num_kv_heads, per, max_seq_len, pages_per_split, &full,
+                  &last, &need) != NVFP4KV_OK)
+    return 0;
+  return need;
 }
 
 int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_qtok,
@@ -351,19 +373,23 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
   if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
   int cols = 0, per = 0;
   if ((rc = check_multi_shape(p, n_qtok, n_q_heads, &cols, &per)) != NVFP4KV_OK) return rc;
-  nvfp4kv::DecodePlan plan;
+  nvfp4kv::DecodePlan full, last;
   rc = check_decode(p, layer, n_seq, p->num_kv_heads * cols, q, nullptr, nullptr, q_dtype, q_positions,
                     rope_cos, rope_sin, max_pos, page_table, page_table_stride, seq_lens, max_seq_len,
-                    sm_scale, workspace, workspace_bytes, pages_per_split, &plan);
+                    sm_scale, workspace, workspace_bytes, pages_per_split, &full, nvfp4kv::kMaxDecodeColumns);
   if (rc != NVFP4KV_OK) return rc;
   if (out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null out");
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
   const int heads = n_q_heads / p->num_kv_heads;
+  size_t need = 0;
+  if ((rc = multi_plans(p, n_seq, n_qtok, heads, per, max_seq_len, pages_per_split, &full, &last, &need)) !=
+      NVFP4KV_OK)
+    return rc;
+  if ((rc = check_workspace(need, workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
   // one split + reduce pair per launch's tokens; the workspace is reused in
   // stream order
   for (int t0 = 0; t0 < n_qtok; t0 += per) {
-    nvfp4kv::DecodePlan pl = plan;
-    pl.group = std::min(per, n_qtok - t0) * heads;
+    const nvfp4kv::DecodePlan& pl = t0 + per <= n_qtok ? full : last;
     const nvfp4kv::QTokens qt{n_qtok, t0, heads};
     hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, nullptr, nullptr,
                                                  (int)q_dtype, q_positions, rope_cos, rope_sin, page_table,

@@ -21,7 +21,7 @@ struct LaunchPool {
 // flattened (sequence, kv head, page) work equally.
 struct DecodePlan {
   int n_waves;
-  int group;             // query heads per kv head
+  int group;             // query columns per kv head (query heads x new tokens of the launch)
 };
 
 // Partial slots: one per (segment, wave) pair that overlaps, indexed segment
@@ -44,8 +44,15 @@ inline size_t ws_bytes(int n_seq, int hkv, const DecodePlan& pl) {
   return ws_ml_offset(n_seq, hkv, pl) + ws_slots(n_seq, hkv, pl) * pl.group * 2 * sizeof(float);
 }
 
-// Resident one-wavefront decode workgroups per CU (0 if the query fails).
-int decode_waves_per_cu();
+// Query columns per kv head that one decode launch takes: one to three
+// column tiles of 16 (a plain decode step has the kv head's query heads, at
+// most 16; several new tokens per sequence fill up to 48).
+constexpr int kMaxDecodeColumns = 48;
+inline int decode_column_tiles(int group) { return (group + 15) / 16; }
+
+// Resident one-wavefront decode workgroups per CU for the kernels with `nt`
+// column tiles (0 if the query fails).
+int decode_waves_per_cu(int nt);
 
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,

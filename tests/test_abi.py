@@ -168,13 +168,17 @@ def test_decode_multi_rejects_bad_arguments(kv):
 
 
 def test_decode_multi_workspace_query(kv):
-    """One launch's partials: floor(16 / 6) = 2 tokens x 6 heads = 12 columns
-    per kv head for 24 query heads over 4 kv heads, so 2x the one-token need."""
+    """The partials of the largest launch: a launch takes up to 48 query
+    columns per kv head, so with 6 query heads per kv head (24 over 4) 7
+    tokens are one launch of 42 columns (7x the one-token need at the same
+    split), and 10 tokens are launches of 8 and 2 tokens (8x)."""
     d = _desc(kv)
     L = kv.lib()
     one = L.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 3, 24, 470001, 64)
     m1 = L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 1, 24, 470001, 64)
     m7 = L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 7, 24, 470001, 64)
+    m10 = L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 10, 24, 470001, 64)
     assert m1 == one
-    assert 2 * one - 1024 <= m7 <= 2 * one + 1024
+    assert 7 * one - 1024 <= m7 <= 7 * one + 1024
+    assert 8 * one - 1024 <= m10 <= 8 * one + 1024
     assert L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 0, 24, 1000, 0) == 0

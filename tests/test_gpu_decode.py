@@ -160,6 +160,23 @@ def test_decode_split_count_invariance():
         assert np.abs(o - outs[0]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
 
 
+def test_decode_ignores_unwritten_workspace():
+    """More wavefronts than pages leaves wavefronts with empty ranges inside a
+    segment's span; their partial slots are never written.  With the
+    workspace filled with NaN bytes beforehand the output must still match
+    the oracle (the reduce gives those slots no weight and never multiplies
+    them)."""
+    c = Case(12, [70, 3, 200], 2, 12)
+    need = c.kv.nvfp4kv_decode_workspace_bytes(c.pool, len(c.lens), c.hq, max(c.lens), 0)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = c.kv.nvfp4kv_decode_attn(
+        c.pool, 0, c.q.cuda(), torch.from_numpy(c.q_pos).cuda(), torch.from_numpy(c.table).cuda(),
+        torch.tensor(c.lens, dtype=torch.int32).cuda(), max(c.lens), 1 / np.sqrt(128), workspace=ws,
+        rope_cos=c.rc, rope_sin=c.rs)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), c.oracle(), "NaN-filled workspace")
+
+
 def test_decode_sm_scale_zero_and_large():
     c = Case(10, [900], 2, 4)
     assert_attention_close(c.gpu(sm_scale=0.0), c.oracle(sm_scale=0.0), "sm_scale 0")

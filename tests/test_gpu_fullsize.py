@@ -95,6 +95,32 @@ def test_three_long_sequences_full_size():
     torch.cuda.empty_cache()
 
 
+def test_three_long_multi_query_full_size():
+    """Speculative verification at the full three-session size: the last 8
+    tokens of every sequence as queries (48 columns per kv head, one launch),
+    sampled sequences against the oracle."""
+    from nvfp4_quantized_kv_amd import workloads as W
+    wl, st = _step("three_long", layers=2)
+    oc, os_ = _oracle_tables(wl, st)
+    layer = 1
+    st.append(layer)
+    st.prepare_multi(8)
+    out = st.decode_multi(layer).cpu().numpy()
+    for seq in (2, 0):
+        T = wl.seq_lens[seq]
+        npg = (T + 63) // 64
+        pages = torch.from_numpy(st.table_np[seq, :npg].astype(np.int64)).cuda()
+        pool = st.pool.data.view(wl.layers, st.pool.num_pages, wl.hkv * 9216)[layer]
+        compact = pool.index_select(0, pages).contiguous().view(-1).cpu().numpy()
+        ref = oracle.decode_attention_multi(compact, npg, wl.hkv, 0, wl.rotary_dim, wl.hadamard,
+                                            st.mq[layer][seq:seq + 1].float().cpu().numpy(),
+                                            st.mq_pos[seq:seq + 1].cpu().numpy(),
+                                            np.arange(npg, dtype=np.int32)[None], [T], W.sm_scale(), oc, os_)
+        assert_attention_close(out[seq:seq + 1], ref, f"three_long multi-query seq {seq}")
+    del st
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["single600k", "single600k_nohad"])
 def test_single_600k_sequence_full_size(name):
     wl, st = _step(name, layers=2)

@@ -38,17 +38,22 @@ def _oracle(c, q, pos):
 
 
 MULTI_CASES = [
-    # (lens, hkv, hq, m, rotary): columns per launch = floor(16 / (hq/hkv)) tokens x heads
-    ([3000, 1234], 4, 24, 2, 32),      # 6 heads: 2 tokens per launch, one launch, unpacked
-    ([3000, 1234], 4, 24, 7, 32),      # 4 launches, the last with one token
-    ([700, 65, 8], 4, 24, 8, 32),      # a sequence of exactly 8 tokens: token 0 sees one
-    ([129, 4100], 2, 2, 16, 16),       # 1 head: 16 tokens in one launch
-    ([513, 70], 2, 2, 5, 0),           # no RoPE
+    # (lens, hkv, hq, m, rotary).  A launch takes floor(48 / heads) tokens,
+    # every query head of a kv head per token: columns in tiles of 16 (one
+    # to three per wavefront), packed weights at 8 columns or fewer.
+    ([3000, 1234], 4, 24, 2, 32),      # 6 heads: 12 columns, one tile
+    ([3000, 1234], 4, 24, 7, 32),      # 42 columns, three tiles, the last partial
+    ([700, 65, 8], 4, 24, 8, 32),      # 48 columns; a sequence of exactly 8 tokens: token 0 sees one
+    ([129, 4100], 2, 2, 16, 16),       # 1 head: 16 tokens, one tile
+    ([513, 70], 2, 2, 5, 0),           # no RoPE; 5 columns, packed
     ([2000, 64 + 3], 2, 4, 4, 32),     # 2 heads: 8 columns, packed; a page edge inside the tail
     ([1500], 1, 8, 2, 128),            # 8 heads: 16 columns; full-width RoPE
-    ([900, 300], 1, 16, 3, 32),        # 16 heads: one token per launch, 3 launches
+    ([900, 300], 1, 16, 3, 32),        # 16 heads: 48 columns in one launch
+    ([3000, 1234], 4, 24, 10, 32),     # launches of 8 tokens (three tiles) and 2 tokens (one tile)
+    ([2500, 90], 2, 2, 40, 32),        # 1 head: 40 tokens, three tiles; causal cut over a page
+    ([777, 1300], 2, 8, 5, 32),        # 4 heads: 20 columns, two tiles
+    ([5000, 64], 1, 1, 64, 32),        # 64 tokens: launches of 48 and 16; a 64-token sequence
 ]
-
 
 @pytest.mark.parametrize("idx", range(len(MULTI_CASES)))
 def test_multi_query_matches_oracle(idx):
@@ -65,6 +70,23 @@ def test_multi_query_split_plans(pages_per_split):
     c = Case(620, [1000, 3, 2049, 777], 2, 12, rotary=32)
     q, pos = _queries(c, 3, 720, torch.float32)
     assert_attention_close(_run(c, q, pos, pages_per_split), _oracle(c, q, pos), f"pps {pages_per_split}")
+
+
+@pytest.mark.parametrize("m", [3, 8])
+def test_multi_query_ignores_unwritten_workspace(m):
+    """Short sequences, far more wavefronts than pages, and a workspace full of
+    NaN bytes: slots of wavefronts with empty ranges are never written and
+    must not reach the output (one and three column tiles)."""
+    c = Case(650 + m, [700, 65, 8], 4, 24, rotary=32)
+    q, pos = _queries(c, m, 750 + m, torch.bfloat16)
+    need = c.kv.nvfp4kv_decode_multi_workspace_bytes(c.pool, len(c.lens), m, c.hq, max(c.lens), 0)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = c.kv.nvfp4kv_decode_attn_multi(
+        c.pool, 0, q.contiguous().cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(c.table).cuda(),
+        torch.tensor(c.lens, dtype=torch.int32).cuda(), max(c.lens), 1 / np.sqrt(128), workspace=ws,
+        rope_cos=c.rc, rope_sin=c.rs)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), _oracle(c, q, pos), f"NaN-filled workspace, m {m}")
 
 
 def test_multi_query_one_token_is_decode():
