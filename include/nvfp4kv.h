@@ -204,10 +204,11 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
  *   workspace   at least nvfp4kv_decode_multi_workspace_bytes(...) bytes,
  *               256-byte aligned; its contents on entry do not matter
  * Other arguments as in nvfp4kv_decode_attn.  The cache is read once per
- * floor(16 / (n_q_heads / num_kv_heads)) query tokens (16 matrix columns
- * hold that many tokens' query heads), each such launch followed by its
- * reduce; 1 <= n_qtok <= 64.  n_qtok = 1 computes what
- * nvfp4kv_decode_attn computes without k_new/v_new. */
+ * floor(48 / (n_q_heads / num_kv_heads)) query tokens (a launch takes up to
+ * 48 matrix columns, each a query head of one token), each such launch
+ * followed by its reduce; 1 <= n_qtok <= 64.  n_qtok = 1 computes what
+ * nvfp4kv_decode_attn computes without k_new/v_new.  The workspace is
+ * reused by the launches in stream order. */
 size_t nvfp4kv_decode_multi_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok,
                                             int32_t n_q_heads, int64_t max_seq_len,
                                             int32_t pages_per_split);
