@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM copy-ceiling measurement")
+    ap.add_argument("--spill", action="store_true",
+                    help="time host spill and restore of the longest sequence's pages instead")
     ap.add_argument("--multi", type=int, default=0,
                     help="time multi-query decode instead: this many new query tokens per sequence")
     return ap.parse_args()
@@ -156,6 +158,8 @@ def main():
     log(f"warmup done ({args.warmup} steps)")
     if args.multi:
         return bench_multi(args, step, wl, torch, kv, W, ceiling)
+    if args.spill:
+        return bench_spill(args, step, wl, torch, kv)
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -306,6 +310,78 @@ def bench_multi(args, step, wl, torch, kv, W, ceiling):
         "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+PEAK_PCIE_GBPS = 64.0          # PCIe 5.0 x16 host link, per direction
+
+
+def bench_spill(args, step, wl, torch, kv):
+    """Host spill and restore: every page of the longest sequence (all layers
+    and kv heads) to a pinned host arena and back into the same page ids."""
+    import numpy as np
+    seq = int(np.argmax(wl.seq_lens))
+    npg = (wl.seq_lens[seq] + 63) // 64
+    ids = torch.from_numpy(step.table_np[seq, :npg].copy()).to(step.pool.data.device)
+    page_bytes = kv.nvfp4kv_page_bytes(step.pool)
+    total = page_bytes * npg
+    log(f"spill: {npg} pages of {page_bytes} bytes ({total / 1e9:.2f} GB) to pinned host memory")
+    arena = torch.empty((npg, wl.layers, wl.hkv, 9216), dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    kv.nvfp4kv_spill_pages(step.pool, ids, arena)
+    kv.nvfp4kv_restore_pages(step.pool, ids, arena)
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    t_sp, t_re = [], []
+    for _ in range(reps):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        kv.nvfp4kv_spill_pages(step.pool, ids, arena)
+        e1.record(stream)
+        kv.nvfp4kv_restore_pages(step.pool, ids, arena)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        t_sp.append(e0.elapsed_time(e1) * 1e-3)
+        t_re.append(e1.elapsed_time(e2) * 1e-3)
+    sp, re_ = sum(t_sp) / reps, sum(t_re) / reps
+    # the arena holds the pool's bytes: sampled pages, every layer
+    rng = np.random.default_rng(0)
+    view = step.pool.data.view(wl.layers, step.pool.num_pages, wl.hkv * 9216)
+    for i in rng.choice(npg, 8, replace=False):
+        got = arena[int(i)].reshape(wl.layers, -1)
+        want = view[:, int(ids[int(i)])].cpu()
+        assert torch.equal(got, want), f"arena page {i} differs from the pool"
+    log(f"spill {total / sp / 1e9:.2f} GB/s ({npg / sp:.0f} pages/s), restore {total / re_ / 1e9:.2f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(npg, 256)
+        sub = view[:, ids[:n].long()].cpu().numpy()            # [layers][n][hkv*9216]: a pool of n pages
+        t0 = time.perf_counter()
+        reps_cpu = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.spill_pages(sub, wl.layers, n, wl.hkv, np.arange(n))
+            reps_cpu += 1
+        secs = (time.perf_counter() - t0) / reps_cpu
+        cpu = {"value": round(n * page_bytes / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle spill_pages of {n} pages ({n * page_bytes / 1e6:.0f} MB) host to host, "
+                         f"{reps_cpu} repetitions in ~10 s"}
+    rec = {
+        "metric": "NVFP4 page spill to pinned host memory, GB/s (pages/s)",
+        "value": round(total / sp / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": reps, "warmup": 1, "ms_per_step": round((sp + re_) * 1e3, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: the {wl.seq_lens[seq]}-token sequence's {npg} pages, "
+                               f"{wl.layers} layers x {wl.hkv} kv heads ({page_bytes} bytes a page)",
+                   "step": "nvfp4kv_spill_pages then nvfp4kv_restore_pages of the same page ids"},
+        "pages_per_s": round(npg / sp, 1),
+        "restore_gbps": round(total / re_ / 1e9, 2),
+        "restore_pages_per_s": round(npg / re_, 1),
+        "roofline": {"bound": "pcie", "kernel": "page_copy_kernel", "achieved": round(total / sp / 1e9, 2),
+                     "peak": PEAK_PCIE_GBPS, "unit": "GB/s", "frac": round(total / sp / 1e9 / PEAK_PCIE_GBPS, 4),
+                     "traffic": None, "restore_achieved": round(total / re_ / 1e9, 2)},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 

@@ -231,6 +231,35 @@ int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const i
                     void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
                     hipStream_t stream);
 
+/* Bytes of one spilled page: every layer's and every kv head's 9216-byte
+ * block of one page id, num_layers * num_kv_heads * 9216 (host; 0 for an
+ * invalid pool). */
+size_t nvfp4kv_page_bytes(const nvfp4kv_pool* p);
+
+/* Host spill and restore of whole cache pages: the pinned host arena of the
+ * release post's section "Multi-level prefix reuse with host-KV safety net"
+ * (pages are copied device to host before eviction, and back on reuse).
+ * nvfp4kv_spill_pages copies page page_ids[i] of every layer and kv head to
+ * arena entry i; nvfp4kv_restore_pages copies arena entry i back into page
+ * page_ids[i].  The bytes are copied unchanged, so a page can come back
+ * under another page id (the page table then names the new id).
+ *   page_ids    [n_pages] int32 in device memory or pinned host memory; ids
+ *               outside [0, num_pages) are skipped (their arena entry is
+ *               left as it was on spill)
+ *   arena       [n_pages][num_layers][num_kv_heads][9216] bytes, at least
+ *               n_pages * nvfp4kv_page_bytes(p) bytes, 16-byte aligned, in
+ *               pinned host memory (hipHostMalloc) or in device memory of
+ *               the current device; any other pointer is refused
+ *               (NVFP4KV_ERR_INVALID_ARG) before anything is launched
+ * One kernel, asynchronous on `stream`; the arena must stay allocated until
+ * it has run.  The ids of a restore must be distinct: entries are copied in
+ * parallel, so a page id listed twice ends with bytes of either entry, mixed
+ * (a spill may list an id several times).  n_pages 0 does nothing. */
+int nvfp4kv_spill_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids, void* arena,
+                        size_t arena_bytes, hipStream_t stream);
+int nvfp4kv_restore_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids,
+                          const void* arena, size_t arena_bytes, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on the same thread. */
 const char* nvfp4kv_last_error(void);

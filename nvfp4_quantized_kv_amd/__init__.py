@@ -72,6 +72,12 @@ def _load():
     L.nvfp4kv_decode_reduce.restype = ctypes.c_int
     L.nvfp4kv_dequant.argtypes = [PD, i32, i32, P, P, P, ctypes.c_int, i32, P]
     L.nvfp4kv_dequant.restype = ctypes.c_int
+    L.nvfp4kv_page_bytes.argtypes = [PD]
+    L.nvfp4kv_page_bytes.restype = sz
+    L.nvfp4kv_spill_pages.argtypes = [PD, i32, P, P, sz, P]
+    L.nvfp4kv_spill_pages.restype = ctypes.c_int
+    L.nvfp4kv_restore_pages.argtypes = [PD, i32, P, P, sz, P]
+    L.nvfp4kv_restore_pages.restype = ctypes.c_int
     L.nvfp4kv_last_error.argtypes = []
     L.nvfp4kv_last_error.restype = ctypes.c_char_p
     L.nvfp4kv_version.argtypes = []
@@ -84,7 +90,7 @@ _lib = _load()
 EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
             "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_splits",
             "nvfp4kv_decode_reduce", "nvfp4kv_decode_multi_workspace_bytes", "nvfp4kv_decode_attn_multi",
-            "nvfp4kv_dequant",
+            "nvfp4kv_dequant", "nvfp4kv_page_bytes", "nvfp4kv_spill_pages", "nvfp4kv_restore_pages",
             "nvfp4kv_last_error", "nvfp4kv_version"]
 
 
@@ -320,6 +326,40 @@ def nvfp4kv_dequant(pool: Pool, layer: int, slots: torch.Tensor, out_dtype=torch
            _lib.nvfp4kv_dequant(ctypes.byref(d), layer, n_tok, _ptr(slots), _ptr(k_out), _ptr(v_out),
                                 code, int(unrotate), _stream(stream)))
     return k_out, v_out
+
+
+def nvfp4kv_page_bytes(pool: Pool) -> int:
+    d = pool.desc()
+    return _lib.nvfp4kv_page_bytes(ctypes.byref(d))
+
+
+def nvfp4kv_spill_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """Copy whole pages (every layer and kv head) to arena [n][num_layers]
+    [num_kv_heads][9216] uint8: pinned host memory by default, or the given
+    pinned-host or device tensor.  page_ids: int32 on the device or pinned."""
+    assert page_ids.dtype == torch.int32 and page_ids.is_contiguous()
+    n = page_ids.numel()
+    shape = (n, pool.num_layers, pool.num_kv_heads, 9216)
+    if arena is None:
+        arena = torch.empty(shape, dtype=torch.uint8, pin_memory=True)
+    assert arena.dtype == torch.uint8 and arena.is_contiguous()
+    d = pool.desc()
+    _check("nvfp4kv_spill_pages",
+           _lib.nvfp4kv_spill_pages(ctypes.byref(d), n, _ptr(page_ids), _ptr(arena),
+                                    arena.numel(), _stream(stream)))
+    return arena
+
+
+def nvfp4kv_restore_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tensor, stream=None) -> None:
+    """Copy arena entry i back into page page_ids[i] of every layer and kv
+    head; the ids must be distinct."""
+    assert page_ids.dtype == torch.int32 and page_ids.is_contiguous()
+    assert arena.dtype == torch.uint8 and arena.is_contiguous()
+    d = pool.desc()
+    _check("nvfp4kv_restore_pages",
+           _lib.nvfp4kv_restore_pages(ctypes.byref(d), page_ids.numel(), _ptr(page_ids), _ptr(arena),
+                                      arena.numel(), _stream(stream)))
 
 
 def default_sm_scale() -> float:

@@ -403,6 +403,69 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
   return NVFP4KV_OK;
 }
 
+size_t nvfp4kv_page_bytes(const nvfp4kv_pool* p) {
+  g_last_error.clear();
+  if (check_pool_shape(p) != NVFP4KV_OK) return 0;
+  return (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::kPoolBlockBytes;
+}
+
+// Device address at which kernels reach `ptr`: device memory of the current
+// device as is, pinned host memory through its device mapping.  Anything
+// else (pageable host memory, another device's memory) is refused before any
+// launch, since a kernel access to it would fault.
+static int device_view(const void* ptr, const char* what, uint8_t** out) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, ptr) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(NVFP4KV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", what);
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_fail(hipGetLastError(), "hipGetDevice");
+  if (at.type == hipMemoryTypeDevice) {
+    if (at.device != dev) return fail(NVFP4KV_ERR_INVALID_ARG, "%s is memory of device %d, not of the current device %d", what, at.device, dev);
+    *out = const_cast<uint8_t*>(static_cast<const uint8_t*>(ptr));
+    return NVFP4KV_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer != nullptr && at.hostPointer != nullptr) {
+    *out = static_cast<uint8_t*>(at.devicePointer) +
+           (static_cast<const uint8_t*>(ptr) - static_cast<const uint8_t*>(at.hostPointer));
+    return NVFP4KV_OK;
+  }
+  return fail(NVFP4KV_ERR_INVALID_ARG, "%s is neither device memory nor pinned host memory", what);
+}
+
+static int page_copy(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids, const void* arena,
+                     size_t arena_bytes, bool to_arena, hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if (n_pages < 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_pages must not be negative (got %d)", n_pages);
+  if (n_pages == 0) return NVFP4KV_OK;
+  if (page_ids == nullptr || arena == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null page_ids or arena");
+  if (!aligned(arena, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "arena must be 16-byte aligned");
+  const size_t page = (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::kPoolBlockBytes;
+  if (arena_bytes / page < (size_t)n_pages)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "arena of %zu bytes holds fewer than %d pages of %zu bytes", arena_bytes, n_pages, page);
+  uint8_t* ids_dev = nullptr;
+  uint8_t* arena_dev = nullptr;
+  if ((rc = device_view(page_ids, "page_ids", &ids_dev)) != NVFP4KV_OK) return rc;
+  if ((rc = device_view(arena, "arena", &arena_dev)) != NVFP4KV_OK) return rc;
+  hipError_t e = nvfp4kv::launch_page_copy(launch_pool(p), p->num_layers, n_pages,
+                                           reinterpret_cast<const int32_t*>(ids_dev), arena_dev, to_arena, stream);
+  if (e != hipSuccess) return hip_fail(e, "page copy launch");
+  return NVFP4KV_OK;
+}
+
+int nvfp4kv_spill_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids, void* arena,
+                        size_t arena_bytes, hipStream_t stream) {
+  return page_copy(p, n_pages, page_ids, arena, arena_bytes, true, stream);
+}
+
+int nvfp4kv_restore_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids,
+                          const void* arena, size_t arena_bytes, hipStream_t stream) {
+  return page_copy(p, n_pages, page_ids, arena, arena_bytes, false, stream);
+}
+
 int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const int64_t* slots,
                     void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
                     hipStream_t stream) {

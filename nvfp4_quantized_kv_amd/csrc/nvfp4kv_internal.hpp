@@ -58,6 +58,11 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
                          int dtype, const int64_t* slots, const int32_t* positions,
                          const float* rope_cos, const float* rope_sin, hipStream_t stream);
 
+// Copies whole pages (every layer and kv head) of the n_pages listed page
+// ids between the pool and the arena [n_pages][num_layers][hkv][9216].
+hipError_t launch_page_copy(const LaunchPool& P, int num_layers, int n_pages, const int32_t* page_ids,
+                            uint8_t* arena, bool to_arena, hipStream_t stream);
+
 hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64_t* slots,
                           void* k_out, void* v_out, int dtype, int unrotate, hipStream_t stream);
 

@@ -208,6 +208,35 @@ def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q,
     return out.reshape(n_seq, m, q.shape[2], HEAD_DIM)
 
 
+def spill_pages(pool, num_layers, num_pages, hkv, page_ids):
+    """Host copy of whole cache pages, for the pinned host arena of the
+    release post's section "Multi-level prefix reuse with host-KV safety
+    net" (pages are spilled device to host before eviction and restored
+    later).  A page is every layer's and every kv head's 9216-byte block of
+    that page id; the arena holds page i of the list at
+    arena[i][layer][kvh][9216].  Pool layout [layer][page][kvh][9216]."""
+    pool = np.asarray(pool, np.uint8).reshape(num_layers, num_pages, hkv, BLOCK_BYTES)
+    ids = np.asarray(page_ids, np.int64)
+    arena = np.empty((len(ids), num_layers, hkv, BLOCK_BYTES), np.uint8)
+    for i, pid in enumerate(ids):
+        arena[i] = pool[:, pid]
+    return arena
+
+
+def restore_pages(pool, num_layers, num_pages, hkv, page_ids, arena):
+    """The reverse of spill_pages: page i of the arena back into page id
+    page_ids[i] of the pool (every layer and kv head), in place.  The ids
+    must be distinct (two arena pages cannot both become one page)."""
+    ids = np.asarray(page_ids, np.int64)
+    if len(np.unique(ids)) != len(ids):
+        raise ValueError("restore_pages: page ids must be distinct")
+    view = np.asarray(pool).reshape(num_layers, num_pages, hkv, BLOCK_BYTES)
+    arena = np.asarray(arena, np.uint8).reshape(-1, num_layers, hkv, BLOCK_BYTES)
+    for i, pid in enumerate(ids):
+        view[:, pid] = arena[i]
+    return pool
+
+
 def reference_attention(q, q_pos, k, v, k_pos, rotary_dim, sm_scale, cos_tab=None, sin_tab=None):
     """fp64 attention on unquantized rows for one sequence: q [hq][128], k/v [T][hkv][128]."""
     q = _c(q, np.float32)

@@ -146,6 +146,29 @@ def test_dequant_rejects_bad_arguments(kv):
     assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 0, 4096, 4096, 4096, 0, 0, None) == 0
 
 
+def test_page_bytes_and_spill_argument_checks(kv):
+    """A spilled page is every layer's and kv head's 9216-byte block; the
+    spill/restore calls reject bad sizes and pointers before any launch (a
+    pageable host buffer is neither device nor pinned memory)."""
+    d = _desc(kv)
+    L = kv.lib()
+    assert L.nvfp4kv_page_bytes(ctypes.byref(d)) == 2 * 4 * 9216
+    assert L.nvfp4kv_page_bytes(None) == 0
+    page = 2 * 4 * 9216
+    host = (ctypes.c_uint8 * (3 * page + 16))()
+    ids = (ctypes.c_int32 * 3)(0, 1, 2)
+    a16 = (ctypes.addressof(host) + 15) // 16 * 16
+    for fn in (L.nvfp4kv_spill_pages, L.nvfp4kv_restore_pages):
+        assert fn(ctypes.byref(d), 0, None, None, 0, None) == 0            # nothing to do
+        assert fn(ctypes.byref(d), -1, ctypes.addressof(ids), a16, 3 * page, None) == -1
+        assert fn(ctypes.byref(d), 3, None, a16, 3 * page, None) == -1
+        assert fn(ctypes.byref(d), 3, ctypes.addressof(ids), None, 3 * page, None) == -1
+        assert fn(ctypes.byref(d), 3, ctypes.addressof(ids), a16 + 1, 3 * page, None) == -1
+        assert fn(ctypes.byref(d), 3, ctypes.addressof(ids), a16, 3 * page - 1, None) == -1
+        assert fn(ctypes.byref(d), 3, ctypes.addressof(ids), a16, 3 * page, None) == -1
+        assert b"pinned" in L.nvfp4kv_last_error()
+
+
 def _multi(kv, d, n_seq=2, n_qtok=3, hq=24, q=4096, pt=4096, stride=16, lens=4096, max_len=1000,
            scale=0.1, out=4096, ws=4096, ws_bytes=1 << 30, pps=0, qpos=4096):
     return kv.lib().nvfp4kv_decode_attn_multi(ctypes.byref(d), 0, n_seq, n_qtok, hq, q, 1, qpos, 4096, 4096,
