@@ -57,16 +57,16 @@ def lib():
         L.orc_rope_table.argtypes = [f64, ctypes.c_int, f64, ctypes.c_int, P, P]
         L.orc_rope_apply.argtypes = [P, ctypes.c_int, P, P]
         L.orc_hadamard128.argtypes = [P]
-        L.orc_quant_row.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P]
+        L.orc_quant_row.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, P]
         L.orc_dequant_row.argtypes = [P, P, P]
         L.orc_pool_bytes.argtypes = [ctypes.c_int, i64, ctypes.c_int]
         L.orc_pool_bytes.restype = ctypes.c_size_t
         L.orc_pool_read_row.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
                                         ctypes.c_int, P, P]
-        L.orc_append.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        L.orc_append.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
                                  ctypes.c_int, P, P, P, P, P, P]
         L.orc_decode_attention.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P,
+                                           ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                            P, ctypes.c_int, P, f64, P]
         L.orc_reference_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, P, i32, P, P, P, P, P, f64, P]
@@ -122,13 +122,30 @@ def hadamard128(x: np.ndarray) -> np.ndarray:
     return x
 
 
-def quant_row(x, rotary_dim=0, c_row=None, s_row=None, hadamard=False):
+def _rotation(hadamard, signs):
+    """(mode, sign mask) for the C side: mode 0 none, 1 the Hadamard rotation,
+    2 the rotation after negating the elements whose bit is set in `signs`
+    (4 x uint32, bit j of element j)."""
+    mode = int(hadamard)
+    if mode not in (0, 1, 2):
+        raise ValueError("hadamard must be 0, 1 or 2")
+    if mode == 2:
+        m = _c(signs, np.uint32)
+        if m.shape != (4,):
+            raise ValueError("signs must be 4 uint32 words")
+        return mode, m
+    return mode, None
+
+
+def quant_row(x, rotary_dim=0, c_row=None, s_row=None, hadamard=False, signs=None):
+    mode, m = _rotation(hadamard, signs)
     x = _c(x, np.float32)
     codes = np.zeros(64, np.uint8)
     scales = np.zeros(8, np.uint8)
     cr = _c(c_row, np.float32) if rotary_dim else np.zeros(1, np.float32)
     sr = _c(s_row, np.float32) if rotary_dim else np.zeros(1, np.float32)
-    lib().orc_quant_row(_p(x), rotary_dim, _p(cr), _p(sr), int(bool(hadamard)), _p(codes), _p(scales))
+    lib().orc_quant_row(_p(x), rotary_dim, _p(cr), _p(sr), mode, _p(m) if m is not None else None, _p(codes),
+                        _p(scales))
     return codes, scales
 
 
@@ -152,9 +169,10 @@ def pool_read_row(pool, num_pages, hkv, layer, slot, kvh, which):
 
 
 def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, positions,
-           cos_tab=None, sin_tab=None):
+           cos_tab=None, sin_tab=None, signs=None):
     """Quantize and write n_tok tokens into `pool` (a writable uint8 array)."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    mode, m = _rotation(hadamard, signs)
     k = _c(k, np.float32)
     v = _c(v, np.float32)
     n_tok = k.shape[0]
@@ -162,13 +180,14 @@ def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, posit
     positions = _c(positions, np.int32)
     ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
     st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
-    lib().orc_append(_p(pool), num_pages, hkv, rotary_dim, int(bool(hadamard)), layer, n_tok,
+    lib().orc_append(_p(pool), num_pages, hkv, rotary_dim, mode, _p(m) if m is not None else None, layer, n_tok,
                      _p(k), _p(v), _p(slots), _p(positions), _p(ct), _p(st))
 
 
 def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
-                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None):
+                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None):
     """fp64 attention for every sequence and query head over the pool's bytes."""
+    mode, m = _rotation(hadamard, signs)
     q = _c(q, np.float32)
     n_seq, hq, _ = q.shape
     page_table = _c(page_table, np.int32)
@@ -176,14 +195,14 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
     ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
     st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
     lib().orc_decode_attention(_p(_c(pool, np.uint8)), num_pages, hkv, layer, rotary_dim,
-                               int(bool(hadamard)), n_seq, hq, _p(q), _p(_c(q_pos, np.int32)),
+                               mode, _p(m) if m is not None else None, n_seq, hq, _p(q), _p(_c(q_pos, np.int32)),
                                _p(ct), _p(st), _p(page_table), page_table.shape[1],
                                _p(_c(seq_lens, np.int32)), float(sm_scale), _p(out))
     return out
 
 
 def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
-                           page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None):
+                           page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None):
     """fp64 attention of M new query tokens per sequence over the pool's bytes,
     causal among the new tokens: the decode step of speculative verification
     (ai-manual.ru article on "Ninfer 4080", section "Key features": the draft
@@ -204,7 +223,7 @@ def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q,
     out = decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard,
                            q.reshape(n_seq * m, q.shape[2], HEAD_DIM),
                            np.asarray(q_pos, np.int32).reshape(-1), rows, pref, sm_scale,
-                           cos_tab, sin_tab)
+                           cos_tab, sin_tab, signs)
     return out.reshape(n_seq, m, q.shape[2], HEAD_DIM)
 
 

@@ -180,17 +180,25 @@ void orc_hadamard128(float* x)
 /* Quantize one 128-element row to NVFP4 (release post, NVFP4 section):
  *   1. RoPE on the first rotary_dim dims (K and Q only; pass rotary_dim 0
  *      for V or when the row carries no position);
- *   2. Hadamard rotation when `hadamard` is non-zero (K and Q only);
+ *   2. Hadamard rotation when `hadamard` is non-zero (K and Q only).  With
+ *      hadamard == 2 (a variant, not the post's: a randomized rotation) the
+ *      elements whose bit is set in the 128-bit mask `signs` (bit j of
+ *      element j: word j / 32, bit j % 32) are negated first, so the row is
+ *      multiplied by H D / sqrt(128) with D = diag(+-1); Q and K get the same
+ *      D, and (H D q) . (H D k) = q . k still holds;
  *   3. per block of 16: amax, E4M3 scale nearest amax/6;
  *   4. per element: E2M1 code against the block scale;
  *   5. pack two codes per byte, element 2j in the low nibble of byte j.
  * codes: 64 bytes, scales: 8 bytes (block b = elements 16b..16b+15). */
 void orc_quant_row(const float* x_in, int rotary_dim, const float* c, const float* s,
-                   int hadamard, uint8_t* codes, uint8_t* scales)
+                   int hadamard, const uint32_t* signs, uint8_t* codes, uint8_t* scales)
 {
     float x[ORC_D];
     memcpy(x, x_in, sizeof x);
     if (rotary_dim > 0) orc_rope_apply(x, rotary_dim, c, s);
+    if (hadamard == 2)
+        for (int j = 0; j < ORC_D; ++j)
+            if ((signs[j >> 5] >> (j & 31)) & 1u) x[j] = -x[j];
     if (hadamard) orc_hadamard128(x);
     int nib[ORC_D];
     for (int b = 0; b < ORC_NBLK; ++b) {
@@ -275,7 +283,7 @@ static void orc_pool_write_row(uint8_t* pool, int64_t num_pages, int hkv, int la
  * k, v: [n_tok][hkv][128] floats (bf16 inputs are widened exactly first).
  * cos_tab/sin_tab: [max_pos][rotary_dim/2]. */
 void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int hadamard,
-                int layer, int n_tok, const float* k, const float* v,
+                const uint32_t* signs, int layer, int n_tok, const float* k, const float* v,
                 const int64_t* slots, const int32_t* positions,
                 const float* cos_tab, const float* sin_tab)
 {
@@ -286,10 +294,10 @@ void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int h
             uint8_t codes[ORC_ROW_CODE], scales[ORC_NBLK];
             const float* c = rotary_dim > 0 ? cos_tab + (size_t)positions[i] * half : NULL;
             const float* s = rotary_dim > 0 ? sin_tab + (size_t)positions[i] * half : NULL;
-            orc_quant_row(k + ((size_t)i * hkv + g) * ORC_D, rotary_dim, c, s, hadamard,
+            orc_quant_row(k + ((size_t)i * hkv + g) * ORC_D, rotary_dim, c, s, hadamard, signs,
                           codes, scales);
             orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 0, codes, scales);
-            orc_quant_row(v + ((size_t)i * hkv + g) * ORC_D, 0, NULL, NULL, 0, codes, scales);
+            orc_quant_row(v + ((size_t)i * hkv + g) * ORC_D, 0, NULL, NULL, 0, NULL, codes, scales);
             orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 1, codes, scales);
         }
     }
@@ -305,7 +313,7 @@ void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int h
  *   o     = sum_t softmax(z)_t * Vhat_t.
  * All of it in double.  q: [n_seq][hq][128] floats; out: [n_seq][hq][128]. */
 void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int layer,
-                          int rotary_dim, int hadamard, int n_seq, int hq,
+                          int rotary_dim, int hadamard, const uint32_t* signs, int n_seq, int hq,
                           const float* q, const int32_t* q_pos,
                           const float* cos_tab, const float* sin_tab,
                           const int32_t* page_table, int page_table_stride,
@@ -322,7 +330,7 @@ void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int l
                 const float* c = rotary_dim > 0 ? cos_tab + (size_t)q_pos[n] * half : NULL;
                 const float* s = rotary_dim > 0 ? sin_tab + (size_t)q_pos[n] * half : NULL;
                 orc_quant_row(q + ((size_t)n * hq + g * grp + r) * ORC_D, rotary_dim, c, s,
-                              hadamard, codes, scales);
+                              hadamard, signs, codes, scales);
                 orc_dequant_row(codes, scales, qh + (size_t)r * ORC_D);
             }
             /* scores */

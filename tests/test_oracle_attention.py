@@ -281,3 +281,21 @@ def test_multi_query_is_causal():
         out = _multi(cs, pool)
         diff = [j for j in range(4) if not (out[0, j] == base[0, j]).all()]
         assert diff == changed, (t, diff)
+
+
+def test_random_sign_attention_close_to_unquantized_reference():
+    """Not a parity gate: with the randomized rotation on K (append) and Q
+    (decode), NVFP4 attention still tracks fp64 attention on the raw rows."""
+    T, hkv, hq = 256, 1, 2
+    rng = np.random.default_rng(61)
+    k = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    q = rng.standard_normal((1, hq, D)).astype(np.float32)
+    mask = rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+    pool = _pool(4, hkv)
+    oracle.append(pool, 4, hkv, 0, 2, 0, k, v, np.arange(T), np.arange(T), signs=mask)
+    out = oracle.decode_attention(pool, 4, hkv, 0, 0, 2, q, [T - 1], np.array([[0, 1, 2, 3]], np.int32),
+                                  [T], 1 / np.sqrt(128), signs=mask)
+    ref = oracle.reference_attention(q[0], T - 1, k, v, np.arange(T), 0, 1 / np.sqrt(128))
+    rel = np.linalg.norm(out[0] - ref) / np.linalg.norm(ref)
+    assert rel < 0.25

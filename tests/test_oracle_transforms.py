@@ -117,3 +117,46 @@ def test_rope_rotates_half_pairs_and_leaves_the_rest():
     y = oracle.rope_apply(e, R, c[77], s[77])
     assert y[5] == c[77, 5] and y[5 + 16] == s[77, 5]
     assert np.count_nonzero(y) == 2
+
+
+# -- randomized rotation (a variant, not the release post's): negate the
+#    elements whose bit is set in a 128-bit mask, then the Hadamard rotation.
+def _mask_signs(mask):
+    """+-1 per element from the documented convention: element j's bit is
+    bit j % 32 of word j // 32."""
+    return np.array([-1.0 if (int(mask[j // 32]) >> (j % 32)) & 1 else 1.0 for j in range(128)], np.float32)
+
+
+def test_random_sign_rotation_is_rotation_of_negated_row():
+    rng = np.random.default_rng(70)
+    for _ in range(20):
+        x = (rng.standard_normal(128) * rng.choice([1, 30], 128)).astype(np.float32)
+        mask = rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+        got = oracle.quant_row(x, hadamard=2, signs=mask)
+        want = oracle.quant_row(x * _mask_signs(mask), hadamard=1)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+def test_random_sign_special_masks():
+    """An empty mask is the plain rotation; a full mask negates the rotated
+    row, which flips the sign bit of every code (0x88 per byte) and keeps
+    every scale."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal(128).astype(np.float32)
+    plain = oracle.quant_row(x, hadamard=1)
+    zero = oracle.quant_row(x, hadamard=2, signs=np.zeros(4, np.uint32))
+    full = oracle.quant_row(x, hadamard=2, signs=np.full(4, 0xFFFFFFFF, np.uint32))
+    assert np.array_equal(zero[0], plain[0]) and np.array_equal(zero[1], plain[1])
+    assert np.array_equal(full[0], plain[0] ^ 0x88) and np.array_equal(full[1], plain[1])
+
+
+def test_random_sign_rotation_preserves_dot_products():
+    """(H D q) . (H D k) = q . k for D = diag(+-1): checked in fp64 with the
+    explicit Sylvester matrix."""
+    rng = np.random.default_rng(72)
+    idx = np.arange(128)
+    H = np.where(np.array([[bin(i & j).count("1") % 2 for j in idx] for i in idx]) == 1, -1.0, 1.0) / np.sqrt(128)
+    for _ in range(10):
+        d = _mask_signs(rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)).astype(np.float64)
+        q, k = rng.standard_normal(128), rng.standard_normal(128)
+        assert abs((H @ (d * q)) @ (H @ (d * k)) - q @ k) <= 1e-12 * np.linalg.norm(q) * np.linalg.norm(k)
