@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM copy-ceiling measurement")
+    ap.add_argument("--quality", action="store_true",
+                    help="report attention error against unquantized attention on the 600K-token "
+                         "outlier workload, per rotation variant, instead of timing")
     ap.add_argument("--spill", action="store_true",
                     help="time host spill and restore of the longest sequence's pages instead")
     ap.add_argument("--multi", type=int, default=0,
@@ -140,6 +143,8 @@ def main():
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
+    if args.quality:
+        return bench_quality(args, torch, kv, W, DecodeStep)
     wl = W.config(args.workload)
     log(f"workload {wl.name}: {wl.n_seq} seqs {wl.cached} cached, {wl.layers} layers, "
         f"hq {wl.hq} hkv {wl.hkv}, {kv.nvfp4kv_version()}")
@@ -310,6 +315,76 @@ def bench_multi(args, step, wl, torch, kv, W, ceiling):
         "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_quality(args, torch, kv, W, DecodeStep):
+    """Attention error of the NVFP4 cache against fp64 attention on the raw
+    (unquantized) rows: one sequence of 600,000 cached tokens + 1, RoPE over
+    32 dims with linear scaling 2.3, N(0,1) bf16 inputs with 3 outlier
+    channels (layer 0 of the workload), for no rotation, the Hadamard
+    rotation and the randomized rotation (a drawn sign mask).  Outlier
+    channels x32 (the workload as defined) scale Q and K alike, so scores
+    spread by ~150 and the softmax is nearly one-hot: its error mostly says
+    whether the top token changed.  Outliers x4 keep the softmax spread out.
+    The GPU's decode output is compared with the reference; so is the
+    oracle's fp64 NVFP4 attention on the GPU's own pool bytes, which
+    separates the format's error from the kernel's."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(2026)
+    mask = tuple(int(x) for x in rng.integers(0, 2 ** 32, 4, dtype=np.uint64))
+    variants = [("none", 0, None), ("hadamard", 1, None), ("random_sign", 2, mask)]
+    report = {}
+    for outlier_scale in (32.0, 4.0):
+        res = {}
+        ref = None
+        for name, had, signs in variants:
+            wl = W.config("single600k")
+            wl.layers, wl.hadamard, wl.outlier_scale = 1, had, outlier_scale
+            step = DecodeStep(wl, signs=signs or (0, 0, 0, 0))
+            step.fill([0])
+            out = step.decode(0, fused=True).cpu().numpy()[0].astype(np.float64)
+            T = wl.seq_lens[0]
+            oc, os_ = oracle.rope_table(wl.theta, wl.rotary_dim, wl.pos_scale, step.max_pos)
+            if ref is None:
+                k = W.rows(wl, "k", 0, step.base[0], T, wl.hkv, "cuda").float().cpu().numpy()
+                v = W.rows(wl, "v", 0, step.base[0], T, wl.hkv, "cuda").float().cpu().numpy()
+                q = step.q[0][0].float().cpu().numpy()
+                t0 = time.perf_counter()
+                ref = oracle.reference_attention(q, wl.cached[0], k, v, np.arange(T), wl.rotary_dim,
+                                                 W.sm_scale(), oc, os_)
+                log(f"outliers x{outlier_scale:g}: reference attention over {T} tokens "
+                    f"{time.perf_counter() - t0:.1f} s")
+                del k, v
+            npg = (T + 63) // 64
+            pages = torch.from_numpy(step.table_np[0, :npg].astype(np.int64)).cuda()
+            compact = step.pool.data.view(1, step.pool.num_pages, wl.hkv * 9216)[0].index_select(0, pages)
+            orc = oracle.decode_attention(compact.contiguous().view(-1).cpu().numpy(), npg, wl.hkv, 0,
+                                          wl.rotary_dim, had, step.q[0].float().cpu().numpy(), [wl.cached[0]],
+                                          np.arange(npg, dtype=np.int32)[None], [T], W.sm_scale(), oc, os_,
+                                          signs=np.array(signs, np.uint32) if signs else None)[0]
+            rel = float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
+            res[name] = {"rel_l2_err": round(rel, 6), "max_abs_err": float(np.abs(out - ref).max()),
+                         "median_head_rel_l2": round(float(np.median([np.linalg.norm(out[h] - ref[h]) /
+                                                                      np.linalg.norm(ref[h])
+                                                                      for h in range(wl.hq)])), 6),
+                         "gpu_vs_oracle_max_abs": float(np.abs(out - orc).max())}
+            log(f"outliers x{outlier_scale:g} {name}: rel L2 {rel:.4g}, median head "
+                f"{res[name]['median_head_rel_l2']:.4g}, GPU vs oracle {res[name]['gpu_vs_oracle_max_abs']:.2g}")
+            del step
+            torch.cuda.empty_cache()
+        report[f"outliers_x{outlier_scale:g}"] = res
+    rec = {
+        "metric": "NVFP4 attention error vs unquantized fp64 attention (relative L2), per rotation",
+        "value": report["outliers_x4"]["hadamard"]["rel_l2_err"], "unit": "relative L2",
+        "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": None, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "single600k layer 0: 600,000 cached tokens + 1, 24 query / 4 KV heads, "
+                               "RoPE 32 dims theta 1e7 scaling 2.3, bf16 N(0,1) with 3 outlier channels "
+                               "(x32 as defined, and x4); value: outliers x4, Hadamard rotation"},
+        "variants": report,
     }
     print(json.dumps(rec), flush=True)
 

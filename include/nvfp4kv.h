@@ -75,7 +75,13 @@ typedef struct {
     int32_t head_dim;       /* must be 128 */
     int32_t page_size;      /* must be 64 */
     int32_t rotary_dim;     /* RoPE dims at the head's start: 0..128, a multiple of 16 */
-    int32_t hadamard;       /* 1: rotate K and Q before quantizing; 0: do not */
+    int32_t hadamard;       /* 1: rotate K and Q before quantizing; 0: do not;
+                               2: rotate after negating the elements marked in
+                               hadamard_signs (a randomized rotation, a variant
+                               the release post does not use) */
+    uint32_t hadamard_signs[4]; /* hadamard 2 only: element j of K and Q rows is
+                                   negated before the transform when bit j % 32
+                                   of word j / 32 is set; the caller draws it */
 } nvfp4kv_pool;
 
 /* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144.

@@ -40,6 +40,7 @@ class _PoolDesc(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("rotary_dim", ctypes.c_int32),
         ("hadamard", ctypes.c_int32),
+        ("hadamard_signs", ctypes.c_uint32 * 4),
     ]
 
 
@@ -131,22 +132,25 @@ class Pool:
     num_layers: int
     num_kv_heads: int
     rotary_dim: int = 0
-    hadamard: bool = True
+    hadamard: int = 1           # 0 none, 1 Hadamard rotation, 2 randomized rotation
+    signs: tuple = (0, 0, 0, 0)  # hadamard 2: 128-bit element mask, 4 uint32 words
 
     @classmethod
     def allocate(cls, num_pages: int, num_layers: int, num_kv_heads: int, rotary_dim: int = 0,
-                 hadamard: bool = True, device="cuda") -> "Pool":
+                 hadamard: int = 1, device="cuda", signs=(0, 0, 0, 0)) -> "Pool":
+        signs = tuple(int(x) & 0xFFFFFFFF for x in signs)
         desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE,
-                         rotary_dim, int(hadamard))
+                         rotary_dim, int(hadamard), (ctypes.c_uint32 * 4)(*signs))
         nbytes = _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
         if nbytes == 0:
             raise ValueError("invalid pool shape")
         data = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, hadamard)
+        return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, int(hadamard), signs)
 
     def desc(self) -> _PoolDesc:
         return _PoolDesc(self.data.data_ptr(), self.num_pages, self.num_layers, self.num_kv_heads,
-                         HEAD_DIM, PAGE_SIZE, self.rotary_dim, int(self.hadamard))
+                         HEAD_DIM, PAGE_SIZE, self.rotary_dim, int(self.hadamard),
+                         (ctypes.c_uint32 * 4)(*self.signs))
 
 
 def nvfp4kv_version() -> str:

@@ -277,7 +277,7 @@ template <bool PACKED, int kPasses, bool MQ, int NT>
 __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group, int rotary_dim,
                                                 const float* __restrict__ rope_cos,
                                                 const float* __restrict__ rope_sin, int hadamard,
-                                                _Float16* qrow, h8 (*slot)[4][64]) {
+                                                const SignMask& signs, _Float16* qrow, h8 (*slot)[4][64]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   constexpr int kTilePasses = kPasses / NT;
@@ -297,7 +297,8 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
 #pragma unroll
         for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
     }
-    quant_row16_v(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0, codes, scode);
+    quant_row16_v(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0, lane_signs(hadamard, signs, c16),
+                  codes, scode);
     const float s = e4m3_value(scode);
     h8 qv;
 #pragma unroll
@@ -328,7 +329,7 @@ __device__ __forceinline__ void append_new_token(
     int sg, uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer,
     const void* __restrict__ k_new, const void* __restrict__ v_new, int in_dtype,
     const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, int rotary_dim, int hadamard,
+    const float* __restrict__ rope_sin, int rotary_dim, int hadamard, const SignMask& signs,
     const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens) {
   const int lane = (int)threadIdx.x;
   const int c16 = lane & 15;
@@ -345,7 +346,8 @@ __device__ __forceinline__ void append_new_token(
     srow = rope_sin + (size_t)pos * (rotary_dim / 2);
   }
   uint32_t codes, scode;
-  quant_row16(x, c16, rot, crow, srow, which ? false : (hadamard != 0), codes, scode);
+  quant_row16(x, c16, rot, crow, srow, which ? false : (hadamard != 0),
+              which ? 0u : lane_signs(hadamard, signs, c16), codes, scode);
   if (lane < 32) {
     const int tok = seq_lens[seq] - 1;
     const int page = page_table[(size_t)seq * pt_stride + tok / kPageSize];
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     QCols qc, const void* __restrict__ q, const void* __restrict__ k_new,
     const void* __restrict__ v_new, int in_dtype, const int32_t* __restrict__ q_positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard, const int32_t* __restrict__ page_table, int pt_stride,
+    int hadamard, SignMask signs, const int32_t* __restrict__ page_table, int pt_stride,
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
@@ -675,12 +677,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
                          rotary_dim, qin);
   const bool two_segs = b > seq_base + (int64_t)(kvh0 + 1) * pg;
   if (NT > 1) {
-    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, signs, qrow,
                                              q_lds[0]);
     if (two_segs) {
       load_q_inputs<kPasses, MQ>(seg0 + 1, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                                  rope_sin, rotary_dim, qin2);
-      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard,
+      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard, signs,
                                                qrow, q_lds[1]);
     }
   } else if (two_segs) {
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       const int64_t last = sstart + pgl - 1;
       if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
         append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
-                         q_positions, rope_cos, rope_sin, rotary_dim, hadamard, page_table,
+                         q_positions, rope_cos, rope_sin, rotary_dim, hadamard, signs, page_table,
                          pt_stride, seq_lens);
         any = true;
       }
@@ -783,10 +785,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // the first pages load
   const bool late_appends = k_new != nullptr && append_tokens(false);
   if (NT == 1) {
-    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+    make_q_operands<PACKED, kPasses, MQ, NT>(qin, group, rotary_dim, rope_cos, rope_sin, hadamard, signs, qrow,
                                              q_lds[0]);
     if (two_segs)
-      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard,
+      make_q_operands<PACKED, kPasses, MQ, NT>(qin2, group, rotary_dim, rope_cos, rope_sin, hadamard, signs,
                                                qrow, q_lds[1]);
   }
   if (late_appends) {
@@ -850,7 +852,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       QIn<kPasses, MQ> in;
       load_q_inputs<kPasses, MQ>(q_ready, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                              rope_sin, rotary_dim, in);
-      make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, qrow,
+      make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, signs, qrow,
                                                q_lds[(q_ready - seg0) % kQSlots]);
     }
 
@@ -1061,7 +1063,7 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
                         : (mq ? decode_attn_splitk_kernel<false, true, 1> : decode_attn_splitk_kernel<false, false, 1>);
   hipLaunchKernelGGL(kern, dim3(plan.n_waves), dim3(64), 0, stream, P.base, P.num_pages, P.hkv,
                      layer, n_seq, n_q_heads, qc, q, k_new, v_new, in_dtype, q_positions,
-                     rope_cos, rope_sin, P.rotary_dim, P.hadamard, page_table, page_table_stride,
+                     rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs, page_table, page_table_stride,
                      seq_lens, c_log2, ws_acc, ws_ml);
   return hipGetLastError();
 }

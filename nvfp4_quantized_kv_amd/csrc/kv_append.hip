@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v, int dtype,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard) {
+    int hadamard, SignMask signs) {
   const int lane = (int)__lane_id();
   const int r = lane & 15;
   const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(
   // group, and all 16 lanes of a group hold the same row kind, so the source
   // lane is always active on the path that reads it.
   uint32_t codes, scode;
-  quant_row16(x, r, rot, crow, srow, had, codes, scode);
+  quant_row16(x, r, rot, crow, srow, had, which ? 0u : lane_signs(hadamard, signs, r), codes, scode);
   if (!active) return;
   const int64_t slot = slots[tok];
   const int64_t page = slot / kPageSize;
@@ -83,7 +83,7 @@ __device__ inline void store8(void* dst, int dtype, size_t elem_off, const float
 __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
     const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_rows,
     const int64_t* __restrict__ slots, void* __restrict__ k_out, void* __restrict__ v_out,
-    int dtype, int unrotate) {
+    int dtype, int unrotate, int hadamard, SignMask signs) {
   const int r = (int)(threadIdx.x & 15);
   const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
   const bool active = row < n_rows;
@@ -104,7 +104,8 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
   for (int k = 0; k < 8; ++k) x[k] = e2m1_value((codes >> (4 * k)) & 15u) * s;
   if (unrotate && which == 0) {
     // H is symmetric and orthogonal: applying the transform again undoes it
-    // (up to float rounding).  Every lane of the group runs the shuffles.
+    // (up to float rounding), and the randomized rotation's negations come
+    // after it.  Every lane of the group runs the shuffles.
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -126,6 +127,10 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] = x[k] * __uint_as_float(0x3DB504F3u);
+    const uint32_t neg = lane_signs(hadamard, signs, r);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((neg >> k) & 1u) x[k] = -x[k];
   }
   if (!active) return;
   void* dst = which ? v_out : k_out;
@@ -143,7 +148,7 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
   const int grid = (n_rows + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(kv_quant_append_kernel, dim3(grid), dim3(256), 0, stream, P.base,
                      P.num_pages, P.hkv, layer, n_rows, k, v, dtype, slots, positions, rope_cos,
-                     rope_sin, P.rotary_dim, P.hadamard);
+                     rope_sin, P.rotary_dim, P.hadamard, P.signs);
   return hipGetLastError();
 }
 
@@ -152,7 +157,8 @@ hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64
   const int n_rows = n_tok * P.hkv * 2;
   const int grid = (n_rows + 15) / 16;
   hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(grid), dim3(256), 0, stream, P.base, P.num_pages,
-                     P.hkv, layer, n_rows, slots, k_out, v_out, dtype, unrotate && P.hadamard);
+                     P.hkv, layer, n_rows, slots, k_out, v_out, dtype, unrotate && P.hadamard, P.hadamard,
+                     P.signs);
   return hipGetLastError();
 }
 

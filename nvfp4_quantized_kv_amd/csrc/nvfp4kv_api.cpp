@@ -39,7 +39,7 @@ int check_pool_shape(const nvfp4kv_pool* p) {
   if (p->num_kv_heads <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", p->num_kv_heads);
   if (p->rotary_dim < 0 || p->rotary_dim > 128 || p->rotary_dim % 16 != 0)
     return fail(NVFP4KV_ERR_UNSUPPORTED, "rotary_dim %d unsupported (0..128, multiple of 16)", p->rotary_dim);
-  if (p->hadamard != 0 && p->hadamard != 1) return fail(NVFP4KV_ERR_INVALID_ARG, "hadamard must be 0 or 1 (got %d)", p->hadamard);
+  if (p->hadamard < 0 || p->hadamard > 2) return fail(NVFP4KV_ERR_INVALID_ARG, "hadamard must be 0, 1 or 2 (got %d)", p->hadamard);
   return NVFP4KV_OK;
 }
 
@@ -80,6 +80,7 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   L.hkv = p->num_kv_heads;
   L.rotary_dim = p->rotary_dim;
   L.hadamard = p->hadamard;
+  for (int i = 0; i < 4; ++i) L.signs.w[i] = p->hadamard == 2 ? p->hadamard_signs[i] : 0u;
   return L;
 }
 

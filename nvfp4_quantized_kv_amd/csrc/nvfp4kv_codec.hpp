@@ -125,11 +125,13 @@ __device__ inline void rope_coeffs(int r, int rotary_dim, const float* cos_row, 
 // RoPE coefficients from rope_coeffs (unused when rotary_dim is 0).  On
 // return `x` holds the rotated (RoPE'd, Hadamard'd) floats, `codes` the
 // lane's 8 E2M1 codes (element 8r+k in bits 4k..4k+3) and `scode` the E4M3
-// code of the lane's block (elements 16(r/2) .. 16(r/2)+15).  All 64 lanes of
+// code of the lane's block (elements 16(r/2) .. 16(r/2)+15).  With the
+// rotation, the elements whose bit is set in `neg` (bit k: element 8r+k; the
+// randomized rotation's mask, else 0) are negated before it.  All 64 lanes of
 // the wavefront must call it together (it uses cross-lane shuffles).
 __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const float (&cv)[8],
-                                     const float (&sv)[8], bool hadamard, uint32_t& codes,
-                                     uint32_t& scode) {
+                                     const float (&sv)[8], bool hadamard, uint32_t neg,
+                                     uint32_t& codes, uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
   // RoPE, rotate-half pairs (i, i + R/2) on the first R dims.
@@ -155,6 +157,9 @@ __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const
     }
   }
   if (hadamard) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((neg >> k) & 1u) x[k] = -x[k];
     // strides 1, 2, 4 inside the lane
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
@@ -194,7 +199,7 @@ __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const
 
 // quant_row16_v with the RoPE coefficients read from the table rows.
 __device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
-                                   const float* sin_row, bool hadamard, uint32_t& codes,
+                                   const float* sin_row, bool hadamard, uint32_t neg, uint32_t& codes,
                                    uint32_t& scode) {
   float cv[8], sv[8];
   if (rotary_dim > 0) {
@@ -203,7 +208,7 @@ __device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const f
 #pragma unroll
     for (int k = 0; k < 8; ++k) cv[k] = sv[k] = 0.0f;
   }
-  quant_row16_v(x, r, rotary_dim, cv, sv, hadamard, codes, scode);
+  quant_row16_v(x, r, rotary_dim, cv, sv, hadamard, neg, codes, scode);
 }
 
 }  // namespace nvfp4kv

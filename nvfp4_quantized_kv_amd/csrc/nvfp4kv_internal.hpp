@@ -9,12 +9,28 @@ namespace nvfp4kv {
 // Bytes of one (layer, page, kv head) block: 64 tokens x (K, V) x (64 code + 8 scale bytes).
 constexpr size_t kPoolBlockBytes = 9216;
 
+// Element mask of the randomized rotation (hadamard 2): element j of a K or
+// Q row is negated before the transform when bit j % 32 of word j / 32 is set.
+struct SignMask {
+  uint32_t w[4];
+};
+
+// Lane r's 8 bits of the mask (elements 8r .. 8r+7, bit k for element 8r+k);
+// 0 unless the rotation is the randomized one.
+__device__ inline uint32_t lane_signs(int hadamard, const SignMask& m, int r) {
+  if (hadamard != 2) return 0u;
+  const int q = r >> 2;
+  const uint32_t word = q == 0 ? m.w[0] : q == 1 ? m.w[1] : q == 2 ? m.w[2] : m.w[3];
+  return (word >> (8 * (r & 3))) & 0xFFu;
+}
+
 struct LaunchPool {
   uint8_t* base;
   int64_t num_pages;
   int hkv;
   int rotary_dim;
   int hadamard;
+  SignMask signs;
 };
 
 // Split-K plan of one decode call: the number of wavefronts that share the

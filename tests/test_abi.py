@@ -72,7 +72,7 @@ def _append(kv, d, layer=0, n_tok=4, k=4096, v=4096, dtype=1, slots=4096, pos=40
 
 @pytest.mark.parametrize("over,code", [
     (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(rotary_dim=24), -2),
-    (dict(rotary_dim=-16), -2), (dict(hadamard=2), -1), (dict(num_pages=0), -1),
+    (dict(rotary_dim=-16), -2), (dict(hadamard=3), -1), (dict(num_pages=0), -1),
     (dict(num_kv_heads=0), -1), (dict(base=0), -1), (dict(base=4100), -1)])
 def test_append_rejects_bad_pool(kv, over, code):
     assert _append(kv, _desc(kv, **over)) == code
@@ -144,6 +144,16 @@ def test_dequant_rejects_bad_arguments(kv):
     assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 4, 4096, 4096, 4096, 0, 3, None) == -1
     assert L.nvfp4kv_dequant(ctypes.byref(d), 5, 4, 4096, 4096, 4096, 0, 0, None) == -1
     assert L.nvfp4kv_dequant(ctypes.byref(d), 0, 0, 4096, 4096, 4096, 0, 0, None) == 0
+
+
+def test_pool_rotation_modes(kv):
+    """hadamard 0, 1 and 2 (the randomized rotation) are valid pools; 3 and -1
+    are not (an empty dequant validates the pool and launches nothing)."""
+    L = kv.lib()
+    for h in (0, 1, 2):
+        assert L.nvfp4kv_dequant(ctypes.byref(_desc(kv, hadamard=h)), 0, 0, 4096, 4096, 4096, 0, 0, None) == 0
+    for h in (3, -1):
+        assert L.nvfp4kv_dequant(ctypes.byref(_desc(kv, hadamard=h)), 0, 0, 4096, 4096, 4096, 0, 0, None) == -1
 
 
 def test_page_bytes_and_spill_argument_checks(kv):

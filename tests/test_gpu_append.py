@@ -88,9 +88,11 @@ def test_append_layer8k_bitexact():
 
 @pytest.mark.parametrize("rotary,hadamard,dtype", [
     (0, False, np.float32), (16, True, np.float32), (32, True, "bf16"), (64, False, "bf16"),
-    (128, True, np.float32), (48, True, np.float32), (112, True, "bf16")])
+    (128, True, np.float32), (48, True, np.float32), (112, True, "bf16"), (32, 2, "bf16"), (0, 2, np.float32)])
 def test_append_shapes_and_flags_bitexact(rotary, hadamard, dtype):
-    rng = np.random.default_rng(rotary * 7 + hadamard)
+    """hadamard 2: the randomized rotation, with a drawn element mask."""
+    rng = np.random.default_rng(rotary * 7 + int(hadamard))
+    signs = rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32) if hadamard == 2 else None
     hkv, n_tok, num_pages = 3, 150, 9
     k = rng.standard_normal((n_tok, hkv, 128)).astype(np.float32) * np.exp(rng.uniform(-4, 4, (n_tok, hkv, 1)))
     v = rng.standard_normal((n_tok, hkv, 128)).astype(np.float32) * np.exp(rng.uniform(-4, 4, (n_tok, hkv, 1)))
@@ -102,7 +104,8 @@ def test_append_shapes_and_flags_bitexact(rotary, hadamard, dtype):
     slots = rng.choice(num_pages * 64, size=n_tok, replace=False)
     pos = rng.integers(0, 100000, size=n_tok)
     kv = _kv()
-    pool = kv.Pool.allocate(num_pages, 2, hkv, rotary, hadamard)
+    pool = kv.Pool.allocate(num_pages, 2, hkv, rotary, hadamard,
+                            signs=tuple(signs) if signs is not None else (0, 0, 0, 0))
     pool.data.zero_()
     rc = rs = oc = os_ = None
     if rotary:
@@ -117,7 +120,7 @@ def test_append_shapes_and_flags_bitexact(rotary, hadamard, dtype):
                       torch.from_numpy(pos.astype(np.int32)).cuda(), rc, rs)
     torch.cuda.synchronize()
     ref = np.zeros(oracle.pool_bytes(2, num_pages, hkv), np.uint8)
-    oracle.append(ref, num_pages, hkv, rotary, hadamard, 1, k, v, slots, pos, oc, os_)
+    oracle.append(ref, num_pages, hkv, rotary, hadamard, 1, k, v, slots, pos, oc, os_, signs=signs)
     _assert_same_bytes(pool.data.cpu().numpy(), ref)
 
 
@@ -200,3 +203,35 @@ def test_dequant_exact(out_dtype):
             assert (kh[i, g] == kref).all() and (vh[i, g] == vref).all()
             # un-rotated K-hat is the quantized K back in the input domain
             assert np.linalg.norm(kh2[i, g] - k[i, g]) <= 0.2 * np.linalg.norm(k[i, g])
+
+
+def test_dequant_unrotates_the_randomized_rotation():
+    """With the randomized rotation, un-rotating applies the transform again
+    and then the element negations: K-hat back in the input domain, which
+    must equal the oracle's dequantized row pushed through H then D in fp64
+    (to float rounding) and stay near the input row."""
+    rng = np.random.default_rng(19)
+    hkv, n_tok, num_pages = 2, 64, 2
+    signs = rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+    k = (rng.standard_normal((n_tok, hkv, 128)) * 3).astype(np.float32)
+    v = (rng.standard_normal((n_tok, hkv, 128)) * 3).astype(np.float32)
+    slots = rng.choice(num_pages * 64, size=n_tok, replace=False).astype(np.int64)
+    kv = _kv()
+    pool = kv.Pool.allocate(num_pages, 1, hkv, 0, 2, signs=tuple(signs))
+    pool.data.zero_()
+    st = torch.from_numpy(slots).cuda()
+    kv.nvfp4kv_append(pool, 0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), st,
+                      torch.zeros(n_tok, dtype=torch.int32).cuda())
+    kh, _ = kv.nvfp4kv_dequant(pool, 0, st, torch.float32, unrotate=True, want_v=False)
+    torch.cuda.synchronize()
+    pb = pool.data.cpu().numpy()
+    kh = kh.cpu().numpy()
+    idx = np.arange(128)
+    H = np.where(np.array([[bin(i & j).count("1") % 2 for j in idx] for i in idx]) == 1, -1.0, 1.0) / np.sqrt(128)
+    d = np.array([-1.0 if (int(signs[j // 32]) >> (j % 32)) & 1 else 1.0 for j in idx])
+    for i in range(n_tok):
+        for g in range(hkv):
+            rot = oracle.dequant_row(*oracle.pool_read_row(pb, num_pages, hkv, 0, slots[i], g, 0))
+            want = d * (H @ rot)
+            assert np.abs(kh[i, g] - want).max() <= 1e-5 * max(1.0, np.abs(want).max())
+            assert np.linalg.norm(kh[i, g] - k[i, g]) <= 0.2 * np.linalg.norm(k[i, g])

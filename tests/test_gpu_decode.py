@@ -41,7 +41,10 @@ class Case:
         self.kv = kv
         rng = np.random.default_rng(seed)
         self.lens = list(lens)
-        self.hkv, self.hq, self.rotary, self.hadamard = hkv, hq, rotary, hadamard
+        self.hkv, self.hq, self.rotary, self.hadamard = hkv, hq, rotary, int(hadamard)
+        # hadamard 2: the randomized rotation's element mask, drawn here
+        self.signs = (rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
+                      if self.hadamard == 2 else None)
         pages = [(t + 63) // 64 for t in lens]
         self.num_pages = sum(pages) + extra_pages
         perm = rng.permutation(self.num_pages).astype(np.int32)
@@ -63,7 +66,8 @@ class Case:
             return torch.from_numpy(x).to(dtype)
 
         self.max_pos = max(lens) + 1
-        self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard)
+        self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard,
+                                     signs=tuple(self.signs) if self.signs is not None else (0, 0, 0, 0))
         self.pool.data.fill_(0x7F)  # stale bytes decode to NaN if ever read unmasked
         self.rc = self.rs = self.oc = self.os = None
         if rotary:
@@ -109,7 +113,7 @@ class Case:
         pool = self.pool.data.cpu().numpy()
         return oracle.decode_attention(pool, self.num_pages, self.hkv, 0, self.rotary, self.hadamard,
                                        self.q.float().numpy(), self.q_pos, self.table, self.lens,
-                                       sm_scale, self.oc, self.os)
+                                       sm_scale, self.oc, self.os, signs=self.signs)
 
 
 def test_decode_tiny_workload():
@@ -139,7 +143,8 @@ def test_decode_group_sizes(group):
 
 
 @pytest.mark.parametrize("hadamard,rotary,pos_scale", [(False, 32, 2.3), (True, 32, 2.3), (True, 0, 1.0),
-                                                        (True, 128, 1.0), (False, 0, 1.0)])
+                                                        (True, 128, 1.0), (False, 0, 1.0), (2, 32, 2.3),
+                                                        (2, 0, 1.0)])
 def test_decode_flags(hadamard, rotary, pos_scale):
     c = Case(7, [3000, 1234], 4, 24, rotary=rotary, hadamard=hadamard, pos_scale=pos_scale,
              outlier_scale=32.0)
@@ -209,6 +214,7 @@ FUSED_CASES = [
     dict(lens=[1000, 3, 2049, 777], dtype=torch.float32),
     dict(lens=[700, 1500], hq=32, rotary=16),         # 16 query heads per kv head
     dict(lens=[3000, 1234], rotary=128, pos_scale=2.3),
+    dict(lens=[1000, 130], hadamard=2),               # randomized rotation of the new K and of Q
 ]
 
 

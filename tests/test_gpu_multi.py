@@ -34,7 +34,8 @@ def _run(c, q, pos, pages_per_split=0):
 
 def _oracle(c, q, pos):
     return oracle.decode_attention_multi(c.pool.data.cpu().numpy(), c.num_pages, c.hkv, 0, c.rotary, c.hadamard,
-                                         q.float().numpy(), pos, c.table, c.lens, 1 / np.sqrt(128), c.oc, c.os)
+                                         q.float().numpy(), pos, c.table, c.lens, 1 / np.sqrt(128), c.oc, c.os,
+                                         signs=c.signs)
 
 
 MULTI_CASES = [
