@@ -17,10 +17,13 @@ namespace nvfp4kv {
 
 namespace {
 
-// Rows are ordered (token, kv head, K|V) so that the 4 rows of a wavefront
-// read neighbouring input rows.
+// Row slots come in groups of 8: the K rows of four consecutive (token, kv
+// head) pairs, then their four V rows.  The 4 rows of a wavefront are thus
+// all K or all V: only K rows take RoPE and the rotation, and a wavefront
+// mixing both kinds would run that path with its V lanes idle.  The rows of
+// a wavefront are neighbouring input rows (1 KB of bf16 contiguous).
 __global__ __launch_bounds__(256) void kv_quant_append_kernel(
-    uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_rows,
+    uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_pairs,
     const void* __restrict__ k, const void* __restrict__ v, int dtype,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
@@ -28,13 +31,14 @@ __global__ __launch_bounds__(256) void kv_quant_append_kernel(
   const int lane = (int)__lane_id();
   const int r = lane & 15;
   const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
-  // Lanes past the last row still take part in the shuffles, on a copy of the
-  // last row, and store nothing.
-  const bool active = row < n_rows;
-  const int rr = active ? row : n_rows - 1;
-  const int which = rr & 1;               // 0 = K, 1 = V
-  const int g = (rr >> 1) % hkv;
-  const int tok = (rr >> 1) / hkv;
+  const int which = (row >> 2) & 1;       // 0 = K, 1 = V
+  // Lanes past the last pair still take part in the shuffles, on a copy of
+  // the last pair's row of their kind, and store nothing.
+  int pair = (row >> 3) * 4 + (row & 3);  // token * hkv + kv head
+  const bool active = pair < n_pairs;
+  pair = active ? pair : n_pairs - 1;
+  const int g = pair % hkv;
+  const int tok = pair / hkv;
   const size_t elem_off = ((size_t)tok * hkv + g) * kHeadDim + 8 * r;
   float x[8];
   load8(which ? v : k, dtype, elem_off, x);
@@ -143,11 +147,12 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,
                          const float* rope_cos, const float* rope_sin, hipStream_t stream) {
-  const int n_rows = n_tok * P.hkv * 2;
-  const int rows_per_block = 16;  // 256 threads, 16 lanes per row
-  const int grid = (n_rows + rows_per_block - 1) / rows_per_block;
+  const int n_pairs = n_tok * P.hkv;
+  const int n_slots = 8 * ((n_pairs + 3) / 4);   // groups of 4 K rows + 4 V rows
+  const int rows_per_block = 16;                 // 256 threads, 16 lanes per row
+  const int grid = (n_slots + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL(kv_quant_append_kernel, dim3(grid), dim3(256), 0, stream, P.base,
-                     P.num_pages, P.hkv, layer, n_rows, k, v, dtype, slots, positions, rope_cos,
+                     P.num_pages, P.hkv, layer, n_pairs, k, v, dtype, slots, positions, rope_cos,
                      rope_sin, P.rotary_dim, P.hadamard, P.signs);
   return hipGetLastError();
 }
