@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--quality", action="store_true",
                     help="report attention error against unquantized attention on the 600K-token "
                          "outlier workload, per rotation variant, instead of timing")
+    ap.add_argument("--append", action="store_true",
+                    help="time the prefill-style append of the workload's chunk per sequence instead "
+                         "(batch64: 64 x 8192 tokens)")
     ap.add_argument("--spill", action="store_true",
                     help="time host spill and restore of the longest sequence's pages instead")
     ap.add_argument("--multi", type=int, default=0,
@@ -165,6 +168,8 @@ def main():
         return bench_multi(args, step, wl, torch, kv, W, ceiling)
     if args.spill:
         return bench_spill(args, step, wl, torch, kv)
+    if args.append:
+        return bench_append(args, step, wl, torch, kv, W)
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -390,6 +395,91 @@ def bench_quality(args, torch, kv, W, DecodeStep):
 
 
 PEAK_PCIE_GBPS = 64.0          # PCIe 5.0 x16 host link, per direction
+
+
+def bench_append(args, step, wl, torch, kv, W):
+    """Prefill-style append: every sequence's chunk of wl.prefill_chunk tokens
+    (positions T+1 .. T+chunk, after the step's token) quantized into the
+    pool in one nvfp4kv_append call on layer 0; inputs resident in HBM."""
+    import numpy as np
+    chunk = wl.prefill_chunk
+    if chunk <= 0:
+        raise SystemExit(f"workload {wl.name} has no prefill chunk")
+    ks, vs, sl, ps = [], [], [], []
+    for i, T in enumerate(wl.cached):
+        first = T + 1
+        ks.append(W.rows(wl, "k", 0, step.base[i] + first, chunk, wl.hkv, "cuda"))
+        vs.append(W.rows(wl, "v", 0, step.base[i] + first, chunk, wl.hkv, "cuda"))
+        pos = np.arange(first, first + chunk)
+        sl.append(W.slots(step.table_np, i, pos))
+        ps.append(pos.astype(np.int32))
+    k = torch.cat(ks).contiguous()
+    v = torch.cat(vs).contiguous()
+    del ks, vs
+    slots = torch.from_numpy(np.concatenate(sl)).cuda()
+    pos = torch.from_numpy(np.concatenate(ps)).cuda()
+    n_tok = k.shape[0]
+    for _ in range(2):
+        kv.nvfp4kv_append(step.pool, 0, k, v, slots, pos, step.rope_cos, step.rope_sin)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kv.nvfp4kv_append(step.pool, 0, k, v, slots, pos, step.rope_cos, step.rope_sin)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+    t = sum(times) / len(times)
+    in_bytes = 2 * n_tok * wl.hkv * 128 * k.element_size()
+    out_bytes = 144 * n_tok * wl.hkv
+    gbps = (in_bytes + out_bytes) / t / 1e9
+    # sampled rows against the oracle's quantization of the same inputs
+    cpu = None
+    import oracle
+    rng = np.random.default_rng(0)
+    oc, os_ = oracle.rope_table(wl.theta, wl.rotary_dim, wl.pos_scale, step.max_pos) if wl.rotary_dim else (None, None)
+    view = step.pool.data.view(wl.layers, step.pool.num_pages, wl.hkv * 9216)
+    for j in rng.choice(n_tok, 16, replace=False):
+        j = int(j)
+        s_ = int(slots[j]); page, off = s_ // 64, s_ % 64
+        blk = view[0, page].cpu().numpy()
+        for g in range(wl.hkv):
+            p_ = int(pos[j])
+            kc, ksc = oracle.quant_row(k[j, g].float().cpu().numpy(), wl.rotary_dim,
+                                       oc[p_] if oc is not None else None, os_[p_] if os_ is not None else None,
+                                       int(wl.hadamard))
+            gk = oracle.pool_read_row(blk, 1, wl.hkv, 0, off, g, 0)
+            assert (gk[0] == kc).all() and (gk[1] == ksc).all(), f"appended K row {j} differs from the oracle"
+    if not args.no_cpu_baseline:
+        n = 2048
+        kk, vv = k[:n].float().cpu().numpy(), v[:n].float().cpu().numpy()
+        pool_h = np.zeros(oracle.pool_bytes(1, step.pool.num_pages, wl.hkv), np.uint8)
+        t0 = time.perf_counter()
+        oracle.append(pool_h, step.pool.num_pages, wl.hkv, wl.rotary_dim, int(wl.hadamard), 0, kk, vv,
+                      slots[:n].cpu().numpy(), pos[:n].cpu().numpy(), oc, os_)
+        secs = time.perf_counter() - t0
+        cpu = {"value": round(n * wl.hkv * (2 * 128 * 2 + 144) / secs / 1e9, 4), "unit": "GB/s",
+               "cores": int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0)))), "kind": "oracle",
+               "sample": f"oracle append of the first {n} tokens x {wl.hkv} kv heads ({secs:.2f} s)"}
+    log(f"append of {n_tok} tokens x {wl.hkv} kv heads: {t * 1e3:.3f} ms, {gbps:.1f} GB/s")
+    rec = {
+        "metric": "NVFP4 prefill append achieved HBM GB/s (tokens/s)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 2,
+        "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.n_seq} sequences x {chunk}-token chunk ({n_tok} tokens), "
+                               f"{wl.hkv} kv heads, {wl.dtype} inputs, RoPE {wl.rotary_dim} dims, "
+                               f"rotation {int(wl.hadamard)}",
+                   "step": "one nvfp4kv_append call"},
+        "tokens_per_s": round(n_tok / t, 1),
+        "roofline": {"bound": "hbm", "kernel": "kv_quant_append_kernel", "achieved": round(gbps, 2),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None, "algo_bytes_per_launch": in_bytes + out_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def bench_spill(args, step, wl, torch, kv):
