@@ -134,9 +134,10 @@ def cpu_baseline(step, wl, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        log("multi-GPU runs are not part of this build (see DESIGN.md for how the path would shard)")
+        log("only one GPU is used: the attention path shards by kv head, sequence or context with no "
+            "exchange inside the kernels, and a single GPU runs one shard at its real shape")
         sys.exit(2)
     import torch
     import nvfp4_quantized_kv_amd as kv
