@@ -67,7 +67,7 @@ def lib():
                                  ctypes.c_int, P, P, P, P, P, P]
         L.orc_decode_attention.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, P, P, P,
-                                           P, ctypes.c_int, P, f64, P]
+                                           P, ctypes.c_int, P, f64, P, P]
         L.orc_reference_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, P, i32, P, P, P, P, P, f64, P]
         _lib = L
@@ -185,9 +185,16 @@ def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, posit
 
 
 def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
-                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None):
-    """fp64 attention for every sequence and query head over the pool's bytes."""
+                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None, v_rows=None):
+    """fp64 attention for every sequence and query head over the pool's bytes.
+    v_rows [T][hkv][128] (one sequence only): V values taken from it instead
+    of the pool, for the variant that keeps V unquantized."""
     mode, m = _rotation(hadamard, signs)
+    vr = None
+    if v_rows is not None:
+        vr = _c(v_rows, np.float32)
+        if len(seq_lens) != 1 or vr.shape != (int(seq_lens[0]), hkv, HEAD_DIM):
+            raise ValueError("v_rows needs one sequence and [T][hkv][128] rows")
     q = _c(q, np.float32)
     n_seq, hq, _ = q.shape
     page_table = _c(page_table, np.int32)
@@ -197,7 +204,8 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
     lib().orc_decode_attention(_p(_c(pool, np.uint8)), num_pages, hkv, layer, rotary_dim,
                                mode, _p(m) if m is not None else None, n_seq, hq, _p(q), _p(_c(q_pos, np.int32)),
                                _p(ct), _p(st), _p(page_table), page_table.shape[1],
-                               _p(_c(seq_lens, np.int32)), float(sm_scale), _p(out))
+                               _p(_c(seq_lens, np.int32)), float(sm_scale), _p(vr) if vr is not None else None,
+                               _p(out))
     return out
 
 

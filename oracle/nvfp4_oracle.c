@@ -311,13 +311,17 @@ void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int h
  *   z_t   = sm_scale * sum_d Qhat[d] * Khat_t[d],  t = 0 .. seq_lens[n]-1,
  *           Khat/Vhat dequantized from the slots page_table[n][t/64]*64 + t%64;
  *   o     = sum_t softmax(z)_t * Vhat_t.
- * All of it in double.  q: [n_seq][hq][128] floats; out: [n_seq][hq][128]. */
+ * All of it in double.  q: [n_seq][hq][128] floats; out: [n_seq][hq][128].
+ * With v_rows (one sequence only) the V values are taken from v_rows
+ * [T][hkv][128] instead of the pool: the K-only-quantized variant of a
+ * quality study (V kept in a 16-bit format by the caller). */
 void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int layer,
                           int rotary_dim, int hadamard, const uint32_t* signs, int n_seq, int hq,
                           const float* q, const int32_t* q_pos,
                           const float* cos_tab, const float* sin_tab,
                           const int32_t* page_table, int page_table_stride,
-                          const int32_t* seq_lens, double sm_scale, double* out)
+                          const int32_t* seq_lens, double sm_scale, const float* v_rows,
+                          double* out)
 {
     int grp = hq / hkv, half = rotary_dim / 2;
     for (int n = 0; n < n_seq; ++n) {
@@ -370,8 +374,12 @@ void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int l
                     double vh[ORC_D];
                     int64_t slot = (int64_t)page_table[(size_t)n * page_table_stride + t / ORC_PAGE]
                                    * ORC_PAGE + t % ORC_PAGE;
-                    orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 1, codes, scales);
-                    orc_dequant_row(codes, scales, vh);
+                    if (v_rows != NULL) {
+                        for (int d = 0; d < ORC_D; ++d) vh[d] = v_rows[((size_t)t * hkv + g) * ORC_D + d];
+                    } else {
+                        orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 1, codes, scales);
+                        orc_dequant_row(codes, scales, vh);
+                    }
                     for (int r = 0; r < grp; ++r) {
                         double p = z[(size_t)r * T + t];
                         acc[(size_t)r * (ORC_D + 1) + ORC_D] += p;

@@ -299,3 +299,26 @@ def test_random_sign_attention_close_to_unquantized_reference():
     ref = oracle.reference_attention(q[0], T - 1, k, v, np.arange(T), 0, 1 / np.sqrt(128))
     rel = np.linalg.norm(out[0] - ref) / np.linalg.norm(ref)
     assert rel < 0.25
+
+
+def test_v_rows_option_reads_the_given_values():
+    """Given the pool's own dequantized V rows, the V-rows option reproduces
+    the plain decode bit for bit; given other rows it uses them (a row of
+    zeros everywhere gives a zero output)."""
+    T, hkv, hq = 150, 2, 4
+    rng = np.random.default_rng(62)
+    k = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, hkv, D)).astype(np.float32)
+    q = rng.standard_normal((1, hq, D)).astype(np.float32)
+    pool = _pool(3, hkv)
+    table = np.array([[2, 0, 1]], np.int32)
+    slots = table[0, np.arange(T) // 64].astype(np.int64) * 64 + np.arange(T) % 64
+    oracle.append(pool, 3, hkv, 0, True, 0, k, v, slots, np.arange(T))
+    plain = oracle.decode_attention(pool, 3, hkv, 0, 0, True, q, [T - 1], table, [T], 0.1)
+    vh = np.stack([[oracle.dequant_row(*oracle.pool_read_row(pool, 3, hkv, 0, s, g, 1)) for g in range(hkv)]
+                   for s in slots]).astype(np.float32)
+    same = oracle.decode_attention(pool, 3, hkv, 0, 0, True, q, [T - 1], table, [T], 0.1, v_rows=vh)
+    assert np.array_equal(plain, same)
+    zero = oracle.decode_attention(pool, 3, hkv, 0, 0, True, q, [T - 1], table, [T], 0.1,
+                                   v_rows=np.zeros_like(vh))
+    assert not zero.any()
