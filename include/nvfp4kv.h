@@ -106,8 +106,8 @@ int nvfp4kv_rope_table(double theta, int32_t rotary_dim, double pos_scale, int32
  *   k, v       [n_tok][num_kv_heads][128], dtype in_dtype (bf16 or f32)
  *   slots      [n_tok] int64, page * 64 + offset, page < num_pages
  *   positions  [n_tok] int32, < max_pos (read only when rotary_dim > 0)
- *   rope_cos/rope_sin [max_pos][rotary_dim/2] float (may be null when
- *              rotary_dim == 0)
+ *   rope_cos/rope_sin [max_pos][rotary_dim/2] float, 16-byte aligned (may
+ *              be null when rotary_dim == 0; nvfp4kv_rope_table fills them)
  * Two tokens with the same slot in one call race. */
 int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok,
                    const void* k, const void* v, nvfp4kv_dtype in_dtype,

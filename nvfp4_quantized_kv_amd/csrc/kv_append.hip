@@ -17,55 +17,175 @@ namespace nvfp4kv {
 
 namespace {
 
-// Row slots come in groups of 8: the K rows of four consecutive (token, kv
-// head) pairs, then their four V rows.  The 4 rows of a wavefront are thus
-// all K or all V: only K rows take RoPE and the rotation, and a wavefront
-// mixing both kinds would run that path with its V lanes idle.  The rows of
-// a wavefront are neighbouring input rows (1 KB of bf16 contiguous).
-__global__ __launch_bounds__(256) void kv_quant_append_kernel(
-    uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_pairs,
+// x from lane r ^ BIT of the same 16-lane row (BIT = 1, 2, 4 or 8), through
+// DPP: quad permutes for 1 and 2; for 4 the half-row mirror (r ^ 7) then the
+// quad reversal (^ 3); for 8 the row mirror (r ^ 15) then the half-row mirror.
+template <int BIT>
+__device__ __forceinline__ float xor_lane(float x) {
+  const int i = __float_as_int(x);
+  int o;
+  if (BIT == 1) {
+    o = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false);
+  } else if (BIT == 2) {
+    o = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false);
+  } else if (BIT == 4) {
+    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, false), 0x1B, 0xF,
+                                    0xF, false);
+  } else {
+    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x140, 0xF, 0xF, false), 0x141, 0xF,
+                                    0xF, false);
+  }
+  return __int_as_float(o);
+}
+
+// One cross-lane stage of the transform: the lower lane of a pair keeps
+// a + b, the upper one b - a (its own value subtracted from the partner's),
+// as one fused multiply-add by +-1, which rounds exactly as the addition or
+// subtraction does.
+template <int BIT>
+__device__ __forceinline__ void fwht_stage(float (&x)[8], int r) {
+  const float sgn = (r & BIT) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(sgn, x[k], xor_lane<BIT>(x[k]));
+}
+
+// E2M1 magnitude code of |y| for block scale s by a three-level search over
+// the same exact thresholds as e2m1_code: 1.75s (>=) splits codes 0-3 from
+// 4-7, then 0.75s or 3.5s (>=), then 0.25s, 1.25s, 2.5s or 5s (>).  The
+// thresholds increase and each test is monotone in |y|, so the result is the
+// count of thresholds passed, as in e2m1_code.
+__device__ __forceinline__ uint32_t e2m1_code_search(float y, const float (&t)[7], float s) {
+  const float a = fabsf(y);
+  const bool b2 = a >= t[3];
+  const bool b1 = a >= (b2 ? t[5] : t[1]);
+  const float t0 = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);
+  const bool b0 = a > t0;
+  uint32_t c = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
+  if (s == 0.0f) c = 0;
+  return c | (signbit(y) ? 8u : 0u);
+}
+
+// The append kernel's row quantizer: what quant_row16 computes, bit for bit
+// (same binary32 operations in the same order), with the RoPE coefficients
+// read as 16-byte vectors, RoPE without branches, the transform's cross-lane
+// stages through DPP and the E2M1 code by search.  All 16 lanes of a row
+// must call it together.
+__device__ __forceinline__ void append_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
+                                             const float* sin_row, bool hadamard, uint32_t neg,
+                                             uint32_t& codes, uint32_t& scode) {
+#pragma clang fp contract(off)
+  const int lane = (int)__lane_id();
+  if (rotary_dim > 0) {
+    const int half = rotary_dim / 2;          // a multiple of 8
+    const int hl = half / 8;                  // lanes per half
+    const bool first = r < hl;
+    const bool in_rot = r < 2 * hl;
+    const int base = in_rot ? (first ? 8 * r : 8 * r - half) : 0;
+    float cv[8], sv[8];
+    const float4* cp = reinterpret_cast<const float4*>(cos_row + base);
+    const float4* sp = reinterpret_cast<const float4*>(sin_row + base);
+    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w; cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
+    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+    const int src = in_rot ? (first ? r + hl : r - hl) : r;
+    const int src_lane = (lane & ~15) + src;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float other = __shfl(x[k], src_lane, 64);
+      // first half: x c - o s; second half: x c + o s (a - b is a + (-b))
+      const float t = x[k] * cv[k] + other * (first ? -sv[k] : sv[k]);
+      x[k] = in_rot ? t : x[k];
+    }
+  }
+  if (hadamard) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if ((neg >> k) & 1u) x[k] = -x[k];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (k & h) continue;
+        const float a = x[k], b = x[k + h];
+        x[k] = a + b;
+        x[k + h] = a - b;
+      }
+    }
+    fwht_stage<1>(x, r);
+    fwht_stage<2>(x, r);
+    fwht_stage<4>(x, r);
+    fwht_stage<8>(x, r);
+    const float inv_sqrt128 = __uint_as_float(0x3DB504F3u);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = x[k] * inv_sqrt128;
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
+  am = fmaxf(am, xor_lane<1>(am));
+  scode = e4m3_scale_code(am);
+  const float s = e4m3_value(scode);
+  const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) w |= e2m1_code_search(x[k], t, s) << (4 * k);
+  codes = w;
+}
+
+// One workgroup (8 wavefronts) per run of 64 consecutive tokens, every kv
+// head in turn, in passes of 16 tokens: wavefronts 0-3 take the 16 tokens' K
+// rows, 4-7 their V rows (4 rows of 16 lanes each), so every wavefront's rows
+// are all K or all V and only K rows run RoPE and the rotation.  The kv heads
+// of a token share its RoPE table rows, read once into the CU's L2.  Consecutive
+// tokens of a prefill sit in consecutive slots, whose code bytes share
+// 128-byte lines (16 bytes per token in the K tiles, 4 in the V tiles) and
+// whose scale bytes do too: one workgroup completes those lines in its CU's
+// L2.  Spread over workgroups (and so over XCDs), each line was written back
+// in pieces: twice the algorithmic write traffic, measured.
+__global__ __launch_bounds__(512) void kv_quant_append_kernel(
+    uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_tok,
     const void* __restrict__ k, const void* __restrict__ v, int dtype,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, SignMask signs) {
   const int lane = (int)__lane_id();
   const int r = lane & 15;
-  const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
-  const int which = (row >> 2) & 1;       // 0 = K, 1 = V
-  // Lanes past the last pair still take part in the shuffles, on a copy of
-  // the last pair's row of their kind, and store nothing.
-  int pair = (row >> 3) * 4 + (row & 3);  // token * hkv + kv head
-  const bool active = pair < n_pairs;
-  pair = active ? pair : n_pairs - 1;
-  const int g = pair % hkv;
-  const int tok = pair / hkv;
-  const size_t elem_off = ((size_t)tok * hkv + g) * kHeadDim + 8 * r;
-  float x[8];
-  load8(which ? v : k, dtype, elem_off, x);
+  const int wv = (int)(threadIdx.x >> 6);
+  const int which = wv >> 2;                       // 0 = K, 1 = V
   const int rot = which ? 0 : rotary_dim;
   const bool had = which ? false : (hadamard != 0);
-  const float* crow = nullptr;
-  const float* srow = nullptr;
-  if (rot > 0) {
-    const int pos = positions[tok];
-    crow = rope_cos + (size_t)pos * (rotary_dim / 2);
-    srow = rope_sin + (size_t)pos * (rotary_dim / 2);
+  const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
+#pragma unroll 1
+  for (int it = 0; it < 4 * hkv; ++it) {
+    const int g = it % hkv, pass = it / hkv;
+    int tok = (int)blockIdx.x * 64 + pass * 16 + (wv & 3) * 4 + (lane >> 4);
+    // Lanes past the last token still take part in the shuffles, on a copy
+    // of the last token's row of their kind, and store nothing.
+    const bool active = tok < n_tok;
+    tok = active ? tok : n_tok - 1;
+    const size_t elem_off = ((size_t)tok * hkv + g) * kHeadDim + 8 * r;
+    float x[8];
+    load8(which ? v : k, dtype, elem_off, x);
+    const float* crow = nullptr;
+    const float* srow = nullptr;
+    if (rot > 0) {
+      const int pos = positions[tok];
+      crow = rope_cos + (size_t)pos * (rotary_dim / 2);
+      srow = rope_sin + (size_t)pos * (rotary_dim / 2);
+    }
+    uint32_t codes, scode;
+    append_row16(x, r, rot, crow, srow, had, neg, codes, scode);
+    if (active) {
+      const int64_t slot = slots[tok];
+      const int64_t page = slot / kPageSize;
+      const uint32_t t = (uint32_t)(slot % kPageSize);
+      uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
+                                (size_t)kBlockBytes;
+      const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
+      *reinterpret_cast<uint32_t*>(blk + woff) = codes;
+      if ((r & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + r / 2] = (uint8_t)scode;
+    }
   }
-  // K rows and V rows of a wavefront take different paths through RoPE and
-  // the rotation.  Every shuffle inside reads from a lane of the same 16-lane
-  // group, and all 16 lanes of a group hold the same row kind, so the source
-  // lane is always active on the path that reads it.
-  uint32_t codes, scode;
-  quant_row16(x, r, rot, crow, srow, had, which ? 0u : lane_signs(hadamard, signs, r), codes, scode);
-  if (!active) return;
-  const int64_t slot = slots[tok];
-  const int64_t page = slot / kPageSize;
-  const uint32_t t = (uint32_t)(slot % kPageSize);
-  uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
-                            (size_t)kBlockBytes;
-  const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
-  *reinterpret_cast<uint32_t*>(blk + woff) = codes;
-  if ((r & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + r / 2] = (uint8_t)scode;
 }
 
 __device__ inline void store8(void* dst, int dtype, size_t elem_off, const float (&x)[8]) {
@@ -147,12 +267,9 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,
                          const float* rope_cos, const float* rope_sin, hipStream_t stream) {
-  const int n_pairs = n_tok * P.hkv;
-  const int n_slots = 8 * ((n_pairs + 3) / 4);   // groups of 4 K rows + 4 V rows
-  const int rows_per_block = 16;                 // 256 threads, 16 lanes per row
-  const int grid = (n_slots + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(kv_quant_append_kernel, dim3(grid), dim3(256), 0, stream, P.base,
-                     P.num_pages, P.hkv, layer, n_pairs, k, v, dtype, slots, positions, rope_cos,
+  const int runs = (n_tok + 63) / 64;            // 64 tokens, every kv head, per workgroup
+  hipLaunchKernelGGL(kv_quant_append_kernel, dim3(runs), dim3(512), 0, stream, P.base,
+                     P.num_pages, P.hkv, layer, n_tok, k, v, dtype, slots, positions, rope_cos,
                      rope_sin, P.rotary_dim, P.hadamard, P.signs);
   return hipGetLastError();
 }

@@ -66,6 +66,7 @@ int check_rope(const nvfp4kv_pool* p, const float* c, const float* s, int32_t ma
   if (p->rotary_dim == 0) return NVFP4KV_OK;
   if (c == nullptr || s == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs rope_cos and rope_sin");
   if (max_pos <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "max_pos must be positive when rotary_dim > 0");
+  if (!aligned(c, 16) || !aligned(s, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "rope_cos and rope_sin must be 16-byte aligned");
   return NVFP4KV_OK;
 }
 
