@@ -28,6 +28,9 @@
 //         tokens), B = the weights split into fp16 high and low parts, so
 //         they keep ~22 bits (for groups of up to 8 heads both parts share
 //         one MFMA: columns 0-7 carry the high parts, 8-15 the low parts).
+// Groups of up to 8 heads take the softmax a page at a time: the QK^T of a
+// page's two units land in the two halves of each 16-lane row (the query
+// operand's other half zeroed), so one pass of exponentials covers 64 tokens.
 // Partial (m, l, acc) per (pair, wavefront) go to the workspace;
 // decode_reduce combines them per (sequence, query head).
 #include <hip/hip_runtime.h>
@@ -48,11 +51,6 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 __device__ inline h2 bits_h2(uint32_t b) { return __builtin_bit_cast(h2, b); }
 
-// Buffer resource over one 9216-byte pool block (raw buffer, gfx9 format
-// word); loads past the block's end read zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* blk) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blk), 0, kBlockBytes, 0x00020000);
-}
 // 16 bytes at block byte offset voff + soff (voff per lane, soff uniform).
 __device__ __forceinline__ u4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
@@ -97,7 +95,7 @@ constexpr float kMargin = 7.0f;
 // hold the lane's 32 codes of token c16 (+16) for dims 32*g4 .. +31; `sk`
 // points at the lane's K scale pair (blocks 2*g4, 2*g4+1) of the unit's
 // first token row in the staged page (tile stride 128 bytes).
-template <int NT>
+template <int NT, bool ACCUM = false>
 __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_t* __restrict__ sk,
                                         const h8 (&qb)[NT][4], f4 (&S)[NT][2]) {
 #pragma unroll
@@ -108,8 +106,9 @@ __device__ __forceinline__ void qk_unit(const u4& k0, const u4& k1, const uint8_
     const h2 sc = bits_h2(__builtin_amdgcn_perm(0u, ku, 0x0c010c00u) << 7);
     const h2 sc0 = __builtin_shufflevector(sc, sc, 0, 0), sc1 = __builtin_shufflevector(sc, sc, 1, 1);
     const u4& kc = i ? k1 : k0;
+    if (!ACCUM)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) S[t][i] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT; ++t) S[t][i] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t w = kc[c];
@@ -265,6 +264,10 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, co
   }
 }
 
+// Entries per row of a query-operand slot in LDS: one per lane, then a zero
+// entry (read by lanes whose operand columns are to be zero).
+constexpr int kQEntries = 65;
+
 // Query operands of one segment into an LDS slot: RoPE, Hadamard and the
 // NVFP4 round trip of the group's query columns (exact in fp16), laid out as
 // the B operands of QK^T: slot[t][c][lane] holds, for lane (c16, g4), dims
@@ -277,7 +280,7 @@ template <bool PACKED, int kPasses, bool MQ, int NT>
 __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group, int rotary_dim,
                                                 const float* __restrict__ rope_cos,
                                                 const float* __restrict__ rope_sin, int hadamard,
-                                                const SignMask& signs, _Float16* qrow, h8 (*slot)[4][64]) {
+                                                const SignMask& signs, _Float16* qrow, h8 (*slot)[4][kQEntries]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   constexpr int kTilePasses = kPasses / NT;
@@ -360,9 +363,15 @@ __device__ __forceinline__ void append_new_token(
   }
 }
 
+__device__ inline float row_ror8(float x) {
+  // the value of lane (c16 + 8) % 16 of the same 16-lane row
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
 // Partial (m, l, acc) of the columns col0 .. col0 + 15 (those below
-// `group`) to slot `slot`.
-template <bool PACKED>
+// `group`) to slot `slot`.  PAIRED: lanes c16 and c16 + 8 summed the
+// weights of different tokens of the same column, so their sums add up.
+template <bool PACKED, bool PAIRED = false>
 __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, float l_run, int c16,
                                               int g4, int group, float* __restrict__ ws_acc,
                                               float2* __restrict__ ws_ml, size_t slot, int col0) {
@@ -377,7 +386,8 @@ __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, f
         o[j][i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[j][i]), 0x128, 0xF, 0xF, false));
     }
   }
-  const float l_tot = sum4lanes(l_run);
+  float l_tot = sum4lanes(l_run);
+  if (PAIRED) l_tot += row_ror8(l_tot);
   const int col = col0 + c16;
   if (col < group) {
     // lane holds dims 32*g4 + 8i + j in o[j][i]
@@ -540,6 +550,90 @@ __device__ __forceinline__ void softmax_pick(int nvalid, int full_at, const f4 (
   if (sw) st.slot += 1;
 }
 
+// Softmax of a whole page (both 32-token units) at once, for groups of up
+// to 8 query heads.  Their query operands repeat columns 0-7 in columns
+// 8-15; QK^T of the page's first unit takes them with columns 8-15 zeroed,
+// that of its second unit with columns 0-7 zeroed and accumulates onto the
+// first, so lanes c16 < 8 hold unit 0's scores (token 16i + 4*g4 + r of the
+// page in S[i][r]) and lanes c16 >= 8 unit 1's (token 32 + 16i + 4*g4 + r),
+// and one pass of exponentials covers the page.  Lanes c16 and
+// c16 ^ 8 belong to the same query head and keep the same reference.  The
+// weight operands of the two PV steps then take the fp16 high part in
+// columns 0-7 and the exact remainder in columns 8-15, the half that lives
+// in the other lane of the pair brought over by a row rotation:
+//   unit 0 (pa): c16 < 8 own high part, c16 >= 8 partner's remainder;
+//   unit 1 (pb): c16 < 8 partner's high part, c16 >= 8 own remainder.
+__device__ __forceinline__ void pair_operands(const float (&P)[8], bool upper, h8& pa, h8& pb) {
+  u4 ua, ub;
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const float x = P[2 * s2], y = P[2 * s2 + 1];
+    const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(x, y));
+    const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-1.0f, (float)hi[0], x),
+                                                                   fmaf(-1.0f, (float)hi[1], y)));
+    const uint32_t hb = __builtin_bit_cast(uint32_t, hi), lb = __builtin_bit_cast(uint32_t, lo);
+    const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hb, 0x128, 0xF, 0xF, false);
+    const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lb, 0x128, 0xF, 0xF, false);
+    ua[s2] = upper ? lr : hb;
+    ub[s2] = upper ? lb : hr;
+  }
+  pa = __builtin_bit_cast(h8, ua);
+  pb = __builtin_bit_cast(h8, ub);
+}
+
+// Page softmax: tokens past `nvalid` (the page's valid tokens, less `cut`
+// for the lane's column) are masked when MASKED, and `sw` starts a new
+// segment (the finished one's partial goes to slot `slot` first).  The
+// reference moves only when some score passes it by kMargin.
+template <bool MASKED>
+__device__ __forceinline__ void softmax_page(const f4 (&S)[2], int g4, int c16, int nvalid,
+                                             float c_log2, f4 (&acc)[8], float& m_ref, float& l_run,
+                                             h8& pa, h8& pb, bool sw, int group,
+                                             float* __restrict__ ws_acc, float2* __restrict__ ws_ml,
+                                             size_t slot, int cut) {
+  const bool upper = c16 >= 8;
+  const int nv = nvalid - (upper ? 32 : 0) - cut;
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[4 * i + r] = S[i][r];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (!MASKED || 16 * i + 4 * g4 + r < nv) mx = fmaxf(mx, x[4 * i + r]);
+  mx *= c_log2;
+  if (sw || __builtin_amdgcn_ballot_w64(mx > m_ref + kMargin)) {
+    if (sw) {
+      write_partial<true, true>(acc, m_ref, l_run, c16, g4, group, ws_acc, ws_ml, slot, 0);
+      m_ref = -INFINITY;
+      l_run = 0.0f;
+    }
+    float mg = max4lanes(mx);
+    mg = fmaxf(mg, row_ror8(mg));
+    const float m_new = fmaxf(m_ref, mg);
+    const float alpha = m_new == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    m_ref = m_new;
+  }
+  const float off = kOff - m_ref;
+  float P[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e = __builtin_amdgcn_exp2f(fmaf(x[4 * i + r], c_log2, off));
+      if (MASKED && 16 * i + 4 * g4 + r >= nv) e = 0.0f;
+      P[4 * i + r] = e;
+      l_run += e;
+    }
+  pair_operands(P, upper, pa, pb);
+}
+
 // Query-operand slots in LDS per wave: segment s of the range uses slot
 // (s - first segment) % 3, enough for the (at most three) segments one trip
 // of the page loop touches.
@@ -585,10 +679,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
-  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][64];
+  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][kQEntries];
   __shared__ __attribute__((aligned(16))) _Float16 qrow[NT > 1 ? 8 : 16 * kHeadDim];
 
   const int lane = (int)threadIdx.x;
+  // the zero entry of every slot row
+  if (lane < kQSlots * NT * 4) q_lds[lane / (NT * 4)][(lane / 4) % NT][lane % 4][64] = h8{0, 0, 0, 0, 0, 0, 0, 0};
   const int g4 = lane >> 4;     // lane group
   const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
   const int group = qc.group;
@@ -745,14 +841,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   SegState st{(size_t)seg0 + (size_t)w};
   int q_ready = two_segs ? seg0 + 1 : seg0;   // last segment whose query operands are in LDS
   // query operands of a segment from its LDS slot
-  auto q_of = [&](int sg, h8 (&qb)[NT][4]) {
+  // (entry e: the lane's own, or 64 for zero columns)
+  auto q_of = [&](int sg, h8 (&qb)[NT][4], int e) {
     if (NT > 1) asm volatile("" ::: "memory");
     const int sl = (sg - seg0) % kQSlots;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qb[t][c] = q_lds[sl][t][c][lane];
+      for (int c = 0; c < 4; ++c) qb[t][c] = q_lds[sl][t][c][e];
   };
+  // Page softmax (one-tile groups of up to 8 heads): a page's first unit is
+  // scored with columns 8-15 zero, its second with columns 0-7 zero
+  constexpr bool kPageSoftmax = PACKED && NT == 1;
+  const int e_lo = (kPageSoftmax && c16 >= 8) ? 64 : lane;
+  const int e_hi = c16 >= 8 ? lane : 64;
   auto seg_of = [&](int64_t x) { return __builtin_amdgcn_readlane(w_sg, (int)(min(x, b - 1) - win)); };
 
   // ---- prologue: loads of the range's first two pages; unit 0's scores and
@@ -801,15 +903,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r2, voff, kKScaleOff);
-    q_of(seg0, qb);
+    q_of(seg0, qb, e_lo);
     qk_unit<NT>(kA[0], kA[1], reinterpret_cast<const uint8_t*>(&sc_lds[0][0]) + sk_off, qb, S);
     kA[0] = ld16(r2, voff, 0);
     kA[1] = ld16(r2, voff, 1024);
     vB[2] = ld16(r1, voff, kVCodeOff + 2048);
     vB[3] = ld16(r1, voff, kVCodeOff + 3072);
     __builtin_amdgcn_sched_barrier(0);
-    softmax_pick<PACKED, NT>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
-                             pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
+    // (one-tile groups of up to 8 heads take the softmax a page at a time,
+    // in the loop: page a's first unit stays scored, not yet weighted)
+    if (!kPageSoftmax)
+      softmax_pick<PACKED, NT>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+                               pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
   }
 
   // ---- main loop, two pages (p in set A, p+1 in set B) per trip.  Page p
@@ -824,6 +929,116 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // slots to whichever wavefront is behind.
   const int64_t t50 = a + (b - a) / 2, t75 = a + 3 * (b - a) / 4, t90 = a + 9 * (b - a) / 10;
   int prio_level = 0;
+  if constexpr (kPageSoftmax) {
+  // One-tile groups of up to 8 heads: the softmax covers a page (two units)
+  // at once.  S[0] holds the page's scores (its first unit in lanes c16 <
+  // 8, its second in lanes c16 >= 8), pa/pb the weight operands of its two
+  // units.  A trip: QK^T of page p's second unit, softmax of page p, PV of
+  // its first unit; QK^T of page p+1's first unit and PV of page p's
+  // second; the same for page p+1 (with QK^T of page p+2's first unit).
+  // Loads go out in the same order as in the unit-by-unit form below.
+  h8 pa, pb;
+  for (int64_t p = a; p < b; p += 2) {
+    {
+      const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
+      if (lv != prio_level) {
+        prio_level = lv;
+        if (lv == 1) __builtin_amdgcn_s_setprio(2);
+        else if (lv == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    if (min(p + 4, b - 1) - win >= 64) {   // ranges of more than 64 pages
+      const int o = (int)(p - win);
+      const int sg = __builtin_amdgcn_readlane(w_sg, o);
+      const int j = __builtin_amdgcn_readlane(w_j, o);
+      win = p;
+      load_window(sg / hkv, sg % hkv, p - j, seq_pages(seq_lens, sg / hkv));
+    }
+    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(p + 2), r3 = rsrc_of(p + 3), r4 = rsrc_of(p + 4);
+    const int nv0 = nvalid_of(p), nv1 = nvalid_of(p + 1);
+    const bool sw0 = p > a && starts_segment(p), sw1 = starts_segment(p + 1);
+    const int sg0 = seg_of(p), sg1 = seg_of(p + 1), sg2 = seg_of(p + 2);
+    while (q_ready < sg2) {
+      ++q_ready;
+      QIn<kPasses, MQ> in;
+      load_q_inputs<kPasses, MQ>(q_ready, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
+                                 rope_sin, rotary_dim, in);
+      make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, signs,
+                                               qrow, q_lds[(q_ready - seg0) % kQSlots]);
+    }
+    auto qk1 = [&]() {    // page p: tokens 32..63 scored
+      q_of(sg0, qb, e_hi);
+      qk_unit<NT, true>(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
+      kA[2] = ld16(r2, voff, 2048);
+      kA[3] = ld16(r2, voff, 3072);
+    };
+    auto pv1 = [&]() {    // page p: tokens 0..31 accumulated
+      pv_unit<PACKED, NT>(vA[0], vA[1], sb0 + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
+      vA[0] = ld16(r2, voff, kVCodeOff);
+      vA[1] = ld16(r2, voff, kVCodeOff + 1024);
+    };
+    auto blk2 = [&]() {   // page p+1 staged; its 0..31 scored, page p's 32..63 accumulated
+      sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
+      sB = ld16(r3, voff, kKScaleOff);
+      q_of(sg1, qb, e_lo);
+      qk_unit<NT>(kB[0], kB[1], sb1 + sk_off, qb, S);
+      kB[0] = ld16(r3, voff, 0);
+      kB[1] = ld16(r3, voff, 1024);
+      pv_unit<PACKED, NT>(vA[2], vA[3], sb0 + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
+      vA[2] = ld16(r2, voff, kVCodeOff + 2048);
+      vA[3] = ld16(r2, voff, kVCodeOff + 3072);
+    };
+    auto qk3 = [&]() {    // page p+1: tokens 32..63 scored
+      q_of(sg1, qb, e_hi);
+      qk_unit<NT, true>(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
+      kB[2] = ld16(r3, voff, 2048);
+      kB[3] = ld16(r3, voff, 3072);
+    };
+    auto pv3 = [&]() {    // page p+1: tokens 0..31 accumulated
+      pv_unit<PACKED, NT>(vB[0], vB[1], sb1 + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
+      vB[0] = ld16(r3, voff, kVCodeOff);
+      vB[1] = ld16(r3, voff, kVCodeOff + 1024);
+    };
+    auto blk4 = [&]() {   // page p+2 staged; its 0..31 scored, page p+1's 32..63 accumulated
+      sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
+      sA = ld16(r4, voff, kKScaleOff);
+      q_of(sg2, qb, e_lo);
+      qk_unit<NT>(kA[0], kA[1], sb0 + sk_off, qb, S);
+      kA[0] = ld16(r4, voff, 0);
+      kA[1] = ld16(r4, voff, 1024);
+      pv_unit<PACKED, NT>(vB[2], vB[3], sb1 + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
+      vB[2] = ld16(r3, voff, kVCodeOff + 2048);
+      vB[3] = ld16(r3, voff, kVCodeOff + 3072);
+    };
+    auto page_sm = [&](int nv, bool sw) {
+      if (nv >= 64 + mcut)
+        softmax_page<false>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group,
+                            ws_acc, ws_ml, st.slot, cut[0]);
+      else
+        softmax_page<true>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group,
+                           ws_acc, ws_ml, st.slot, cut[0]);
+      if (sw) st.slot += 1;
+    };
+    // (a separate path for common trips without the rescale branch, as the
+    // unit-by-unit form below has, made the register allocator keep two
+    // copies of the accumulators here; with one check per page the single
+    // path is the faster one)
+    qk1();
+    page_sm(nv0, sw0);
+    pv1();
+    blk2();
+    if (p + 1 >= b) break;
+    qk3();
+    page_sm(nv1, sw1);
+    pv3();
+    blk4();
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    write_partial<PACKED, kPageSoftmax>(acc[t], m_ref[t], l_run[t], c16, g4, group, ws_acc, ws_ml, st.slot, 16 * t);
+  return;
+  } else {
   for (int64_t p = a; p < b; p += 2) {
     {
       const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
@@ -860,7 +1075,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     // unit before it, and refills the registers it consumed with the page
     // two ahead.
     auto blk1 = [&]() {   // page p: tokens 32..63 scored, 0..31 accumulated
-      q_of(sg0, qb);
+      q_of(sg0, qb, lane);
       qk_unit<NT>(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
       kA[2] = ld16(r2, voff, 2048);
       kA[3] = ld16(r2, voff, 3072);
@@ -871,7 +1086,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     auto blk2 = [&]() {   // page p+1 staged; its 0..31 scored, page p's 32..63 accumulated
       sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
       sB = ld16(r3, voff, kKScaleOff);
-      q_of(sg1, qb);
+      q_of(sg1, qb, lane);
       qk_unit<NT>(kB[0], kB[1], sb1 + sk_off, qb, S);
       kB[0] = ld16(r3, voff, 0);
       kB[1] = ld16(r3, voff, 1024);
@@ -880,7 +1095,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       vA[3] = ld16(r2, voff, kVCodeOff + 3072);
     };
     auto blk3 = [&]() {   // page p+1: tokens 32..63 scored, 0..31 accumulated
-      q_of(sg1, qb);
+      q_of(sg1, qb, lane);
       qk_unit<NT>(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
       kB[2] = ld16(r3, voff, 2048);
       kB[3] = ld16(r3, voff, 3072);
@@ -891,7 +1106,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     auto blk4 = [&]() {   // page p+2 staged; its 0..31 scored, page p+1's 32..63 accumulated
       sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
       sA = ld16(r4, voff, kKScaleOff);
-      q_of(sg2, qb);
+      q_of(sg2, qb, lane);
       qk_unit<NT>(kA[0], kA[1], sb0 + sk_off, qb, S);
       kA[0] = ld16(r4, voff, 0);
       kA[1] = ld16(r4, voff, 1024);
@@ -935,6 +1150,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     if (bail < 4) blk4();
     softmax_pick<PACKED, NT>(nv2, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
                                 pw1, sw2, group, ws_acc, ws_ml, st, cut);
+  }
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
