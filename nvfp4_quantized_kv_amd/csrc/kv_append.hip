@@ -20,20 +20,23 @@ namespace {
 // x from lane r ^ BIT of the same 16-lane row (BIT = 1, 2, 4 or 8), through
 // DPP: quad permutes for 1 and 2; for 4 the half-row mirror (r ^ 7) then the
 // quad reversal (^ 3); for 8 the row mirror (r ^ 15) then the half-row mirror.
+// Every lane has a source lane in these patterns, so bound_ctrl is set: the
+// compiler then needs no copy of the `old` operand (and no wait states for
+// it) before each move.
 template <int BIT>
 __device__ __forceinline__ float xor_lane(float x) {
   const int i = __float_as_int(x);
   int o;
   if (BIT == 1) {
-    o = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, false);
+    o = __builtin_amdgcn_update_dpp(0, i, 0xB1, 0xF, 0xF, true);
   } else if (BIT == 2) {
-    o = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, false);
+    o = __builtin_amdgcn_update_dpp(0, i, 0x4E, 0xF, 0xF, true);
   } else if (BIT == 4) {
-    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, false), 0x1B, 0xF,
-                                    0xF, false);
+    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x141, 0xF, 0xF, true), 0x1B, 0xF,
+                                    0xF, true);
   } else {
-    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x140, 0xF, 0xF, false), 0x141, 0xF,
-                                    0xF, false);
+    o = __builtin_amdgcn_update_dpp(0, __builtin_amdgcn_update_dpp(0, i, 0x140, 0xF, 0xF, true), 0x141, 0xF,
+                                    0xF, true);
   }
   return __int_as_float(o);
 }
@@ -45,8 +48,20 @@ __device__ __forceinline__ float xor_lane(float x) {
 template <int BIT>
 __device__ __forceinline__ void fwht_stage(float (&x)[8], int r) {
   const float sgn = (r & BIT) ? -1.0f : 1.0f;
+  if (BIT >= 4) {
+    // two chained row permutes: the first for all 8 elements, then the
+    // second, so no permute waits on the one just before it
+    const int c1 = BIT == 4 ? 0x141 : 0x140, c2 = BIT == 4 ? 0x1B : 0x141;
+    int t[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(sgn, x[k], xor_lane<BIT>(x[k]));
+    for (int k = 0; k < 8; ++k) t[k] = __builtin_amdgcn_update_dpp(0, __float_as_int(x[k]), c1, 0xF, 0xF, true);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      x[k] = __builtin_fmaf(sgn, x[k], __int_as_float(__builtin_amdgcn_update_dpp(0, t[k], c2, 0xF, 0xF, true)));
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(sgn, x[k], xor_lane<BIT>(x[k]));
+  }
 }
 
 // E2M1 magnitude code of |y| for block scale s by a three-level search over
@@ -65,36 +80,49 @@ __device__ __forceinline__ uint32_t e2m1_code_search(float y, const float (&t)[7
   return c | (signbit(y) ? 8u : 0u);
 }
 
+// RoPE coefficients of lane r of a row (16 lanes, 8 elements each) at one
+// position: 16-byte vector reads of the table rows; lanes outside the
+// rotary dims read the first entries and do not use them.
+struct RopeLane {
+  float cv[8], sv[8];
+  bool first, in_rot;
+  int src;   // the lane of the row holding the partner elements
+};
+
+__device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* cos_row, const float* sin_row,
+                                          RopeLane& rl) {
+  const int half = rotary_dim / 2;          // a multiple of 8
+  const int hl = half / 8;                  // lanes per half
+  rl.first = r < hl;
+  rl.in_rot = r < 2 * hl;
+  const int base = rl.in_rot ? (rl.first ? 8 * r : 8 * r - half) : 0;
+  const float4* cp = reinterpret_cast<const float4*>(cos_row + base);
+  const float4* sp = reinterpret_cast<const float4*>(sin_row + base);
+  const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  rl.cv[0] = c0.x; rl.cv[1] = c0.y; rl.cv[2] = c0.z; rl.cv[3] = c0.w;
+  rl.cv[4] = c1.x; rl.cv[5] = c1.y; rl.cv[6] = c1.z; rl.cv[7] = c1.w;
+  rl.sv[0] = s0.x; rl.sv[1] = s0.y; rl.sv[2] = s0.z; rl.sv[3] = s0.w;
+  rl.sv[4] = s1.x; rl.sv[5] = s1.y; rl.sv[6] = s1.z; rl.sv[7] = s1.w;
+  rl.src = rl.in_rot ? (rl.first ? r + hl : r - hl) : r;
+}
+
 // The append kernel's row quantizer: what quant_row16 computes, bit for bit
 // (same binary32 operations in the same order), with the RoPE coefficients
-// read as 16-byte vectors, RoPE without branches, the transform's cross-lane
-// stages through DPP and the E2M1 code by search.  All 16 lanes of a row
-// must call it together.
-__device__ __forceinline__ void append_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
-                                             const float* sin_row, bool hadamard, uint32_t neg,
-                                             uint32_t& codes, uint32_t& scode) {
+// read beforehand (`rl`, used when `rope`), RoPE without branches, the
+// transform's cross-lane stages through DPP and the E2M1 code by search.
+// All 16 lanes of a row must call it together.
+__device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, const RopeLane& rl,
+                                             bool hadamard, uint32_t neg, uint32_t& codes, uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
-  if (rotary_dim > 0) {
-    const int half = rotary_dim / 2;          // a multiple of 8
-    const int hl = half / 8;                  // lanes per half
-    const bool first = r < hl;
-    const bool in_rot = r < 2 * hl;
-    const int base = in_rot ? (first ? 8 * r : 8 * r - half) : 0;
-    float cv[8], sv[8];
-    const float4* cp = reinterpret_cast<const float4*>(cos_row + base);
-    const float4* sp = reinterpret_cast<const float4*>(sin_row + base);
-    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-    cv[0] = c0.x; cv[1] = c0.y; cv[2] = c0.z; cv[3] = c0.w; cv[4] = c1.x; cv[5] = c1.y; cv[6] = c1.z; cv[7] = c1.w;
-    sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w; sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
-    const int src = in_rot ? (first ? r + hl : r - hl) : r;
-    const int src_lane = (lane & ~15) + src;
+  if (rope) {
+    const int src_lane = (lane & ~15) + rl.src;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float other = __shfl(x[k], src_lane, 64);
       // first half: x c - o s; second half: x c + o s (a - b is a + (-b))
-      const float t = x[k] * cv[k] + other * (first ? -sv[k] : sv[k]);
-      x[k] = in_rot ? t : x[k];
+      const float t = x[k] * rl.cv[k] + other * (rl.first ? -rl.sv[k] : rl.sv[k]);
+      x[k] = rl.in_rot ? t : x[k];
     }
   }
   if (hadamard) {
@@ -132,19 +160,60 @@ __device__ __forceinline__ void append_row16(float (&x)[8], int r, int rotary_di
   codes = w;
 }
 
+// A lane's 8 inputs of a row as raw words: bf16 (DT 1) takes 4 words, f32
+// (DT 0) 8.
+template <int DT>
+struct RawRow {
+  uint32_t w[DT == 1 ? 4 : 8];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_raw(const void* src, size_t elem_off, RawRow<DT>& rw) {
+  if (DT == 1) {
+    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + elem_off);
+    rw.w[0] = q.x; rw.w[1] = q.y; rw.w[2] = q.z; rw.w[3] = q.w;
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + elem_off);
+    const uint4 a = p[0], b = p[1];
+    rw.w[0] = a.x; rw.w[1] = a.y; rw.w[2] = a.z; rw.w[3] = a.w;
+    rw.w[4] = b.x; rw.w[5] = b.y; rw.w[6] = b.z; rw.w[7] = b.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void raw_to_float(const RawRow<DT>& rw, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < (DT == 1 ? 4 : 8); ++i) {
+    if (DT == 1) {
+      x[2 * i] = __uint_as_float(rw.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(rw.w[i] & 0xFFFF0000u);
+    } else {
+      x[i] = __uint_as_float(rw.w[i]);
+    }
+  }
+}
+
 // One workgroup (8 wavefronts) per run of 64 consecutive tokens, every kv
 // head in turn, in passes of 16 tokens: wavefronts 0-3 take the 16 tokens' K
 // rows, 4-7 their V rows (4 rows of 16 lanes each), so every wavefront's rows
 // are all K or all V and only K rows run RoPE and the rotation.  The kv heads
-// of a token share its RoPE table rows, read once into the CU's L2.  Consecutive
-// tokens of a prefill sit in consecutive slots, whose code bytes share
-// 128-byte lines (16 bytes per token in the K tiles, 4 in the V tiles) and
-// whose scale bytes do too: one workgroup completes those lines in its CU's
-// L2.  Spread over workgroups (and so over XCDs), each line was written back
-// in pieces: twice the algorithmic write traffic, measured.
+// of a token share its RoPE table rows, read once into the CU's L2.
+// Software pipeline over a wavefront's rows: an iteration first issues the
+// loads of its own RoPE coefficients, then those of the next row (its
+// token's slot and position and the row itself, unconditionally, with the
+// indices clamped), then quantizes its row; so a row's chain of dependent
+// loads (position, then table) overlaps the quantization of the row before
+// (one row per chain and nothing in flight meanwhile made the kernel bound
+// by load latency).  Consecutive tokens of a prefill sit in consecutive
+// slots, whose code bytes share 128-byte lines (16 bytes per token in the K
+// tiles, 4 in the V tiles) and whose scale bytes do too: one workgroup
+// completes those lines in its CU's L2.  Spread over workgroups (and so over
+// XCDs), each line was written back in pieces: twice the algorithmic write
+// traffic, measured.
+template <int DT>
 __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_tok,
-    const void* __restrict__ k, const void* __restrict__ v, int dtype,
+    const void* __restrict__ k, const void* __restrict__ v,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, SignMask signs) {
@@ -155,28 +224,45 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
   const int rot = which ? 0 : rotary_dim;
   const bool had = which ? false : (hadamard != 0);
   const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
+  const void* src = which ? v : k;
+  const int n_it = 4 * hkv;
+  // token of iteration `it` (kv head it % hkv, pass it / hkv); lanes past
+  // the last token take a copy of the last token's row of their kind (they
+  // still take part in the shuffles) and store nothing
+  auto token = [&](int it) {
+    return min((int)blockIdx.x * 64 + (it / hkv) * 16 + (wv & 3) * 4 + (lane >> 4), n_tok - 1);
+  };
+  // the next row's inputs, loaded one iteration ahead
+  auto fetch = [&](int it, int64_t& slot, int& pos, RawRow<DT>& rw) {
+    it = min(it, n_it - 1);
+    const int tok = token(it);
+    slot = slots[tok];
+    pos = rot > 0 ? positions[tok] : 0;
+    load_raw<DT>(src, ((size_t)tok * hkv + it % hkv) * kHeadDim + 8 * r, rw);
+  };
+  int64_t slot;
+  int pos;
+  RawRow<DT> rw;
+  fetch(0, slot, pos, rw);
 #pragma unroll 1
-  for (int it = 0; it < 4 * hkv; ++it) {
-    const int g = it % hkv, pass = it / hkv;
-    int tok = (int)blockIdx.x * 64 + pass * 16 + (wv & 3) * 4 + (lane >> 4);
-    // Lanes past the last token still take part in the shuffles, on a copy
-    // of the last token's row of their kind, and store nothing.
-    const bool active = tok < n_tok;
-    tok = active ? tok : n_tok - 1;
-    const size_t elem_off = ((size_t)tok * hkv + g) * kHeadDim + 8 * r;
+  for (int it = 0; it < n_it; ++it) {
+    const int g = it % hkv;
+    const bool active = (int)blockIdx.x * 64 + (it / hkv) * 16 + (wv & 3) * 4 + (lane >> 4) < n_tok;
+    RopeLane rl;
+    if (rot > 0)
+      rope_lane(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2), rope_sin + (size_t)pos * (rotary_dim / 2),
+                rl);
+    __builtin_amdgcn_sched_barrier(0);
+    int64_t slot_n;
+    int pos_n;
+    RawRow<DT> rw_n;
+    fetch(it + 1, slot_n, pos_n, rw_n);
+    __builtin_amdgcn_sched_barrier(0);
     float x[8];
-    load8(which ? v : k, dtype, elem_off, x);
-    const float* crow = nullptr;
-    const float* srow = nullptr;
-    if (rot > 0) {
-      const int pos = positions[tok];
-      crow = rope_cos + (size_t)pos * (rotary_dim / 2);
-      srow = rope_sin + (size_t)pos * (rotary_dim / 2);
-    }
+    raw_to_float<DT>(rw, x);
     uint32_t codes, scode;
-    append_row16(x, r, rot, crow, srow, had, neg, codes, scode);
+    append_row16(x, r, rot > 0, rl, had, neg, codes, scode);
     if (active) {
-      const int64_t slot = slots[tok];
       const int64_t page = slot / kPageSize;
       const uint32_t t = (uint32_t)(slot % kPageSize);
       uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
@@ -185,6 +271,9 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
       *reinterpret_cast<uint32_t*>(blk + woff) = codes;
       if ((r & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + r / 2] = (uint8_t)scode;
     }
+    slot = slot_n;
+    pos = pos_n;
+    rw = rw_n;
   }
 }
 
@@ -268,9 +357,9 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
                          int dtype, const int64_t* slots, const int32_t* positions,
                          const float* rope_cos, const float* rope_sin, hipStream_t stream) {
   const int runs = (n_tok + 63) / 64;            // 64 tokens, every kv head, per workgroup
-  hipLaunchKernelGGL(kv_quant_append_kernel, dim3(runs), dim3(512), 0, stream, P.base,
-                     P.num_pages, P.hkv, layer, n_tok, k, v, dtype, slots, positions, rope_cos,
-                     rope_sin, P.rotary_dim, P.hadamard, P.signs);
+  auto kern = dtype == 1 ? kv_quant_append_kernel<1> : kv_quant_append_kernel<0>;
+  hipLaunchKernelGGL(kern, dim3(runs), dim3(512), 0, stream, P.base, P.num_pages, P.hkv, layer, n_tok, k,
+                     v, slots, positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs);
   return hipGetLastError();
 }
 
