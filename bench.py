@@ -495,7 +495,8 @@ def bench_append(args, step, wl, torch, kv, W):
         "tokens_per_s": round(n_tok / t, 1),
         "roofline": {"bound": "hbm", "kernel": "kv_quant_append_kernel", "achieved": round(gbps, 2),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": None, "algo_bytes_per_launch": in_bytes + out_bytes},
+                     "traffic": traffic_from_profiles("kv_quant_append", wl.name),
+                     "algo_bytes_per_launch": in_bytes + out_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
