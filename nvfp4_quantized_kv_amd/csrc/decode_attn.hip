@@ -265,8 +265,11 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, co
 }
 
 // Entries per row of a query-operand slot in LDS: one per lane, then a zero
-// entry (read by lanes whose operand columns are to be zero).
-constexpr int kQEntries = 65;
+// entry (read by lanes whose operand columns are to be zero).  For groups
+// of up to 8 heads (PACKED) lanes c16 and c16 + 8 take the same operand: one
+// entry per (g4, c16 % 8), 32 of them, then the zero entry.
+template <bool PACKED>
+constexpr int q_entries() { return PACKED ? 33 : 65; }
 
 // Query operands of one segment into an LDS slot: RoPE, Hadamard and the
 // NVFP4 round trip of the group's query columns (exact in fp16), laid out as
@@ -280,13 +283,17 @@ template <bool PACKED, int kPasses, bool MQ, int NT>
 __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group, int rotary_dim,
                                                 const float* __restrict__ rope_cos,
                                                 const float* __restrict__ rope_sin, int hadamard,
-                                                const SignMask& signs, _Float16* qrow, h8 (*slot)[4][kQEntries]) {
+                                                const SignMask& signs, _Float16* qrow,
+                                                h8 (*slot)[4][q_entries<PACKED>()]) {
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   constexpr int kTilePasses = kPasses / NT;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-  _Float16* rows = NT > 1 ? reinterpret_cast<_Float16*>(&slot[t][0][0]) : qrow;
+  // (rows staged in the slot itself when it holds them: several tiles, or
+  // the up to 8 rows of a packed group)
+  constexpr bool kInSlot = NT > 1 || PACKED;
+  _Float16* rows = kInSlot ? reinterpret_cast<_Float16*>(&slot[t][0][0]) : qrow;
 #pragma unroll
   for (int pass = kTilePasses * t; pass < kTilePasses * (t + 1); ++pass) {
     if (pass * 4 >= group) break;
@@ -316,9 +323,14 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
     h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
     v[c] = (16 * t + qcol < group) ? *reinterpret_cast<const h8*>(&rows[qcol * kHeadDim + 32 * g4 + 8 * c]) : z;
   }
-  if (NT > 1) __syncthreads();   // every row read before the slot is rewritten
+  if (kInSlot) __syncthreads();   // every row read before the slot is rewritten
 #pragma unroll
-  for (int c = 0; c < 4; ++c) slot[t][c][lane] = v[c];
+  for (int c = 0; c < 4; ++c) {
+    if (!PACKED) slot[t][c][lane] = v[c];
+    else if (c16 < 8) slot[t][c][g4 * 8 + c16] = v[c];
+  }
+  // the zero entries (rows staged in the slot may have covered them)
+  if (lane < 4) slot[t][lane][q_entries<PACKED>() - 1] = h8{0, 0, 0, 0, 0, 0, 0, 0};
   __syncthreads();
   }
 }
@@ -679,12 +691,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
     float2* __restrict__ ws_ml) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
-  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][kQEntries];
-  __shared__ __attribute__((aligned(16))) _Float16 qrow[NT > 1 ? 8 : 16 * kHeadDim];
+  constexpr int kQE = q_entries<PACKED>();
+  __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][kQE];
+  __shared__ __attribute__((aligned(16))) _Float16 qrow[(NT > 1 || PACKED) ? 8 : 16 * kHeadDim];
 
   const int lane = (int)threadIdx.x;
   // the zero entry of every slot row
-  if (lane < kQSlots * NT * 4) q_lds[lane / (NT * 4)][(lane / 4) % NT][lane % 4][64] = h8{0, 0, 0, 0, 0, 0, 0, 0};
+  if (lane < kQSlots * NT * 4) q_lds[lane / (NT * 4)][(lane / 4) % NT][lane % 4][kQE - 1] = h8{0, 0, 0, 0, 0, 0, 0, 0};
   const int g4 = lane >> 4;     // lane group
   const int c16 = lane & 15;    // column: query head for S/P/O, operand row for K/V
   const int group = qc.group;
@@ -841,7 +854,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   SegState st{(size_t)seg0 + (size_t)w};
   int q_ready = two_segs ? seg0 + 1 : seg0;   // last segment whose query operands are in LDS
   // query operands of a segment from its LDS slot
-  // (entry e: the lane's own, or 64 for zero columns)
+  // (entry e: the lane's own, or kQE - 1 for zero columns)
   auto q_of = [&](int sg, h8 (&qb)[NT][4], int e) {
     if (NT > 1) asm volatile("" ::: "memory");
     const int sl = (sg - seg0) % kQSlots;
@@ -853,8 +866,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // Page softmax (one-tile groups of up to 8 heads): a page's first unit is
   // scored with columns 8-15 zero, its second with columns 0-7 zero
   constexpr bool kPageSoftmax = PACKED && NT == 1;
-  const int e_lo = (kPageSoftmax && c16 >= 8) ? 64 : lane;
-  const int e_hi = c16 >= 8 ? lane : 64;
+  const int e_own = PACKED ? g4 * 8 + (c16 & 7) : lane;
+  const int e_lo = (kPageSoftmax && c16 >= 8) ? kQE - 1 : e_own;
+  const int e_hi = c16 >= 8 ? e_own : kQE - 1;
   auto seg_of = [&](int64_t x) { return __builtin_amdgcn_readlane(w_sg, (int)(min(x, b - 1) - win)); };
 
   // ---- prologue: loads of the range's first two pages; unit 0's scores and
@@ -862,7 +876,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // loop's back edge, so the wait counts at the loop head are the same on
   // entry and on the back edge.
   u4 kA[4], vA[4], sA, kB[4], vB[4], sB;
-  {
+  if constexpr (kPageSoftmax) {
+    // one register set, loads one page ahead: page a's scales, K and V
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a);
+    sA = ld16(r0, voff, kKScaleOff);
+    kA[0] = ld16(r0, voff, 0);
+    kA[1] = ld16(r0, voff, 1024);
+    kA[2] = ld16(r0, voff, 2048);
+    kA[3] = ld16(r0, voff, 3072);
+    vA[0] = ld16(r0, voff, kVCodeOff);
+    vA[1] = ld16(r0, voff, kVCodeOff + 1024);
+    vA[2] = ld16(r0, voff, kVCodeOff + 2048);
+    vA[3] = ld16(r0, voff, kVCodeOff + 3072);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
     const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a), r1 = rsrc_of(a + 1);
     sA = ld16(r0, voff, kKScaleOff);
     kA[0] = ld16(r0, voff, 0);
@@ -899,6 +926,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   }
   f4 S[NT][2];
   h8 pw0[NT], pw1[NT], qb[NT][4];
+  if constexpr (kPageSoftmax) {
+    // page a staged and scored (both units); its scales in buffer 0, then
+    // page a+1's scales and K on their way
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1);
+    sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
+    sA = ld16(r1, voff, kKScaleOff);
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
+    q_of(seg0, qb, e_lo);
+    qk_unit<NT>(kA[0], kA[1], sb + sk_off, qb, S);
+    kA[0] = ld16(r1, voff, 0);
+    kA[1] = ld16(r1, voff, 1024);
+    q_of(seg0, qb, e_hi);
+    qk_unit<NT, true>(kA[2], kA[3], sb + sk_off + 256, qb, S);
+    kA[2] = ld16(r1, voff, 2048);
+    kA[3] = ld16(r1, voff, 3072);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
   {
     const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
@@ -917,6 +961,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
                                pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
   }
 
+  }
   // ---- main loop, two pages (p in set A, p+1 in set B) per trip.  Page p
   // is staged in LDS buffer 0, page p+1 in buffer 1.
   const uint8_t* sb0 = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
@@ -931,14 +976,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   int prio_level = 0;
   if constexpr (kPageSoftmax) {
   // One-tile groups of up to 8 heads: the softmax covers a page (two units)
-  // at once.  S[0] holds the page's scores (its first unit in lanes c16 <
-  // 8, its second in lanes c16 >= 8), pa/pb the weight operands of its two
-  // units.  A trip: QK^T of page p's second unit, softmax of page p, PV of
-  // its first unit; QK^T of page p+1's first unit and PV of page p's
-  // second; the same for page p+1 (with QK^T of page p+2's first unit).
-  // Loads go out in the same order as in the unit-by-unit form below.
+  // at once, and a page is one block of the software pipeline, its loads
+  // one page ahead in one register set: softmax of page p (its scores made
+  // by the block before), PV of its two units, QK^T of page p+1's two units.
+  // At the top of the block for page p: S[0] holds page p's scores (its
+  // first unit in lanes c16 < 8, its second in lanes c16 >= 8); page p's
+  // scales are staged in LDS buffer (p - a) % 2; the registers hold page
+  // p's V codes and page p+1's K codes and scales, in flight.  pa/pb are
+  // the weight operands of page p's two units.
   h8 pa, pb;
-  for (int64_t p = a; p < b; p += 2) {
+  for (int64_t p = a; p < b; ++p) {
     {
       const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
       if (lv != prio_level) {
@@ -948,18 +995,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
         else __builtin_amdgcn_s_setprio(0);
       }
     }
-    if (min(p + 4, b - 1) - win >= 64) {   // ranges of more than 64 pages
+    if (min(p + 2, b - 1) - win >= 64) {   // ranges of more than 64 pages
       const int o = (int)(p - win);
       const int sg = __builtin_amdgcn_readlane(w_sg, o);
       const int j = __builtin_amdgcn_readlane(w_j, o);
       win = p;
       load_window(sg / hkv, sg % hkv, p - j, seq_pages(seq_lens, sg / hkv));
     }
-    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(p + 2), r3 = rsrc_of(p + 3), r4 = rsrc_of(p + 4);
-    const int nv0 = nvalid_of(p), nv1 = nvalid_of(p + 1);
-    const bool sw0 = p > a && starts_segment(p), sw1 = starts_segment(p + 1);
-    const int sg0 = seg_of(p), sg1 = seg_of(p + 1), sg2 = seg_of(p + 2);
-    while (q_ready < sg2) {
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(p + 1), r2 = rsrc_of(p + 2);
+    const int nv = nvalid_of(p);
+    const bool sw = p > a && starts_segment(p);
+    const int sg1 = seg_of(p + 1);
+    // query operands of a segment that starts at page p+1 (rare)
+    while (q_ready < sg1) {
       ++q_ready;
       QIn<kPasses, MQ> in;
       load_q_inputs<kPasses, MQ>(q_ready, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
@@ -967,72 +1015,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, signs,
                                                qrow, q_lds[(q_ready - seg0) % kQSlots]);
     }
-    auto qk1 = [&]() {    // page p: tokens 32..63 scored
-      q_of(sg0, qb, e_hi);
-      qk_unit<NT, true>(kA[2], kA[3], sb0 + sk_off + 256, qb, S);
-      kA[2] = ld16(r2, voff, 2048);
-      kA[3] = ld16(r2, voff, 3072);
-    };
-    auto pv1 = [&]() {    // page p: tokens 0..31 accumulated
-      pv_unit<PACKED, NT>(vA[0], vA[1], sb0 + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
-      vA[0] = ld16(r2, voff, kVCodeOff);
-      vA[1] = ld16(r2, voff, kVCodeOff + 1024);
-    };
-    auto blk2 = [&]() {   // page p+1 staged; its 0..31 scored, page p's 32..63 accumulated
-      sc_lds[1][lane] = sB & 0x7F7F7F7Fu;
-      sB = ld16(r3, voff, kKScaleOff);
-      q_of(sg1, qb, e_lo);
-      qk_unit<NT>(kB[0], kB[1], sb1 + sk_off, qb, S);
-      kB[0] = ld16(r3, voff, 0);
-      kB[1] = ld16(r3, voff, 1024);
-      pv_unit<PACKED, NT>(vA[2], vA[3], sb0 + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
-      vA[2] = ld16(r2, voff, kVCodeOff + 2048);
-      vA[3] = ld16(r2, voff, kVCodeOff + 3072);
-    };
-    auto qk3 = [&]() {    // page p+1: tokens 32..63 scored
-      q_of(sg1, qb, e_hi);
-      qk_unit<NT, true>(kB[2], kB[3], sb1 + sk_off + 256, qb, S);
-      kB[2] = ld16(r3, voff, 2048);
-      kB[3] = ld16(r3, voff, 3072);
-    };
-    auto pv3 = [&]() {    // page p+1: tokens 0..31 accumulated
-      pv_unit<PACKED, NT>(vB[0], vB[1], sb1 + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
-      vB[0] = ld16(r3, voff, kVCodeOff);
-      vB[1] = ld16(r3, voff, kVCodeOff + 1024);
-    };
-    auto blk4 = [&]() {   // page p+2 staged; its 0..31 scored, page p+1's 32..63 accumulated
-      sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
-      sA = ld16(r4, voff, kKScaleOff);
-      q_of(sg2, qb, e_lo);
-      qk_unit<NT>(kA[0], kA[1], sb0 + sk_off, qb, S);
-      kA[0] = ld16(r4, voff, 0);
-      kA[1] = ld16(r4, voff, 1024);
-      pv_unit<PACKED, NT>(vB[2], vB[3], sb1 + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
-      vB[2] = ld16(r3, voff, kVCodeOff + 2048);
-      vB[3] = ld16(r3, voff, kVCodeOff + 3072);
-    };
-    auto page_sm = [&](int nv, bool sw) {
-      if (nv >= 64 + mcut)
-        softmax_page<false>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group,
-                            ws_acc, ws_ml, st.slot, cut[0]);
-      else
-        softmax_page<true>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group,
-                           ws_acc, ws_ml, st.slot, cut[0]);
-      if (sw) st.slot += 1;
-    };
-    // (a separate path for common trips without the rescale branch, as the
-    // unit-by-unit form below has, made the register allocator keep two
-    // copies of the accumulators here; with one check per page the single
-    // path is the faster one)
-    qk1();
-    page_sm(nv0, sw0);
-    pv1();
-    blk2();
-    if (p + 1 >= b) break;
-    qk3();
-    page_sm(nv1, sw1);
-    pv3();
-    blk4();
+    const int cur = (int)((p - a) & 1);
+    const uint8_t* sb_cur = reinterpret_cast<const uint8_t*>(&sc_lds[cur][0]);
+    const uint8_t* sb_nxt = reinterpret_cast<const uint8_t*>(&sc_lds[cur ^ 1][0]);
+    // page p+1's scales staged, page p+2's on their way
+    sc_lds[cur ^ 1][lane] = sA & 0x7F7F7F7Fu;
+    sA = ld16(r2, voff, kKScaleOff);
+    if (nv >= 64 + mcut)
+      softmax_page<false>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group, ws_acc,
+                          ws_ml, st.slot, cut[0]);
+    else
+      softmax_page<true>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group, ws_acc,
+                         ws_ml, st.slot, cut[0]);
+    if (sw) st.slot += 1;
+    pv_unit<PACKED, NT>(vA[0], vA[1], sb_cur + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
+    vA[0] = ld16(r1, voff, kVCodeOff);
+    vA[1] = ld16(r1, voff, kVCodeOff + 1024);
+    pv_unit<PACKED, NT>(vA[2], vA[3], sb_cur + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
+    vA[2] = ld16(r1, voff, kVCodeOff + 2048);
+    vA[3] = ld16(r1, voff, kVCodeOff + 3072);
+    q_of(sg1, qb, e_lo);
+    qk_unit<NT>(kA[0], kA[1], sb_nxt + sk_off, qb, S);
+    kA[0] = ld16(r2, voff, 0);
+    kA[1] = ld16(r2, voff, 1024);
+    q_of(sg1, qb, e_hi);
+    qk_unit<NT, true>(kA[2], kA[3], sb_nxt + sk_off + 256, qb, S);
+    kA[2] = ld16(r2, voff, 2048);
+    kA[3] = ld16(r2, voff, 3072);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t)
@@ -1297,16 +1306,16 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
   return hipGetLastError();
 }
 
-int decode_waves_per_cu(int nt) {
+int decode_waves_per_cu(int nt, bool packed) {
   int lo = 1 << 30;
-  const void* one[4] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false, 1>),
-                        reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false, 1>),
-                        reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true, 1>),
+  const void* one_packed[2] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false, 1>),
+                               reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true, 1>)};
+  const void* one[2] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false, 1>),
                         reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 1>)};
   const void* two[1] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 2>)};
   const void* three[1] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, true, 3>)};
-  const int n = nt == 3 || nt == 2 ? 1 : 4;
-  const void* const* kernels = nt == 3 ? three : nt == 2 ? two : one;
+  const int n = nt == 3 || nt == 2 ? 1 : 2;
+  const void* const* kernels = nt == 3 ? three : nt == 2 ? two : packed ? one_packed : one;
   for (int i = 0; i < n; ++i) {
     const void* k = kernels[i];
     int blocks = 0;

@@ -85,29 +85,31 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   return L;
 }
 
-// Resident wavefronts of the decode kernels with `nt` column tiles on the
-// current device: CUs times one-wavefront workgroups per CU.  Cached per
-// device; if the device cannot be queried (no GPU), 256 CUs x 8 (x 4 for
-// several tiles) is assumed so that size queries still work.
-int resident_decode_waves(int nt) {
-  static int cached[64][4] = {};
+// Resident wavefronts of the decode kernels with `nt` column tiles (for one
+// tile, packed groups or not) on the current device: CUs times one-wavefront
+// workgroups per CU.  Cached per device; if the device cannot be queried (no
+// GPU), 256 CUs x 8 (one tile) or 4 (several tiles) is assumed so that size
+// queries still work.
+int resident_decode_waves(int nt, bool packed) {
+  static int cached[64][4][2] = {};
   const int fallback = nt > 1 ? 256 * 4 : 256 * 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return fallback;
   }
-  if (cached[dev][nt] == 0) {
+  int& c = cached[dev][nt][packed ? 1 : 0];
+  if (c == 0) {
     int cus = 0;
-    const int per_cu = nvfp4kv::decode_waves_per_cu(nt);
+    const int per_cu = nvfp4kv::decode_waves_per_cu(nt, packed);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
       (void)hipGetLastError();
       return fallback;
     }
-    cached[dev][nt] = cus * per_cu;
+    c = cus * per_cu;
   }
-  return cached[dev][nt];
+  return c;
 }
 
 // Split-K plan.  The flattened (sequence, kv head, page) work is shared
@@ -132,7 +134,7 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   const int64_t max_total = (int64_t)n_seq * p->num_kv_heads * max_pages;
   int64_t waves;
   if (pages_per_split == 0)
-    waves = resident_decode_waves(nvfp4kv::decode_column_tiles(group));
+    waves = resident_decode_waves(nvfp4kv::decode_column_tiles(group), group <= 8);
   else
     waves = (max_total + pages_per_split - 1) / pages_per_split;
   waves = std::max<int64_t>(1, std::min<int64_t>(waves, std::min<int64_t>(max_total, (int64_t)1 << 24)));

@@ -67,8 +67,9 @@ constexpr int kMaxDecodeColumns = 48;
 inline int decode_column_tiles(int group) { return (group + 15) / 16; }
 
 // Resident one-wavefront decode workgroups per CU for the kernels with `nt`
-// column tiles (0 if the query fails).
-int decode_waves_per_cu(int nt);
+// column tiles, for one tile those of packed groups (up to 8 query columns)
+// or the others (0 if the query fails).
+int decode_waves_per_cu(int nt, bool packed);
 
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,
