@@ -76,6 +76,27 @@ def copy_ceiling_gbps(torch) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def stream_read_ceiling_gbps(step, wl, torch, kv) -> float:
+    """Achieved rate of nvfp4kv_stream_read over layer 0: every block a decode
+    launch reads, with the decode kernel's loads, one wavefront per resident
+    decode slot (8 per CU), no compute.  The measured ceiling of the decode
+    access pattern on this device."""
+    n_waves = torch.cuda.get_device_properties(0).multi_processor_count * 8
+    words = torch.empty(n_waves, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        kv.nvfp4kv_stream_read(step.pool, 0, step.table, step.seq_lens, n_waves, words)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        kv.nvfp4kv_stream_read(step.pool, 0, step.table, step.seq_lens, n_waves, words)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return wl.decode_bytes_per_layer() / (ms * 1e-3) / 1e9
+
+
 def traffic_from_profiles(kernel_tag: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
     taken on the current kernel source (same hash); else None."""
@@ -198,6 +219,9 @@ def main():
     tok_heads = sum(wl.seq_lens) * wl.hkv * wl.layers
     achieved = bytes_per_layer / (avg_kernel_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles("decode_attn_splitk", wl.name)
+    read_ceiling = None if args.no_ceiling else stream_read_ceiling_gbps(step, wl, torch, kv)
+    if read_ceiling:
+        log(f"stream-read ceiling of the same blocks {read_ceiling:.0f} GB/s")
 
     cpu = None
     parity_err = None
@@ -242,7 +266,9 @@ def main():
             "traffic": traffic,
             "avg_launch_us": round(avg_kernel_ms * 1e3, 2),
             "algo_bytes_per_launch": bytes_per_layer,
+            "frac_of_stream_read_ceiling": round(achieved / read_ceiling, 4) if read_ceiling else None,
         },
+        "stream_read_ceiling_gbps": round(read_ceiling, 1) if read_ceiling else None,
         "hbm_copy_ceiling_gbps": round(ceiling, 1) if ceiling else None,
         "cpu_baseline": cpu,
         "parity_max_abs_err_layer0": parity_err,

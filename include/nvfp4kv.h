@@ -266,6 +266,25 @@ int nvfp4kv_spill_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* p
 int nvfp4kv_restore_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids,
                           const void* arena, size_t arena_bytes, hipStream_t stream);
 
+/* Read-bandwidth probe of the decode access pattern (a measurement aid, not
+ * a step of the method): reads every 9216-byte block of `layer` that
+ * nvfp4kv_decode_attn over the same sequences reads (segment seq *
+ * num_kv_heads + kvh holds pages 0 .. ceil(seq_lens[seq] / 64) - 1 of the
+ * sequence, segments in order), split into n_waves equal ranges of that flat
+ * list, one wavefront each, with the decode kernel's loads (nine 16-byte
+ * non-temporal loads per lane and block, the next block in flight), and
+ * writes the XOR of the 32-bit words wavefront w read to words[w].  The XOR
+ * of all n_waves words is the XOR of every 32-bit word of those blocks,
+ * whatever the split.
+ *   page_table  [n_seq][page_table_stride] int32 page ids (device)
+ *   seq_lens    [n_seq] int32 (device), >= 0
+ *   words       [n_waves] uint32 (device)
+ * Device-side contents are trusted, as for decode.  One kernel, asynchronous
+ * on `stream`. */
+int nvfp4kv_stream_read(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, const int32_t* page_table,
+                        int32_t page_table_stride, const int32_t* seq_lens, int32_t n_waves, uint32_t* words,
+                        hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on the same thread. */
 const char* nvfp4kv_last_error(void);

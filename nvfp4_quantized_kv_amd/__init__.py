@@ -79,6 +79,8 @@ def _load():
     L.nvfp4kv_spill_pages.restype = ctypes.c_int
     L.nvfp4kv_restore_pages.argtypes = [PD, i32, P, P, sz, P]
     L.nvfp4kv_restore_pages.restype = ctypes.c_int
+    L.nvfp4kv_stream_read.argtypes = [PD, i32, i32, P, i32, P, i32, P, P]
+    L.nvfp4kv_stream_read.restype = ctypes.c_int
     L.nvfp4kv_last_error.argtypes = []
     L.nvfp4kv_last_error.restype = ctypes.c_char_p
     L.nvfp4kv_version.argtypes = []
@@ -92,7 +94,7 @@ EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
             "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_splits",
             "nvfp4kv_decode_reduce", "nvfp4kv_decode_multi_workspace_bytes", "nvfp4kv_decode_attn_multi",
             "nvfp4kv_dequant", "nvfp4kv_page_bytes", "nvfp4kv_spill_pages", "nvfp4kv_restore_pages",
-            "nvfp4kv_last_error", "nvfp4kv_version"]
+            "nvfp4kv_stream_read", "nvfp4kv_last_error", "nvfp4kv_version"]
 
 
 def lib() -> ctypes.CDLL:
@@ -353,6 +355,23 @@ def nvfp4kv_spill_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tensor 
            _lib.nvfp4kv_spill_pages(ctypes.byref(d), n, _ptr(page_ids), _ptr(arena),
                                     arena.numel(), _stream(stream)))
     return arena
+
+
+def nvfp4kv_stream_read(pool: Pool, layer: int, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                        n_waves: int, words: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Read-bandwidth probe: read every block of `layer` that decode over these
+    sequences reads, n_waves wavefronts; returns the [n_waves] int32 (uint32
+    bits) XOR words."""
+    assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+    assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous()
+    if words is None:
+        words = torch.empty(n_waves, dtype=torch.int32, device=page_table.device)
+    d = pool.desc()
+    _check("nvfp4kv_stream_read",
+           _lib.nvfp4kv_stream_read(ctypes.byref(d), int(layer), seq_lens.numel(), _ptr(page_table),
+                                    page_table.shape[1], _ptr(seq_lens), int(n_waves), _ptr(words),
+                                    _stream(stream)))
+    return words
 
 
 def nvfp4kv_restore_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tensor, stream=None) -> None:

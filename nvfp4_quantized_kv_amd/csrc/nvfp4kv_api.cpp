@@ -470,6 +470,24 @@ int nvfp4kv_restore_pages(const nvfp4kv_pool* p, int32_t n_pages, const int32_t*
   return page_copy(p, n_pages, page_ids, arena, arena_bytes, false, stream);
 }
 
+int nvfp4kv_stream_read(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, const int32_t* page_table,
+                        int32_t page_table_stride, const int32_t* seq_lens, int32_t n_waves, uint32_t* words,
+                        hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
+  if (n_seq <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+  if (n_waves <= 0 || n_waves > (1 << 24)) return fail(NVFP4KV_ERR_INVALID_ARG, "n_waves %d out of range (1..2^24)", n_waves);
+  if (page_table == nullptr || seq_lens == nullptr || words == nullptr)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "null page_table, seq_lens or words");
+  if (page_table_stride <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride must be positive");
+  hipError_t e = nvfp4kv::launch_stream_read(launch_pool(p), layer, n_seq, page_table, page_table_stride,
+                                             seq_lens, n_waves, words, stream);
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  return NVFP4KV_OK;
+}
+
 int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const int64_t* slots,
                     void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
                     hipStream_t stream) {

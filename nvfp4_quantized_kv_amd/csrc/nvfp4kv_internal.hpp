@@ -80,6 +80,13 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
 hipError_t launch_page_copy(const LaunchPool& P, int num_layers, int n_pages, const int32_t* page_ids,
                             uint8_t* arena, bool to_arena, hipStream_t stream);
 
+// Reads every block of `layer` that a decode call over the same sequences
+// reads, split over n_waves wavefronts; words[w] gets the XOR of wave w's
+// 32-bit words.
+hipError_t launch_stream_read(const LaunchPool& P, int layer, int n_seq, const int32_t* page_table,
+                              int page_table_stride, const int32_t* seq_lens, int n_waves, uint32_t* words,
+                              hipStream_t stream);
+
 hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64_t* slots,
                           void* k_out, void* v_out, int dtype, int unrotate, hipStream_t stream);
 

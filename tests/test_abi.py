@@ -215,3 +215,20 @@ def test_decode_multi_workspace_query(kv):
     assert 7 * one - 1024 <= m7 <= 7 * one + 1024
     assert 8 * one - 1024 <= m10 <= 8 * one + 1024
     assert L.nvfp4kv_decode_multi_workspace_bytes(ctypes.byref(d), 3, 0, 24, 1000, 0) == 0
+
+
+def test_stream_read_rejects_bad_arguments(kv):
+    """The read-bandwidth probe checks its arguments on the host before any
+    launch."""
+    d = _desc(kv)
+    L = kv.lib()
+    f = L.nvfp4kv_stream_read
+    assert f(ctypes.byref(d), 0, 0, 4096, 16, 4096, 64, 4096, None) == -1      # n_seq 0
+    assert f(ctypes.byref(d), 0, 2, 4096, 16, 4096, 0, 4096, None) == -1      # no wavefronts
+    assert "n_waves" in kv.nvfp4kv_last_error()
+    assert f(ctypes.byref(d), 0, 2, 4096, 16, 4096, (1 << 24) + 1, 4096, None) == -1
+    assert f(ctypes.byref(d), 0, 2, None, 16, 4096, 64, 4096, None) == -1
+    assert f(ctypes.byref(d), 0, 2, 4096, 16, None, 64, 4096, None) == -1
+    assert f(ctypes.byref(d), 0, 2, 4096, 16, 4096, 64, None, None) == -1
+    assert f(ctypes.byref(d), 0, 2, 4096, 0, 4096, 64, 4096, None) == -1      # stride
+    assert f(ctypes.byref(d), 99, 2, 4096, 16, 4096, 64, 4096, None) == -1     # layer
