@@ -82,6 +82,16 @@ typedef struct {
     uint32_t hadamard_signs[4]; /* hadamard 2 only: element j of K and Q rows is
                                    negated before the transform when bit j % 32
                                    of word j / 32 is set; the caller draws it */
+    float k_scale;          /* per-tensor global scale of K, 0 meaning 1: append
+                               multiplies each K input element by the binary32
+                               1/k_scale before RoPE and quantization, so the
+                               E4M3 block scales see amax/k_scale; dequant and
+                               decode multiply the stored values back by it.
+                               0 or a finite value in [2^-64, 2^64].  NVFP4's
+                               second scaling level (a tensor-wide FP32 factor
+                               over the block scales); the release post keeps
+                               it at 1 */
+    float v_scale;          /* the same for V */
 } nvfp4kv_pool;
 
 /* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144.

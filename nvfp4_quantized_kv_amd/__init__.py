@@ -41,6 +41,8 @@ class _PoolDesc(ctypes.Structure):
         ("rotary_dim", ctypes.c_int32),
         ("hadamard", ctypes.c_int32),
         ("hadamard_signs", ctypes.c_uint32 * 4),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -136,23 +138,27 @@ class Pool:
     rotary_dim: int = 0
     hadamard: int = 1           # 0 none, 1 Hadamard rotation, 2 randomized rotation
     signs: tuple = (0, 0, 0, 0)  # hadamard 2: 128-bit element mask, 4 uint32 words
+    k_scale: float = 1.0        # per-tensor global scales of K and V (stored values are x / scale)
+    v_scale: float = 1.0
 
     @classmethod
     def allocate(cls, num_pages: int, num_layers: int, num_kv_heads: int, rotary_dim: int = 0,
-                 hadamard: int = 1, device="cuda", signs=(0, 0, 0, 0)) -> "Pool":
+                 hadamard: int = 1, device="cuda", signs=(0, 0, 0, 0), k_scale: float = 1.0,
+                 v_scale: float = 1.0) -> "Pool":
         signs = tuple(int(x) & 0xFFFFFFFF for x in signs)
         desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE,
-                         rotary_dim, int(hadamard), (ctypes.c_uint32 * 4)(*signs))
+                         rotary_dim, int(hadamard), (ctypes.c_uint32 * 4)(*signs), k_scale, v_scale)
         nbytes = _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
         if nbytes == 0:
             raise ValueError("invalid pool shape")
         data = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, int(hadamard), signs)
+        return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, int(hadamard), signs, float(k_scale),
+                   float(v_scale))
 
     def desc(self) -> _PoolDesc:
         return _PoolDesc(self.data.data_ptr(), self.num_pages, self.num_layers, self.num_kv_heads,
                          HEAD_DIM, PAGE_SIZE, self.rotary_dim, int(self.hadamard),
-                         (ctypes.c_uint32 * 4)(*self.signs))
+                         (ctypes.c_uint32 * 4)(*self.signs), self.k_scale, self.v_scale)
 
 
 def nvfp4kv_version() -> str:

@@ -345,13 +345,18 @@ __device__ __forceinline__ void append_new_token(
     const void* __restrict__ k_new, const void* __restrict__ v_new, int in_dtype,
     const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, int rotary_dim, int hadamard, const SignMask& signs,
-    const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens) {
+    const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens,
+    float2 kv_inv) {
   const int lane = (int)threadIdx.x;
   const int c16 = lane & 15;
   const int which = (lane >> 4) & 1;   // 0 = K, 1 = V
   const int seq = sg / hkv, kvh = sg % hkv;
   float x[8];
   load8(which ? v_new : k_new, in_dtype, ((size_t)seq * hkv + kvh) * kHeadDim + 8 * c16, x);
+  // the global scale divides the inputs (by the binary32 reciprocal)
+  const float inv = which ? kv_inv.y : kv_inv.x;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] *= inv;
   const int rot = which ? 0 : rotary_dim;
   const float* crow = nullptr;
   const float* srow = nullptr;
@@ -689,7 +694,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, SignMask signs, const int32_t* __restrict__ page_table, int pt_stride,
     const int32_t* __restrict__ seq_lens, float c_log2, float* __restrict__ ws_acc,
-    float2* __restrict__ ws_ml) {
+    float2* __restrict__ ws_ml, float2 kv_inv) {
   __shared__ __attribute__((aligned(16))) u4 sc_lds[2][64];
   constexpr int kQE = q_entries<PACKED>();
   __shared__ __attribute__((aligned(16))) h8 q_lds[kQSlots][NT][4][kQE];
@@ -814,7 +819,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
         append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
                          q_positions, rope_cos, rope_sin, rotary_dim, hadamard, signs, page_table,
-                         pt_stride, seq_lens);
+                         pt_stride, seq_lens, kv_inv);
         any = true;
       }
       sstart += pgl;
@@ -1174,7 +1179,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
     const int32_t* __restrict__ seq_lens, int n_seq, int hkv, QCols qc, int n_q_heads, int64_t W,
-    float* __restrict__ out) {
+    float v_scale, float* __restrict__ out) {
   const int group = qc.group;
   const int hq_idx = (int)blockIdx.x;     // column over all kv heads: kvh * group + c
   const int seq = (int)blockIdx.y;
@@ -1262,7 +1267,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     // column h of kv head kvh: head h % heads of query token qtok0 + h / heads
     const int tok = qc.qtok0 + h / qc.heads;
     out[(((size_t)seq * qc.n_qtok + tok) * n_q_heads + (size_t)kvh * qc.heads + h % qc.heads) * kHeadDim +
-        d0 + dd] = o / l;
+        d0 + dd] = o * v_scale / l;   // V's global scale: stored V values are V / v_scale
   }
 }
 
@@ -1278,7 +1283,8 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   float* ws_acc = reinterpret_cast<float*>(ws);
   float2* ws_ml = reinterpret_cast<float2*>(ws + ws_ml_offset(n_seq, P.hkv, plan));
-  const float c_log2 = sm_scale * 1.4426950408889634f;
+  // K's global scale enters every score as a factor
+  const float c_log2 = sm_scale * P.k_scale * 1.4426950408889634f;
   const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
   const bool packed = plan.group <= 8, mq = qt.n_qtok > 1;
   const int nt = decode_column_tiles(plan.group);
@@ -1289,20 +1295,20 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
   hipLaunchKernelGGL(kern, dim3(plan.n_waves), dim3(64), 0, stream, P.base, P.num_pages, P.hkv,
                      layer, n_seq, n_q_heads, qc, q, k_new, v_new, in_dtype, q_positions,
                      rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs, page_table, page_table_stride,
-                     seq_lens, c_log2, ws_acc, ws_ml);
+                     seq_lens, c_log2, ws_acc, ws_ml, make_float2(P.k_inv, P.v_inv));
   return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
-                                const QTokens& qt, hipStream_t stream) {
+                                const QTokens& qt, float v_scale, hipStream_t stream) {
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float2* ws_ml = reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) +
                                                         ws_ml_offset(n_seq, hkv, plan));
   const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
   hipLaunchKernelGGL(decode_reduce_kernel, dim3(hkv * plan.group, n_seq, kHeadDim / 32), dim3(256), 0,
                      stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
-                     (int64_t)plan.n_waves, out);
+                     (int64_t)plan.n_waves, v_scale, out);
   return hipGetLastError();
 }
 

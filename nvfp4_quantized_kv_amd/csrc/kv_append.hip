@@ -216,7 +216,7 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard, SignMask signs) {
+    int hadamard, SignMask signs, float k_inv, float v_inv) {
   const int lane = (int)__lane_id();
   const int r = lane & 15;
   const int wv = (int)(threadIdx.x >> 6);
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
   const bool had = which ? false : (hadamard != 0);
   const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
   const void* src = which ? v : k;
+  const float inv = which ? v_inv : k_inv;   // 1 / the global scale
   const int n_it = 4 * hkv;
   // token of iteration `it` (kv head it % hkv, pass it / hkv); lanes past
   // the last token take a copy of the last token's row of their kind (they
@@ -260,6 +261,8 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     __builtin_amdgcn_sched_barrier(0);
     float x[8];
     raw_to_float<DT>(rw, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] *= inv;
     uint32_t codes, scode;
     append_row16(x, r, rot > 0, rl, had, neg, codes, scode);
     if (active) {
@@ -296,7 +299,7 @@ __device__ inline void store8(void* dst, int dtype, size_t elem_off, const float
 __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
     const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_rows,
     const int64_t* __restrict__ slots, void* __restrict__ k_out, void* __restrict__ v_out,
-    int dtype, int unrotate, int hadamard, SignMask signs) {
+    int dtype, int unrotate, int hadamard, SignMask signs, float k_scale, float v_scale) {
   const int r = (int)(threadIdx.x & 15);
   const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
   const bool active = row < n_rows;
@@ -315,6 +318,10 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
   float x[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) x[k] = e2m1_value((codes >> (4 * k)) & 15u) * s;
+  // times the global scale (binary32 product of the exact block value)
+  const float gs = which ? v_scale : k_scale;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = x[k] * gs;
   if (unrotate && which == 0) {
     // H is symmetric and orthogonal: applying the transform again undoes it
     // (up to float rounding), and the randomized rotation's negations come
@@ -359,7 +366,8 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
   const int runs = (n_tok + 63) / 64;            // 64 tokens, every kv head, per workgroup
   auto kern = dtype == 1 ? kv_quant_append_kernel<1> : kv_quant_append_kernel<0>;
   hipLaunchKernelGGL(kern, dim3(runs), dim3(512), 0, stream, P.base, P.num_pages, P.hkv, layer, n_tok, k,
-                     v, slots, positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs);
+                     v, slots, positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs, P.k_inv,
+                     P.v_inv);
   return hipGetLastError();
 }
 
@@ -369,7 +377,7 @@ hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64
   const int grid = (n_rows + 15) / 16;
   hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(grid), dim3(256), 0, stream, P.base, P.num_pages,
                      P.hkv, layer, n_rows, slots, k_out, v_out, dtype, unrotate && P.hadamard, P.hadamard,
-                     P.signs);
+                     P.signs, P.k_scale, P.v_scale);
   return hipGetLastError();
 }
 

@@ -40,6 +40,9 @@ int check_pool_shape(const nvfp4kv_pool* p) {
   if (p->rotary_dim < 0 || p->rotary_dim > 128 || p->rotary_dim % 16 != 0)
     return fail(NVFP4KV_ERR_UNSUPPORTED, "rotary_dim %d unsupported (0..128, multiple of 16)", p->rotary_dim);
   if (p->hadamard < 0 || p->hadamard > 2) return fail(NVFP4KV_ERR_INVALID_ARG, "hadamard must be 0, 1 or 2 (got %d)", p->hadamard);
+  for (const float g : {p->k_scale, p->v_scale})
+    if (g != 0.0f && !(g >= 0x1p-64f && g <= 0x1p64f))
+      return fail(NVFP4KV_ERR_INVALID_ARG, "global scale %g out of range (0 = 1, else 2^-64..2^64)", (double)g);
   return NVFP4KV_OK;
 }
 
@@ -82,6 +85,10 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   L.rotary_dim = p->rotary_dim;
   L.hadamard = p->hadamard;
   for (int i = 0; i < 4; ++i) L.signs.w[i] = p->hadamard == 2 ? p->hadamard_signs[i] : 0u;
+  L.k_scale = p->k_scale == 0.0f ? 1.0f : p->k_scale;
+  L.v_scale = p->v_scale == 0.0f ? 1.0f : p->v_scale;
+  L.k_inv = 1.0f / L.k_scale;
+  L.v_inv = 1.0f / L.v_scale;
   return L;
 }
 
@@ -287,7 +294,7 @@ int nvfp4kv_decode_reduce(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_head
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
   if ((rc = check_workspace(nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan), workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
   hipError_t e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out,
-                                               workspace, plan, one_token(plan), stream);
+                                               workspace, plan, one_token(plan), launch_pool(p).v_scale, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
   return NVFP4KV_OK;
 }
@@ -314,7 +321,7 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                                                workspace, plan, one_token(plan), stream);
   if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
   e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out, workspace,
-                                    plan, one_token(plan), stream);
+                                    plan, one_token(plan), launch_pool(p).v_scale, stream);
   if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
   return NVFP4KV_OK;
 }
@@ -401,7 +408,7 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
                                                  stream);
     if (e != hipSuccess) return hip_fail(e, "decode_attn_splitk launch");
     e = nvfp4kv::launch_decode_reduce(p->num_kv_heads, n_seq, n_q_heads, seq_lens, out, workspace, pl,
-                                      qt, stream);
+                                      qt, launch_pool(p).v_scale, stream);
     if (e != hipSuccess) return hip_fail(e, "decode_reduce launch");
   }
   return NVFP4KV_OK;

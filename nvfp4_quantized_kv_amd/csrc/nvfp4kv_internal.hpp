@@ -31,6 +31,8 @@ struct LaunchPool {
   int rotary_dim;
   int hadamard;
   SignMask signs;
+  float k_scale, v_scale;   // per-tensor global scales (1 when unset)
+  float k_inv, v_inv;       // their binary32 reciprocals, applied to append inputs
 };
 
 // Split-K plan of one decode call: the number of wavefronts that share the
@@ -109,6 +111,6 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
 
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
-                                const QTokens& qt, hipStream_t stream);
+                                const QTokens& qt, float v_scale, hipStream_t stream);
 
 }  // namespace nvfp4kv

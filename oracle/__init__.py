@@ -168,13 +168,25 @@ def pool_read_row(pool, num_pages, hkv, layer, slot, kvh, which):
     return codes, scales
 
 
+def _inverse_scale(g) -> np.float32:
+    """binary32 1/g of a per-tensor global scale (0 meaning 1)."""
+    g = np.float32(1.0 if g == 0 else g)
+    return np.float32(1.0) / g
+
+
 def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, positions,
-           cos_tab=None, sin_tab=None, signs=None):
-    """Quantize and write n_tok tokens into `pool` (a writable uint8 array)."""
+           cos_tab=None, sin_tab=None, signs=None, k_scale=1.0, v_scale=1.0):
+    """Quantize and write n_tok tokens into `pool` (a writable uint8 array).
+
+    k_scale, v_scale: NVFP4's second scaling level, one FP32 factor per tensor
+    over the E4M3 block scales (NVIDIA's NVFP4 format description; the release
+    post keeps it at 1).  Reading taken: each input element is first
+    multiplied, in binary32, by the binary32 reciprocal of the scale; RoPE,
+    rotation and block quantization then run on those values unchanged."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     mode, m = _rotation(hadamard, signs)
-    k = _c(k, np.float32)
-    v = _c(v, np.float32)
+    k = _c(k, np.float32) * _inverse_scale(k_scale)
+    v = _c(v, np.float32) * _inverse_scale(v_scale)
     n_tok = k.shape[0]
     slots = _c(slots, np.int64)
     positions = _c(positions, np.int32)
@@ -185,10 +197,19 @@ def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, posit
 
 
 def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
-                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None, v_rows=None):
+                     page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None, v_rows=None,
+                     k_scale=1.0, v_scale=1.0):
     """fp64 attention for every sequence and query head over the pool's bytes.
     v_rows [T][hkv][128] (one sequence only): V values taken from it instead
-    of the pool, for the variant that keeps V unquantized."""
+    of the pool, for the variant that keeps V unquantized.
+
+    k_scale, v_scale: the pool's global scales; a cached K value is its block
+    value times k_scale, a V value its block value times v_scale.  The factors
+    are applied as sm_scale * k_scale on every score and v_scale on the
+    output, the same products regrouped (exact in real arithmetic)."""
+    gk = 1.0 if k_scale == 0 else float(k_scale)
+    gv = 1.0 if (v_scale == 0 or v_rows is not None) else float(v_scale)
+    sm_scale = float(sm_scale) * gk
     mode, m = _rotation(hadamard, signs)
     vr = None
     if v_rows is not None:
@@ -206,11 +227,12 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
                                _p(ct), _p(st), _p(page_table), page_table.shape[1],
                                _p(_c(seq_lens, np.int32)), float(sm_scale), _p(vr) if vr is not None else None,
                                _p(out))
-    return out
+    return out * gv
 
 
 def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
-                           page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None):
+                           page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None,
+                           k_scale=1.0, v_scale=1.0):
     """fp64 attention of M new query tokens per sequence over the pool's bytes,
     causal among the new tokens: the decode step of speculative verification
     (ai-manual.ru article on "Ninfer 4080", section "Key features": the draft
@@ -231,7 +253,7 @@ def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q,
     out = decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard,
                            q.reshape(n_seq * m, q.shape[2], HEAD_DIM),
                            np.asarray(q_pos, np.int32).reshape(-1), rows, pref, sm_scale,
-                           cos_tab, sin_tab, signs)
+                           cos_tab, sin_tab, signs, k_scale=k_scale, v_scale=v_scale)
     return out.reshape(n_seq, m, q.shape[2], HEAD_DIM)
 
 

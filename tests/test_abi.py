@@ -232,3 +232,15 @@ def test_stream_read_rejects_bad_arguments(kv):
     assert f(ctypes.byref(d), 0, 2, 4096, 16, 4096, 64, None, None) == -1
     assert f(ctypes.byref(d), 0, 2, 4096, 0, 4096, 64, 4096, None) == -1      # stride
     assert f(ctypes.byref(d), 99, 2, 4096, 16, 4096, 64, 4096, None) == -1     # layer
+
+
+def test_global_scale_out_of_range_is_refused():
+    """The pool's per-tensor global scales: 0 (meaning 1) or 2^-64..2^64; the
+    descriptor check of every call refuses others (the workspace query returns 0)."""
+    import ctypes
+    import math
+    import nvfp4_quantized_kv_amd as kv
+    for ks, vs, ok in ((0.0, 0.0, True), (3.7, 0.25, True), (-1.0, 1.0, False), (1.0, math.inf, False),
+                       (math.nan, 1.0, False), (1.0, 2.0 ** -70, False)):
+        d = kv._PoolDesc(None, 4, 1, 2, 128, 64, 32, 1, (ctypes.c_uint32 * 4)(0, 0, 0, 0), ks, vs)
+        assert (kv._lib.nvfp4kv_decode_workspace_bytes(ctypes.byref(d), 1, 4, 1000, 0) > 0) == ok, (ks, vs)

@@ -36,12 +36,13 @@ class Case:
 
     def __init__(self, seed, lens, hkv, hq, rotary=32, hadamard=True, pos_scale=1.0,
                  dtype=torch.bfloat16, outliers=3, outlier_scale=16.0, extra_pages=3,
-                 student_t=False, hold_last=False):
+                 student_t=False, hold_last=False, k_scale=1.0, v_scale=1.0):
         import nvfp4_quantized_kv_amd as kv
         self.kv = kv
         rng = np.random.default_rng(seed)
         self.lens = list(lens)
         self.hkv, self.hq, self.rotary, self.hadamard = hkv, hq, rotary, int(hadamard)
+        self.k_scale, self.v_scale = k_scale, v_scale
         # hadamard 2: the randomized rotation's element mask, drawn here
         self.signs = (rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
                       if self.hadamard == 2 else None)
@@ -67,7 +68,8 @@ class Case:
 
         self.max_pos = max(lens) + 1
         self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard,
-                                     signs=tuple(self.signs) if self.signs is not None else (0, 0, 0, 0))
+                                     signs=tuple(self.signs) if self.signs is not None else (0, 0, 0, 0),
+                                     k_scale=k_scale, v_scale=v_scale)
         self.pool.data.fill_(0x7F)  # stale bytes decode to NaN if ever read unmasked
         self.rc = self.rs = self.oc = self.os = None
         if rotary:
@@ -113,7 +115,8 @@ class Case:
         pool = self.pool.data.cpu().numpy()
         return oracle.decode_attention(pool, self.num_pages, self.hkv, 0, self.rotary, self.hadamard,
                                        self.q.float().numpy(), self.q_pos, self.table, self.lens,
-                                       sm_scale, self.oc, self.os, signs=self.signs)
+                                       sm_scale, self.oc, self.os, signs=self.signs, k_scale=self.k_scale,
+                                       v_scale=self.v_scale)
 
 
 def test_decode_tiny_workload():
