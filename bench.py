@@ -113,6 +113,27 @@ def traffic_from_profiles(kernel_tag: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, as lscpu reports it (/proc/cpuinfo if lscpu
+    is missing)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(step, wl, torch):
     """Time the CPU oracle on a bounded sample of the same step: layer 0 of
     the workload, i.e. the append of every sequence's new token and decode
@@ -121,7 +142,7 @@ def cpu_baseline(step, wl, torch):
     import oracle
     from nvfp4_quantized_kv_amd import workloads as W
 
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    cores = oracle.set_threads(int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0)))))
     torch.cuda.synchronize()
     layer_bytes = step.pool.data.numel() // wl.layers
     pool0 = step.pool.data[:layer_bytes].cpu().numpy()       # layer 0 blocks (the layer is first)
@@ -144,7 +165,7 @@ def cpu_baseline(step, wl, torch):
     torch.cuda.synchronize()
     err = float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max())
     return {
-        "value": nbytes / sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "value": nbytes / sec / 1e9, "unit": "GB/s", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
         "sample": f"layer 0 of {wl.layers}: append of {wl.n_seq} new tokens + fp64 decode attention "
                   f"for {wl.n_seq} sequences x {wl.hq} query heads over {sum(wl.seq_lens)} tokens "
                   f"({sec:.1f} s)",

@@ -94,8 +94,10 @@ typedef struct {
     float v_scale;          /* the same for V */
 } nvfp4kv_pool;
 
-/* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144.
- * Returns 0 if `p` is null or its sizes are invalid. */
+/* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144,
+ * i.e. 144 bytes per token per kv head (release post, NVFP4 section, the
+ * "Result" line: 2 x (64 code bytes + 8 E4M3 scale bytes) for a 128-element
+ * head).  Host only.  Returns 0 if `p` is null or its sizes are invalid. */
 size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p);
 
 /* RoPE table on the HOST (section "YaRN context extension"): for position
@@ -125,10 +127,14 @@ int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok,
                    const float* rope_cos, const float* rope_sin, int32_t max_pos,
                    hipStream_t stream);
 
-/* Workspace bytes nvfp4kv_decode_attn needs for this shape (split-K
- * partials).  pages_per_split 0 selects the library's own split plan; the
- * same value must be passed to nvfp4kv_decode_attn.  Returns 0 on invalid
- * arguments. */
+/* Workspace bytes nvfp4kv_decode_attn needs for this shape: the split
+ * partials of the decode attention of the NVFP4 section's bullets 1-3 (the
+ * release post does not describe how its decode kernel splits the work; the
+ * split and its partials are this library's).  Host only; the caller
+ * allocates the workspace.  pages_per_split 0 selects the library's own
+ * split plan; the same value must be passed to nvfp4kv_decode_attn.
+ * Returns 0 on invalid arguments (the reason is left for
+ * nvfp4kv_last_error). */
 size_t nvfp4kv_decode_workspace_bytes(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads,
                                       int64_t max_seq_len, int32_t pages_per_split);
 
@@ -178,16 +184,24 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
  * segment g = seq * num_kv_heads + kvh, segments in order, each segment
  * followed by 5 units of no work, form one flat list of TU units; the plan's
  * W ranges [w*TU/W, (w+1)*TU/W) split it, and every (segment, range) pair
- * whose pages overlap yields one partial in slot g + w: per query head h of the group, a reference m (log2 units of
- * sm_scale * score), the weight sum l and the weighted V sum acc[128], with
- * weights 2^(s - m + 8) for the pair's tokens.  Layout, each part starting
- * at a 256-byte boundary: acc at float offset (slot * group + h) * 128 for
- * slots 0 .. n_seq*num_kv_heads + W - 1; the pairs (m, l) at float2 index
- * slot * group + h.
- * Slots of pairs that do not overlap are not written.
- * nvfp4kv_decode_reduce reads them and writes out = sum_s 2^(m_s - M) acc_s
- * / sum_s 2^(m_s - M) l_s per (sequence, query head).  Both must get the
- * same n_seq, n_q_heads, max_seq_len and pages_per_split. */
+ * whose pages overlap yields one partial in slot g + w.  Per query head h of
+ * the group a partial holds:
+ *   m       a reference in log2 units: scores enter as
+ *           s = sm_scale * k_scale * log2(e) * (Q-hat . K-hat), with K-hat
+ *           the stored (block-scaled) K values, so K's global scale is
+ *           inside m;
+ *   l       the weight sum, sum_t 2^(s_t - m + 8) over the pair's tokens;
+ *   acc     sum_t 2^(s_t - m + 8) V-hat_t with V-hat the STORED V values,
+ *           i.e. V / v_scale (V's global scale is not applied here).
+ * Layout, each part starting at a 256-byte boundary: acc at float offset
+ * (slot * group + h) * 128 for slots 0 .. n_seq*num_kv_heads + W - 1; the
+ * pairs (m, l) at float2 index slot * group + h.  Slots of pairs that do not
+ * overlap are not written.
+ * nvfp4kv_decode_reduce reads them and writes, per (sequence, query head),
+ *   out = v_scale * sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
+ * (M = max_s m_s; v_scale of the pool, 1 when unset): a caller combining
+ * partials itself multiplies by v_scale too.  Both must get the same n_seq,
+ * n_q_heads, max_seq_len and pages_per_split. */
 int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq,
                                int32_t n_q_heads, const void* q, const void* k_new,
                                const void* v_new, nvfp4kv_dtype q_dtype,
@@ -237,10 +251,12 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
                               int64_t max_seq_len, float sm_scale, float* out, void* workspace,
                               size_t workspace_bytes, int32_t pages_per_split, hipStream_t stream);
 
-/* Dequantize cached rows (element = E2M1 value * E4M3 scale, exact in f32 and
- * bf16).  K comes back in the rotated domain unless `unrotate` is 1, which
- * applies the Hadamard transform once more (it is its own inverse; the
- * result then carries float rounding).
+/* Dequantize cached rows (release post, NVFP4 section, bullet 1: the V
+ * operand of PV is the dequantized cache; element = E2M1 value * E4M3 block
+ * scale, exact in f32 and bf16, times the pool's global scale).  K comes
+ * back in the rotated domain (bullet 2) unless `unrotate` is 1, which applies
+ * the Hadamard transform once more (it is its own inverse; the result then
+ * carries float rounding).  A validation and export aid.
  *   slots       [n_tok] int64
  *   k_out/v_out [n_tok][num_kv_heads][128] of out_dtype; either may be null */
 int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const int64_t* slots,
@@ -296,7 +312,11 @@ int nvfp4kv_stream_read(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, con
                         hipStream_t stream);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until
- * the next call on the same thread. */
+ * the next call on the same thread.  Not a step of the method: every entry
+ * point reports failure as a status code and this message instead of
+ * throwing (the release post's section "Also included" lists recovery from
+ * allocation failures in its engine; here no exception ever crosses the C
+ * interface). */
 const char* nvfp4kv_last_error(void);
 
 /* Library version string, e.g. "nvfp4kv 0.1.0 gfx950". */

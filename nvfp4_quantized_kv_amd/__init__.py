@@ -120,6 +120,16 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _scratch(t: torch.Tensor, stream) -> torch.Tensor:
+    """A tensor this binding allocated (on torch's current stream) that the
+    library's kernels use on `stream`: if that is another stream, the
+    caching allocator is told, so the block is not handed to a later
+    allocation before the work queued on `stream` has finished with it."""
+    if stream is not None and stream.cuda_stream != torch.cuda.current_stream(t.device).cuda_stream:
+        t.record_stream(stream)
+    return t
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return F32
@@ -233,10 +243,10 @@ def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: to
     assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     n_seq, n_q_heads, _ = q.shape
     if out is None:
-        out = torch.empty((n_seq, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _scratch(torch.empty((n_seq, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device), stream)
     need = nvfp4kv_decode_workspace_bytes(pool, n_seq, n_q_heads, max_seq_len, pages_per_split)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(torch.empty(max(need, 256), dtype=torch.uint8, device=q.device), stream)
     max_pos = rope_cos.shape[0] if rope_cos is not None else 0
     d = pool.desc()
     _check("nvfp4kv_decode_attn",
@@ -307,11 +317,12 @@ def nvfp4kv_decode_attn_multi(pool: Pool, layer: int, q: torch.Tensor, q_positio
     assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     n_seq, n_qtok, n_q_heads, _ = q.shape
     if out is None:
-        out = torch.empty((n_seq, n_qtok, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+        out = _scratch(torch.empty((n_seq, n_qtok, n_q_heads, HEAD_DIM), dtype=torch.float32, device=q.device),
+                       stream)
     if workspace is None:
         need = nvfp4kv_decode_multi_workspace_bytes(pool, n_seq, n_qtok, n_q_heads, max_seq_len,
                                                     pages_per_split)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(torch.empty(max(need, 256), dtype=torch.uint8, device=q.device), stream)
     max_pos = rope_cos.shape[0] if rope_cos is not None else 0
     d = pool.desc()
     _check("nvfp4kv_decode_attn_multi",
@@ -330,8 +341,8 @@ def nvfp4kv_dequant(pool: Pool, layer: int, slots: torch.Tensor, out_dtype=torch
     assert slots.dtype == torch.int64 and slots.is_contiguous()
     n_tok = slots.shape[0]
     shape = (n_tok, pool.num_kv_heads, HEAD_DIM)
-    k_out = torch.empty(shape, dtype=out_dtype, device=slots.device) if want_k else None
-    v_out = torch.empty(shape, dtype=out_dtype, device=slots.device) if want_v else None
+    k_out = _scratch(torch.empty(shape, dtype=out_dtype, device=slots.device), stream) if want_k else None
+    v_out = _scratch(torch.empty(shape, dtype=out_dtype, device=slots.device), stream) if want_v else None
     code = F32 if out_dtype == torch.float32 else BF16
     d = pool.desc()
     _check("nvfp4kv_dequant",
@@ -371,7 +382,7 @@ def nvfp4kv_stream_read(pool: Pool, layer: int, page_table: torch.Tensor, seq_le
     assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
     assert seq_lens.dtype == torch.int32 and seq_lens.is_contiguous()
     if words is None:
-        words = torch.empty(n_waves, dtype=torch.int32, device=page_table.device)
+        words = _scratch(torch.empty(n_waves, dtype=torch.int32, device=page_table.device), stream)
     d = pool.desc()
     _check("nvfp4kv_stream_read",
            _lib.nvfp4kv_stream_read(ctypes.byref(d), int(layer), seq_lens.numel(), _ptr(page_table),

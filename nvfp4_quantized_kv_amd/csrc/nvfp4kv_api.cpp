@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 
 #include "nvfp4kv_internal.hpp"
@@ -94,18 +95,20 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
 
 // Resident wavefronts of the decode kernels with `nt` column tiles (for one
 // tile, packed groups or not) on the current device: CUs times one-wavefront
-// workgroups per CU.  Cached per device; if the device cannot be queried (no
-// GPU), 256 CUs x 8 (one tile) or 4 (several tiles) is assumed so that size
-// queries still work.
+// workgroups per CU.  Cached per device (any thread may fill an entry; every
+// thread computes the same value, so relaxed atomics suffice); if the device
+// cannot be queried (no GPU), 256 CUs x 8 (one tile) or 4 (several tiles) is
+// assumed so that size queries still work.
 int resident_decode_waves(int nt, bool packed) {
-  static int cached[64][4][2] = {};
+  static std::atomic<int> cached[64][4][2];
   const int fallback = nt > 1 ? 256 * 4 : 256 * 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return fallback;
   }
-  int& c = cached[dev][nt][packed ? 1 : 0];
+  std::atomic<int>& slot = cached[dev][nt][packed ? 1 : 0];
+  int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0;
     const int per_cu = nvfp4kv::decode_waves_per_cu(nt, packed);
@@ -115,6 +118,7 @@ int resident_decode_waves(int nt, bool packed) {
       return fallback;
     }
     c = cus * per_cu;
+    slot.store(c, std::memory_order_relaxed);
   }
   return c;
 }

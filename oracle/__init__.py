@@ -46,6 +46,8 @@ def lib():
         L = ctypes.CDLL(LIB)
         P = ctypes.c_void_p
         i32, i64, f64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_float
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_max_threads.restype = ctypes.c_int
         L.orc_e4m3_value.argtypes = [ctypes.c_int]
         L.orc_e4m3_value.restype = f64
         L.orc_e4m3_scale_code.argtypes = [f32]
@@ -80,6 +82,12 @@ def _p(a: np.ndarray):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def set_threads(n: int) -> int:
+    """Threads of the oracle's OpenMP loops; returns the count now in use."""
+    lib().orc_set_threads(int(n))
+    return lib().orc_max_threads()
 
 
 # -- scalar codecs -----------------------------------------------------------

@@ -34,6 +34,7 @@
  * invariants.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -43,6 +44,15 @@
 #define ORC_NBLK 8        /* blocks per row */
 #define ORC_PAGE 64       /* tokens per page */
 #define ORC_ROW_CODE 64   /* code bytes per row (128 x 4 bit) */
+
+/* Threads of the OpenMP loops below (timing only; results do not depend on
+ * the thread count). */
+void orc_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
+int orc_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* E4M3 (OCP 8-bit float, "FN" variant): 1 sign, 4 exponent (bias 7), 3
