@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="three_long")
     ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="run only this many layers of the workload (0 = all); every layer's decode "
+                         "launch is the same kernel on the same shape, so profiling runs use 1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the HBM copy-ceiling measurement")
     ap.add_argument("--quality", action="store_true",
@@ -192,6 +195,8 @@ def main():
     if args.quality:
         return bench_quality(args, torch, kv, W, DecodeStep)
     wl = W.config(args.workload)
+    if args.layers:
+        wl.layers = min(args.layers, wl.layers)
     log(f"workload {wl.name}: {wl.n_seq} seqs {wl.cached} cached, {wl.layers} layers, "
         f"hq {wl.hq} hkv {wl.hkv}, {kv.nvfp4kv_version()}")
     ceiling = None if args.no_ceiling else copy_ceiling_gbps(torch)

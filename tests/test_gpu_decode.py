@@ -70,7 +70,11 @@ class Case:
         self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard,
                                      signs=tuple(self.signs) if self.signs is not None else (0, 0, 0, 0),
                                      k_scale=k_scale, v_scale=v_scale)
-        self.pool.data.fill_(0x7F)  # stale bytes decode to NaN if ever read unmasked
+        # stale bytes: 0x7F in every byte never written.  The decode kernels
+        # clear scale sign bits, so these read as finite values (scale 1.875,
+        # codes +-6): a masking mistake shows as an error, not as NaN
+        # (test_gpu_contracts.py pins the masking exactly)
+        self.pool.data.fill_(0x7F)
         self.rc = self.rs = self.oc = self.os = None
         if rotary:
             c, s = kv.nvfp4kv_rope_table(1e7, rotary, pos_scale, self.max_pos)
@@ -221,15 +225,30 @@ FUSED_CASES = [
 ]
 
 
+def oracle_pool(c):
+    """The pool bytes the oracle writes for every token of a Case (each
+    sequence's tokens 0 .. T-1), on the Case's 0x7F background."""
+    pool = np.full(c.pool.data.numel(), 0x7F, np.uint8)
+    for n, T in enumerate(c.lens):
+        pos = np.arange(T)
+        sl = c.table[n, pos // 64].astype(np.int64) * 64 + pos % 64
+        oracle.append(pool, c.num_pages, c.hkv, c.rotary, c.hadamard, 0, c.k[n].float().numpy(),
+                      c.v[n].float().numpy(), sl, pos.astype(np.int32), c.oc, c.os, signs=c.signs,
+                      k_scale=c.k_scale, v_scale=c.v_scale)
+    return pool
+
+
 @pytest.mark.parametrize("idx", range(len(FUSED_CASES)))
 @pytest.mark.parametrize("pages_per_split", [0, 1, 4096])
 def test_decode_quantizes_current_token_in_place(idx, pages_per_split):
-    """Decode with k_new/v_new on a cache missing the current token == append
-    of the token + decode: the pool bytes bit for bit (the whole pool, so no
-    other slot is touched) and the attention output exactly; both within the
-    oracle's tolerance.  pages_per_split 1 puts a token's page first in a
-    wavefront's range, 4096 gives one wavefront many segments (appends and
-    query switches past the preloaded slots)."""
+    """Decode with k_new/v_new on a cache missing the current token: the
+    whole pool afterwards equals the oracle's append of every token (so the
+    new token's bytes are the oracle's and no other slot is touched), and
+    equals append + decode on the GPU; the attention output equals that of
+    append + decode exactly and is within the oracle's tolerance.
+    pages_per_split 1 puts a token's page first in a wavefront's range, 4096
+    gives one wavefront many segments (appends and query switches past the
+    preloaded slots)."""
     kw = dict(FUSED_CASES[idx])
     lens = kw.pop("lens")
     hq = kw.pop("hq", 8)
@@ -237,6 +256,7 @@ def test_decode_quantizes_current_token_in_place(idx, pages_per_split):
     held = Case(300 + idx, lens, 2, hq, hold_last=True, **kw)
     out_full = full.gpu(pages_per_split=pages_per_split)
     out_fused = held.gpu(pages_per_split=pages_per_split, fused=True)
+    assert np.array_equal(held.pool.data.cpu().numpy(), oracle_pool(held)), "pool bytes differ from the oracle"
     assert torch.equal(held.pool.data, full.pool.data), "pool bytes differ from append + decode"
     assert np.array_equal(out_fused, out_full), "output differs from append + decode"
     assert_attention_close(out_fused, held.oracle(), f"fused {lens}")
@@ -251,6 +271,7 @@ def test_decode_quantizes_current_token_many_segments_one_wave():
     held = Case(400, lens, 4, 8, hold_last=True)
     out_full = full.gpu(pages_per_split=4096)
     out_fused = held.gpu(pages_per_split=4096, fused=True)
+    assert np.array_equal(held.pool.data.cpu().numpy(), oracle_pool(held))
     assert torch.equal(held.pool.data, full.pool.data)
     assert np.array_equal(out_fused, out_full)
     assert_attention_close(out_fused, held.oracle(), "many segments")

@@ -80,12 +80,17 @@ def _check_attention(wl, st, layer, seq, out, oc, os_):
 
 
 def test_three_long_sequences_full_size():
+    """The path the benchmark times: the cache holds tokens 0 .. T-2 of every
+    sequence, and the decode launch (automatic split plan, the benchmark's
+    workspace) quantizes token T-1 into the cache itself; its bytes and
+    sampled cached rows must equal the oracle's quantization, the attention
+    the oracle's on the resulting pool."""
     wl, st = _step("three_long")
     oc, os_ = _oracle_tables(wl, st)
     rng = np.random.default_rng(0)
     for layer in (0, wl.layers - 1):
-        st.append(layer)
-        out = st.decode(layer).cpu().numpy()
+        st.decode_splits(layer, fused=True)
+        out = st.decode_reduce(layer).cpu().numpy()
         for seq in range(wl.n_seq):
             pos = np.concatenate([rng.integers(0, wl.cached[seq], 6), [wl.cached[seq]]])
             _check_rows(wl, st, layer, seq, pos, oc, os_)
@@ -127,8 +132,7 @@ def test_single_600k_sequence_full_size(name):
     oc, os_ = _oracle_tables(wl, st)
     rng = np.random.default_rng(1)
     layer = 1
-    st.append(layer)
-    out = st.decode(layer).cpu().numpy()
+    out = st.decode(layer, fused=True).cpu().numpy()     # the new token quantized by the decode launch
     _check_rows(wl, st, layer, 0, np.concatenate([rng.integers(0, wl.cached[0], 6), [wl.cached[0]]]), oc, os_)
     _check_attention(wl, st, layer, 0, out, oc, os_)
     del st
