@@ -177,6 +177,26 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                         float* out, void* workspace, size_t workspace_bytes,
                         int32_t pages_per_split, hipStream_t stream);
 
+/* nvfp4kv_decode_attn without a workspace argument and without allocating
+ * anything: for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The split partials go to the library's own workspace, a device array of
+ * NVFP4KV_STATIC_WORKSPACE_BYTES that every GPU the library runs on holds
+ * until the process ends.  Arguments, outputs and results are those of
+ * nvfp4kv_decode_attn with the same pages_per_split.  A call whose workspace
+ * (nvfp4kv_decode_workspace_bytes) would exceed the array returns
+ * NVFP4KV_ERR_WORKSPACE before anything is queued.  The array keeps the last
+ * call's contents (nothing in it needs clearing); calls that overlap on one
+ * GPU (queued on different streams without ordering) race on it. */
+#define NVFP4KV_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int nvfp4kv_decode_attn_static(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
+                               const void* q, const void* k_new, const void* v_new,
+                               nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                               const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                               const int32_t* page_table, int32_t page_table_stride,
+                               const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, float* out,
+                               int32_t pages_per_split, hipStream_t stream);
+
 /* The two stages of nvfp4kv_decode_attn, for callers that combine split
  * partials themselves (for example across devices) or time the stages apart.
  * nvfp4kv_decode_attn_splits takes the arguments of nvfp4kv_decode_attn

@@ -63,6 +63,9 @@ def _load():
     L.nvfp4kv_decode_attn.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32, P, i32,
                                       P, i64, ctypes.c_float, P, P, sz, i32, P]
     L.nvfp4kv_decode_attn.restype = ctypes.c_int
+    L.nvfp4kv_decode_attn_static.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32, P, i32,
+                                             P, i64, ctypes.c_float, P, i32, P]
+    L.nvfp4kv_decode_attn_static.restype = ctypes.c_int
     L.nvfp4kv_decode_attn_splits.argtypes = [PD, i32, i32, i32, P, P, P, ctypes.c_int, P, P, P, i32,
                                              P, i32, P, i64, ctypes.c_float, P, sz, i32, P]
     L.nvfp4kv_decode_attn_splits.restype = ctypes.c_int
@@ -93,7 +96,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
-            "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_splits",
+            "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_static",
+            "nvfp4kv_decode_attn_splits",
             "nvfp4kv_decode_reduce", "nvfp4kv_decode_multi_workspace_bytes", "nvfp4kv_decode_attn_multi",
             "nvfp4kv_dequant", "nvfp4kv_page_bytes", "nvfp4kv_spill_pages", "nvfp4kv_restore_pages",
             "nvfp4kv_stream_read", "nvfp4kv_last_error", "nvfp4kv_version"]
@@ -257,6 +261,34 @@ def nvfp4kv_decode_attn(pool: Pool, layer: int, q: torch.Tensor, q_positions: to
                                     int(max_seq_len), float(sm_scale), _ptr(out), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), pages_per_split,
                                     _stream(stream)))
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 32 << 20
+
+
+def nvfp4kv_decode_attn_static(pool: Pool, layer: int, q: torch.Tensor, q_positions: torch.Tensor | None,
+                               page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                               sm_scale: float, out: torch.Tensor, rope_cos: torch.Tensor | None = None,
+                               rope_sin: torch.Tensor | None = None, pages_per_split: int = 0,
+                               k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None,
+                               stream=None) -> torch.Tensor:
+    """nvfp4kv_decode_attn on the library's own static workspace: nothing is
+    allocated, so `out` [n_seq][Hq][128] float32 must be given."""
+    assert q.is_contiguous() and page_table.is_contiguous() and seq_lens.is_contiguous()
+    _check_new(q, k_new, v_new)
+    assert page_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert out is not None and out.dtype == torch.float32 and out.is_contiguous()
+    n_seq, n_q_heads, _ = q.shape
+    assert tuple(out.shape) == (n_seq, n_q_heads, HEAD_DIM)
+    max_pos = rope_cos.shape[0] if rope_cos is not None else 0
+    d = pool.desc()
+    _check("nvfp4kv_decode_attn_static",
+           _lib.nvfp4kv_decode_attn_static(ctypes.byref(d), layer, n_seq, n_q_heads, _ptr(q), _ptr(k_new),
+                                           _ptr(v_new), _dtype_code(q), _ptr(q_positions), _ptr(rope_cos),
+                                           _ptr(rope_sin), max_pos, _ptr(page_table), page_table.shape[1],
+                                           _ptr(seq_lens), int(max_seq_len), float(sm_scale), _ptr(out),
+                                           pages_per_split, _stream(stream)))
     return out
 
 

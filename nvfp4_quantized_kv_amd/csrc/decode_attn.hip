@@ -37,6 +37,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
 
@@ -1310,6 +1312,32 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
                      stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
                      (int64_t)plan.n_waves, v_scale, out);
   return hipGetLastError();
+}
+
+// Workspace of the allocation-free decode entry point: every call on a GPU
+// uses that GPU's copy, which keeps the last call's contents (the decode
+// kernels need none of it cleared: the reduce reads only slots written by the
+// same call).  Calls that overlap on one GPU race on it.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // with `dev` current: the address of this device's copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 int decode_waves_per_cu(int nt, bool packed) {

@@ -330,6 +330,32 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   return NVFP4KV_OK;
 }
 
+int nvfp4kv_decode_attn_static(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int32_t n_q_heads,
+                               const void* q, const void* k_new, const void* v_new,
+                               nvfp4kv_dtype q_dtype, const int32_t* q_positions,
+                               const float* rope_cos, const float* rope_sin, int32_t max_pos,
+                               const int32_t* page_table, int32_t page_table_stride,
+                               const int32_t* seq_lens, int64_t max_seq_len, float sm_scale, float* out,
+                               int32_t pages_per_split, hipStream_t stream) {
+  g_last_error.clear();
+  int rc;
+  if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  nvfp4kv::DecodePlan plan;
+  if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, &plan)) != NVFP4KV_OK) return rc;
+  const size_t need = nvfp4kv::ws_bytes(n_seq, p->num_kv_heads, plan);
+  if (need > nvfp4kv::kStaticWorkspaceBytes)
+    return fail(NVFP4KV_ERR_WORKSPACE,
+                "this decode needs %zu workspace bytes, more than the %zu of the static workspace "
+                "(use nvfp4kv_decode_attn with a caller-allocated workspace)",
+                need, nvfp4kv::kStaticWorkspaceBytes);
+  void* ws = nullptr;
+  hipError_t e = nvfp4kv::static_workspace(&ws);
+  if (e != hipSuccess) return hip_fail(e, "static workspace address");
+  return nvfp4kv_decode_attn(p, layer, n_seq, n_q_heads, q, k_new, v_new, q_dtype, q_positions, rope_cos,
+                             rope_sin, max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
+                             out, ws, nvfp4kv::kStaticWorkspaceBytes, pages_per_split, stream);
+}
+
 // Shape checks of a multi-token decode; `cols` = query columns per launch.
 static int check_multi_shape(const nvfp4kv_pool* p, int32_t n_qtok, int32_t n_q_heads, int* cols,
                              int* per_launch) {

@@ -113,4 +113,11 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
                                 float* out, const void* workspace, const DecodePlan& plan,
                                 const QTokens& qt, float v_scale, hipStream_t stream);
 
+// The library's own decode workspace for callers that cannot allocate: a
+// file-scope device array of kStaticWorkspaceBytes per GPU.  Returns its
+// device address on the current device, looked up once per device (the
+// array's name is a host-side stand-in, never a device address).
+constexpr size_t kStaticWorkspaceBytes = (size_t)32 << 20;
+hipError_t static_workspace(void** ptr);
+
 }  // namespace nvfp4kv
