@@ -23,7 +23,12 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 HEAD_DIM = 128
 PAGE = 64
-BLOCK_BYTES = 9216
+BLOCK_BYTES = 9216          # NVFP4 K and V: 144 bytes per token per kv head
+BLOCK_BYTES_F16V = 20992    # NVFP4 K, fp16 V: 328 bytes per token per kv head
+
+
+def block_bytes(v_format: int = 0) -> int:
+    return BLOCK_BYTES_F16V if v_format else BLOCK_BYTES
 
 
 def build() -> str:
@@ -61,15 +66,21 @@ def lib():
         L.orc_hadamard128.argtypes = [P]
         L.orc_quant_row.argtypes = [P, ctypes.c_int, P, P, ctypes.c_int, P, P, P]
         L.orc_dequant_row.argtypes = [P, P, P]
-        L.orc_pool_bytes.argtypes = [ctypes.c_int, i64, ctypes.c_int]
+        L.orc_f32_to_f16.argtypes = [f32]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f16_value.argtypes = [ctypes.c_uint16]
+        L.orc_f16_value.restype = f64
+        L.orc_f32_to_f16_array.argtypes = [P, i64, P]
+        L.orc_pool_bytes.argtypes = [ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
         L.orc_pool_bytes.restype = ctypes.c_size_t
         L.orc_pool_read_row.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int,
-                                        ctypes.c_int, P, P]
+                                        ctypes.c_int, ctypes.c_int, P, P]
+        L.orc_pool_read_v16.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, i64, ctypes.c_int, P]
         L.orc_append.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, ctypes.c_int,
-                                 ctypes.c_int, P, P, P, P, P, P]
+                                 ctypes.c_int, P, P, P, P, P, P, ctypes.c_int]
         L.orc_decode_attention.argtypes = [P, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, P, P, P,
-                                           P, ctypes.c_int, P, f64, P, P]
+                                           P, ctypes.c_int, P, f64, P, ctypes.c_int, P]
         L.orc_reference_attention.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, P, i32, P, P, P, P, P, f64, P]
         _lib = L
@@ -163,17 +174,41 @@ def dequant_row(codes, scales) -> np.ndarray:
     return out
 
 
+# -- fp16 (the V storage of the upstream variant) ---------------------------
+def f16_bits(x) -> np.ndarray:
+    """binary16 bits of float32 values, nearest with ties to even."""
+    x = _c(x, np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    lib().orc_f32_to_f16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def f16_value(bits: int) -> float:
+    return lib().orc_f16_value(int(bits))
+
+
 # -- pool --------------------------------------------------------------------
-def pool_bytes(num_layers: int, num_pages: int, num_kv_heads: int) -> int:
-    return lib().orc_pool_bytes(num_layers, num_pages, num_kv_heads)
+def pool_bytes(num_layers: int, num_pages: int, num_kv_heads: int, v_format: int = 0) -> int:
+    return lib().orc_pool_bytes(num_layers, num_pages, num_kv_heads, int(v_format))
 
 
-def pool_read_row(pool, num_pages, hkv, layer, slot, kvh, which):
+def pool_read_row(pool, num_pages, hkv, layer, slot, kvh, which, v_format=0):
+    """Codes and scales of one cached NVFP4 row (which 0 = K, 1 = V; V only
+    in a v_format 0 pool)."""
+    if which and v_format:
+        raise ValueError("an fp16-V pool holds no V codes (pool_read_v16)")
     codes = np.zeros(64, np.uint8)
     scales = np.zeros(8, np.uint8)
-    lib().orc_pool_read_row(_p(pool), num_pages, hkv, layer, int(slot), kvh, which,
+    lib().orc_pool_read_row(_p(pool), num_pages, hkv, layer, int(slot), kvh, which, int(v_format),
                             _p(codes), _p(scales))
     return codes, scales
+
+
+def pool_read_v16(pool, num_pages, hkv, layer, slot, kvh) -> np.ndarray:
+    """The 128 fp16 V values (bits, uint16) of one cached row of an fp16-V pool."""
+    out = np.zeros(HEAD_DIM, np.uint16)
+    lib().orc_pool_read_v16(_p(pool), num_pages, hkv, layer, int(slot), kvh, _p(out))
+    return out
 
 
 def _inverse_scale(g) -> np.float32:
@@ -183,14 +218,18 @@ def _inverse_scale(g) -> np.float32:
 
 
 def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, positions,
-           cos_tab=None, sin_tab=None, signs=None, k_scale=1.0, v_scale=1.0):
+           cos_tab=None, sin_tab=None, signs=None, k_scale=1.0, v_scale=1.0, v_format=0):
     """Quantize and write n_tok tokens into `pool` (a writable uint8 array).
 
     k_scale, v_scale: NVFP4's second scaling level, one FP32 factor per tensor
     over the E4M3 block scales (NVIDIA's NVFP4 format description; the release
     post keeps it at 1).  Reading taken: each input element is first
     multiplied, in binary32, by the binary32 reciprocal of the scale; RoPE,
-    rotation and block quantization then run on those values unchanged."""
+    rotation and block quantization then run on those values unchanged.
+
+    v_format 1 keeps V in fp16 (the upstream storage the release post names,
+    NVFP4 section, bullet 2): each V element, after the multiplication by
+    1/v_scale, is rounded to binary16 (nearest, ties to even)."""
     assert pool.dtype == np.uint8 and pool.flags.c_contiguous
     mode, m = _rotation(hadamard, signs)
     k = _c(k, np.float32) * _inverse_scale(k_scale)
@@ -201,12 +240,12 @@ def append(pool, num_pages, hkv, rotary_dim, hadamard, layer, k, v, slots, posit
     ct = _c(cos_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
     st = _c(sin_tab, np.float32) if rotary_dim else np.zeros(1, np.float32)
     lib().orc_append(_p(pool), num_pages, hkv, rotary_dim, mode, _p(m) if m is not None else None, layer, n_tok,
-                     _p(k), _p(v), _p(slots), _p(positions), _p(ct), _p(st))
+                     _p(k), _p(v), _p(slots), _p(positions), _p(ct), _p(st), int(v_format))
 
 
 def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
                      page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None, v_rows=None,
-                     k_scale=1.0, v_scale=1.0):
+                     k_scale=1.0, v_scale=1.0, v_format=0):
     """fp64 attention for every sequence and query head over the pool's bytes.
     v_rows [T][hkv][128] (one sequence only): V values taken from it instead
     of the pool, for the variant that keeps V unquantized.
@@ -214,7 +253,10 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
     k_scale, v_scale: the pool's global scales; a cached K value is its block
     value times k_scale, a V value its block value times v_scale.  The factors
     are applied as sm_scale * k_scale on every score and v_scale on the
-    output, the same products regrouped (exact in real arithmetic)."""
+    output, the same products regrouped (exact in real arithmetic).
+
+    v_format 1: the pool keeps V in fp16; a cached V value is its fp16
+    value times v_scale."""
     gk = 1.0 if k_scale == 0 else float(k_scale)
     gv = 1.0 if (v_scale == 0 or v_rows is not None) else float(v_scale)
     sm_scale = float(sm_scale) * gk
@@ -234,13 +276,13 @@ def decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos
                                mode, _p(m) if m is not None else None, n_seq, hq, _p(q), _p(_c(q_pos, np.int32)),
                                _p(ct), _p(st), _p(page_table), page_table.shape[1],
                                _p(_c(seq_lens, np.int32)), float(sm_scale), _p(vr) if vr is not None else None,
-                               _p(out))
+                               int(v_format), _p(out))
     return out * gv
 
 
 def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q, q_pos,
                            page_table, seq_lens, sm_scale, cos_tab=None, sin_tab=None, signs=None,
-                           k_scale=1.0, v_scale=1.0):
+                           k_scale=1.0, v_scale=1.0, v_format=0):
     """fp64 attention of M new query tokens per sequence over the pool's bytes,
     causal among the new tokens: the decode step of speculative verification
     (ai-manual.ru article on "Ninfer 4080", section "Key features": the draft
@@ -261,34 +303,37 @@ def decode_attention_multi(pool, num_pages, hkv, layer, rotary_dim, hadamard, q,
     out = decode_attention(pool, num_pages, hkv, layer, rotary_dim, hadamard,
                            q.reshape(n_seq * m, q.shape[2], HEAD_DIM),
                            np.asarray(q_pos, np.int32).reshape(-1), rows, pref, sm_scale,
-                           cos_tab, sin_tab, signs, k_scale=k_scale, v_scale=v_scale)
+                           cos_tab, sin_tab, signs, k_scale=k_scale, v_scale=v_scale, v_format=v_format)
     return out.reshape(n_seq, m, q.shape[2], HEAD_DIM)
 
 
-def spill_pages(pool, num_layers, num_pages, hkv, page_ids):
+def spill_pages(pool, num_layers, num_pages, hkv, page_ids, v_format=0):
     """Host copy of whole cache pages, for the pinned host arena of the
     release post's section "Multi-level prefix reuse with host-KV safety
     net" (pages are spilled device to host before eviction and restored
     later).  A page is every layer's and every kv head's 9216-byte block of
     that page id; the arena holds page i of the list at
-    arena[i][layer][kvh][9216].  Pool layout [layer][page][kvh][9216]."""
-    pool = np.asarray(pool, np.uint8).reshape(num_layers, num_pages, hkv, BLOCK_BYTES)
+    arena[i][layer][kvh][block].  Pool layout [layer][page][kvh][block]; a
+    block is 9216 bytes (20992 in an fp16-V pool)."""
+    bb = block_bytes(v_format)
+    pool = np.asarray(pool, np.uint8).reshape(num_layers, num_pages, hkv, bb)
     ids = np.asarray(page_ids, np.int64)
-    arena = np.empty((len(ids), num_layers, hkv, BLOCK_BYTES), np.uint8)
+    arena = np.empty((len(ids), num_layers, hkv, bb), np.uint8)
     for i, pid in enumerate(ids):
         arena[i] = pool[:, pid]
     return arena
 
 
-def restore_pages(pool, num_layers, num_pages, hkv, page_ids, arena):
+def restore_pages(pool, num_layers, num_pages, hkv, page_ids, arena, v_format=0):
     """The reverse of spill_pages: page i of the arena back into page id
     page_ids[i] of the pool (every layer and kv head), in place.  The ids
     must be distinct (two arena pages cannot both become one page)."""
     ids = np.asarray(page_ids, np.int64)
     if len(np.unique(ids)) != len(ids):
         raise ValueError("restore_pages: page ids must be distinct")
-    view = np.asarray(pool).reshape(num_layers, num_pages, hkv, BLOCK_BYTES)
-    arena = np.asarray(arena, np.uint8).reshape(-1, num_layers, hkv, BLOCK_BYTES)
+    bb = block_bytes(v_format)
+    view = np.asarray(pool).reshape(num_layers, num_pages, hkv, bb)
+    arena = np.asarray(arena, np.uint8).reshape(-1, num_layers, hkv, bb)
     for i, pid in enumerate(ids):
         view[:, pid] = arena[i]
     return pool

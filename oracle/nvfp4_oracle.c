@@ -238,64 +238,163 @@ void orc_dequant_row(const uint8_t* codes, const uint8_t* scales, double* out)
 }
 
 /* ------------------------------------------------------------------------ */
-/* Paged pool.  One block of 9216 bytes per (layer, page, kv-head), blocks in
- * [layer][page][kv_head] order.  Inside a block (64 tokens t, code byte j):
+/* IEEE 754 binary16 (fp16): the V storage of the variant the release post
+ * names as upstream's ("fp16 V storage", NVFP4 section, bullet 2).  1 sign,
+ * 5 exponent bits (bias 15), 10 mantissa bits; subnormals are multiples of
+ * 2^-24; largest finite 65504. */
+
+/* binary16 bits of the float x, rounded to nearest with ties to even (the
+ * IEEE default), overflowing to infinity, NaN kept a (quiet) NaN.  Written
+ * from the definition: |x| is split into its binary exponent E and the
+ * integer count of binary16 ulps 2^(E-10) (2^-24 below 2^-14), which is
+ * rounded with rint (ties to even under the default rounding mode); every
+ * step before the rounding is exact in double.  Infinities stay infinite. */
+uint16_t orc_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isnan(x)) return sign | 0x7E00;
+    if (isinf(a)) return sign | 0x7C00;
+    if (a < ldexp(1.0, -14)) {                         /* subnormal or zero */
+        double m = rint(a * 16777216.0);                /* units of 2^-24; 1024 = 2^-14 */
+        return sign | (uint16_t)m;
+    }
+    int e;
+    frexp(a, &e);                                       /* a = f 2^e, f in [0.5, 1) */
+    int E = e - 1;                                      /* a in [2^E, 2^(E+1)) */
+    double m = rint(ldexp(a, 10 - E));                  /* [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return sign | 0x7C00;                   /* infinity */
+    return sign | (uint16_t)(((E + 15) << 10) | ((int)m - 1024));
+}
+
+/* The value of binary16 bits h, exactly, in double. */
+double orc_f16_value(uint16_t h)
+{
+    int e = (h >> 10) & 31, m = h & 1023;
+    double mag;
+    if (e == 31) mag = m ? NAN : INFINITY;
+    else if (e == 0) mag = ldexp((double)m, -24);
+    else mag = ldexp(1024.0 + m, e - 25);
+    return (h & 0x8000) ? -mag : mag;
+}
+
+void orc_f32_to_f16_array(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Paged pool.  One block per (layer, page, kv-head), blocks in
+ * [layer][page][kv_head] order; a slot is page*64 + t.
+ *
+ * v_format 0 (NVFP4 V, the release post's format): 9216 bytes per block.
+ * Inside a block (64 tokens t, code byte j):
  *   K codes    at        (t/16)*1024 + (j/16)*256 + (t%16)*16 + (j%16)
  *   V codes    at 4096 + (t/4)*256  + (j/4)*16   + (t%4)*4   + (j%4)
  *   K scales   at 8192 + t*8 + b        (row-major, release post bullet 4)
  *   V scales   at 8704 + t*8 + b
- * A slot is page*64 + t.  Per token and kv-head: 2 * (64 + 8) = 144 bytes. */
-#define ORC_BLOCK_BYTES 9216
+ * Per token and kv-head: 2 * (64 + 8) = 144 bytes.
+ *
+ * v_format 1 (fp16 V, NVFP4 K; the upstream storage named in bullet 2):
+ * 20992 bytes per block, 328 per token and kv-head.
+ *   K codes    as above
+ *   V (fp16)   element d of token t at 4096 + (t/32)*8192 + (d%8)*1024
+ *              + (((t%16)/4)*16 + d/8)*16 + ((t%4) + 4*((t%32)/16))*2,
+ *              2 bytes little-endian
+ *   K scales   at 20480 + t*8 + b
+ * (The V order puts the eight fp16 values one lane of a 16x16x32 matrix
+ * instruction reads next to each other; it is this library's choice, the
+ * pages give none.) */
+static size_t orc_block_bytes(int v_format) { return v_format ? 20992 : 9216; }
+static int orc_kscale_off(int v_format) { return v_format ? 20480 : 8192; }
 
-size_t orc_pool_bytes(int num_layers, int64_t num_pages, int num_kv_heads)
+size_t orc_pool_bytes(int num_layers, int64_t num_pages, int num_kv_heads, int v_format)
 {
-    return (size_t)num_layers * (size_t)num_pages * (size_t)num_kv_heads * ORC_BLOCK_BYTES;
+    return (size_t)num_layers * (size_t)num_pages * (size_t)num_kv_heads * orc_block_bytes(v_format);
 }
 
-static size_t orc_block_base(int64_t num_pages, int hkv, int layer, int64_t page, int kvh)
+static size_t orc_block_base(int64_t num_pages, int hkv, int layer, int64_t page, int kvh, int v_format)
 {
     return (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + (size_t)kvh)
-           * ORC_BLOCK_BYTES;
+           * orc_block_bytes(v_format);
 }
 
 static size_t orc_kcode_off(int t, int j) { return (size_t)((t / 16) * 1024 + (j / 16) * 256 + (t % 16) * 16 + (j % 16)); }
 static size_t orc_vcode_off(int t, int j) { return (size_t)(4096 + (t / 4) * 256 + (j / 4) * 16 + (t % 4) * 4 + (j % 4)); }
+static size_t orc_v16_off(int t, int d)
+{
+    return (size_t)(4096 + (t / 32) * 8192 + (d % 8) * 1024 + (((t % 16) / 4) * 16 + d / 8) * 16
+                    + ((t % 4) + 4 * ((t % 32) / 16)) * 2);
+}
 
-/* Read the codes and scales of one cached row.  which = 0 for K, 1 for V. */
+/* Read the codes and scales of one cached NVFP4 row.  which = 0 for K, 1 for
+ * V (v_format 0 only). */
 void orc_pool_read_row(const uint8_t* pool, int64_t num_pages, int hkv, int layer,
-                       int64_t slot, int kvh, int which, uint8_t* codes, uint8_t* scales)
+                       int64_t slot, int kvh, int which, int v_format, uint8_t* codes, uint8_t* scales)
 {
     int64_t page = slot / ORC_PAGE;
     int t = (int)(slot % ORC_PAGE);
-    const uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh);
+    const uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh, v_format);
     for (int j = 0; j < ORC_ROW_CODE; ++j)
         codes[j] = blk[which ? orc_vcode_off(t, j) : orc_kcode_off(t, j)];
     for (int b = 0; b < ORC_NBLK; ++b)
-        scales[b] = blk[(which ? 8704 : 8192) + t * 8 + b];
+        scales[b] = blk[(which ? 8704 : orc_kscale_off(v_format)) + t * 8 + b];
+}
+
+/* Read the 128 fp16 V values (bits) of one cached row of a v_format 1 pool. */
+void orc_pool_read_v16(const uint8_t* pool, int64_t num_pages, int hkv, int layer, int64_t slot, int kvh,
+                       uint16_t* out)
+{
+    int64_t page = slot / ORC_PAGE;
+    int t = (int)(slot % ORC_PAGE);
+    const uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh, 1);
+    for (int d = 0; d < ORC_D; ++d) {
+        size_t o = orc_v16_off(t, d);
+        out[d] = (uint16_t)(blk[o] | (blk[o + 1] << 8));
+    }
 }
 
 static void orc_pool_write_row(uint8_t* pool, int64_t num_pages, int hkv, int layer,
-                               int64_t slot, int kvh, int which,
+                               int64_t slot, int kvh, int which, int v_format,
                                const uint8_t* codes, const uint8_t* scales)
 {
     int64_t page = slot / ORC_PAGE;
     int t = (int)(slot % ORC_PAGE);
-    uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh);
+    uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh, v_format);
     for (int j = 0; j < ORC_ROW_CODE; ++j)
         blk[which ? orc_vcode_off(t, j) : orc_kcode_off(t, j)] = codes[j];
     for (int b = 0; b < ORC_NBLK; ++b)
-        blk[(which ? 8704 : 8192) + t * 8 + b] = scales[b];
+        blk[(which ? 8704 : orc_kscale_off(v_format)) + t * 8 + b] = scales[b];
+}
+
+static void orc_pool_write_v16(uint8_t* pool, int64_t num_pages, int hkv, int layer, int64_t slot, int kvh,
+                               const float* v)
+{
+    int64_t page = slot / ORC_PAGE;
+    int t = (int)(slot % ORC_PAGE);
+    uint8_t* blk = pool + orc_block_base(num_pages, hkv, layer, page, kvh, 1);
+    for (int d = 0; d < ORC_D; ++d) {
+        uint16_t h = orc_f32_to_f16(v[d]);
+        size_t o = orc_v16_off(t, d);
+        blk[o] = (uint8_t)(h & 0xFF);
+        blk[o + 1] = (uint8_t)(h >> 8);
+    }
 }
 
 /* Append n_tok tokens (release post, NVFP4 section, bullet 3): for every
  * token and kv-head, K gets RoPE (at positions[i]) + Hadamard + NVFP4, V gets
- * NVFP4 only, and both rows are written into the slot's page.
+ * NVFP4 only (v_format 0) or is rounded to fp16 (v_format 1), and both rows
+ * are written into the slot's page.
  * k, v: [n_tok][hkv][128] floats (bf16 inputs are widened exactly first).
  * cos_tab/sin_tab: [max_pos][rotary_dim/2]. */
 void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int hadamard,
                 const uint32_t* signs, int layer, int n_tok, const float* k, const float* v,
                 const int64_t* slots, const int32_t* positions,
-                const float* cos_tab, const float* sin_tab)
+                const float* cos_tab, const float* sin_tab, int v_format)
 {
     int half = rotary_dim / 2;
 #pragma omp parallel for schedule(static)
@@ -306,9 +405,13 @@ void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int h
             const float* s = rotary_dim > 0 ? sin_tab + (size_t)positions[i] * half : NULL;
             orc_quant_row(k + ((size_t)i * hkv + g) * ORC_D, rotary_dim, c, s, hadamard, signs,
                           codes, scales);
-            orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 0, codes, scales);
-            orc_quant_row(v + ((size_t)i * hkv + g) * ORC_D, 0, NULL, NULL, 0, NULL, codes, scales);
-            orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 1, codes, scales);
+            orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 0, v_format, codes, scales);
+            if (v_format) {
+                orc_pool_write_v16(pool, num_pages, hkv, layer, slots[i], g, v + ((size_t)i * hkv + g) * ORC_D);
+            } else {
+                orc_quant_row(v + ((size_t)i * hkv + g) * ORC_D, 0, NULL, NULL, 0, NULL, codes, scales);
+                orc_pool_write_row(pool, num_pages, hkv, layer, slots[i], g, 1, 0, codes, scales);
+            }
         }
     }
 }
@@ -324,14 +427,15 @@ void orc_append(uint8_t* pool, int64_t num_pages, int hkv, int rotary_dim, int h
  * All of it in double.  q: [n_seq][hq][128] floats; out: [n_seq][hq][128].
  * With v_rows (one sequence only) the V values are taken from v_rows
  * [T][hkv][128] instead of the pool: the K-only-quantized variant of a
- * quality study (V kept in a 16-bit format by the caller). */
+ * quality study (V kept in a 16-bit format by the caller).  v_format 1: the
+ * pool keeps V in fp16 (the values are read from it exactly). */
 void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int layer,
                           int rotary_dim, int hadamard, const uint32_t* signs, int n_seq, int hq,
                           const float* q, const int32_t* q_pos,
                           const float* cos_tab, const float* sin_tab,
                           const int32_t* page_table, int page_table_stride,
                           const int32_t* seq_lens, double sm_scale, const float* v_rows,
-                          double* out)
+                          int v_format, double* out)
 {
     int grp = hq / hkv, half = rotary_dim / 2;
     for (int n = 0; n < n_seq; ++n) {
@@ -354,7 +458,7 @@ void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int l
                 double kh[ORC_D];
                 int64_t slot = (int64_t)page_table[(size_t)n * page_table_stride + t / ORC_PAGE]
                                * ORC_PAGE + t % ORC_PAGE;
-                orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 0, codes, scales);
+                orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 0, v_format, codes, scales);
                 orc_dequant_row(codes, scales, kh);
                 for (int r = 0; r < grp; ++r) {
                     double acc = 0.0;
@@ -386,8 +490,12 @@ void orc_decode_attention(const uint8_t* pool, int64_t num_pages, int hkv, int l
                                    * ORC_PAGE + t % ORC_PAGE;
                     if (v_rows != NULL) {
                         for (int d = 0; d < ORC_D; ++d) vh[d] = v_rows[((size_t)t * hkv + g) * ORC_D + d];
+                    } else if (v_format) {
+                        uint16_t h16[ORC_D];
+                        orc_pool_read_v16(pool, num_pages, hkv, layer, slot, g, h16);
+                        for (int d = 0; d < ORC_D; ++d) vh[d] = orc_f16_value(h16[d]);
                     } else {
-                        orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 1, codes, scales);
+                        orc_pool_read_row(pool, num_pages, hkv, layer, slot, g, 1, 0, codes, scales);
                         orc_dequant_row(codes, scales, vh);
                     }
                     for (int r = 0; r < grp; ++r) {
