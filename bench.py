@@ -390,8 +390,8 @@ def bench_quality(args, torch, kv, W, DecodeStep):
     oracle's fp64 NVFP4 attention on the GPU's own pool bytes, which
     separates the format's error from the kernel's.  The fp16-V variant
     (NVFP4 K with the Hadamard rotation, V kept in fp16: 328 bytes per token
-    per kv head) is computed by the oracle from the same pool's K and the
-    raw V rows rounded to fp16."""
+    per kv head, the upstream storage) runs on the GPU through a v_format 1
+    pool and is checked against the oracle on that pool."""
     import numpy as np
     import oracle
     rng = np.random.default_rng(2026)
@@ -418,7 +418,6 @@ def bench_quality(args, torch, kv, W, DecodeStep):
                                                  W.sm_scale(), oc, os_)
                 log(f"outliers x{outlier_scale:g}: reference attention over {T} tokens "
                     f"{time.perf_counter() - t0:.1f} s")
-                v16 = v.astype(np.float16).astype(np.float32)
                 del k, v
             npg = (T + 63) // 64
             pages = torch.from_numpy(step.table_np[0, :npg].astype(np.int64)).cuda()
@@ -435,23 +434,34 @@ def bench_quality(args, torch, kv, W, DecodeStep):
                          "gpu_vs_oracle_max_abs": float(np.abs(out - orc).max())}
             log(f"outliers x{outlier_scale:g} {name}: rel L2 {rel:.4g}, median head "
                 f"{res[name]['median_head_rel_l2']:.4g}, GPU vs oracle {res[name]['gpu_vs_oracle_max_abs']:.2g}")
+            del step, compact
+            torch.cuda.empty_cache()
             if name == "hadamard":
-                o16 = oracle.decode_attention(compact.contiguous().view(-1).cpu().numpy(), npg, wl.hkv, 0,
-                                              wl.rotary_dim, had, step.q[0].float().cpu().numpy(),
-                                              [wl.cached[0]], np.arange(npg, dtype=np.int32)[None], [T],
-                                              W.sm_scale(), oc, os_, v_rows=v16)[0]
+                # the upstream storage: NVFP4 K, V in fp16 (328 bytes per token per kv head), on the
+                # GPU through the fp16-V pool format, checked against the oracle on its own pool
+                step = DecodeStep(wl, v_format=1)
+                step.fill([0])
+                o16 = step.decode(0, fused=True).cpu().numpy()[0].astype(np.float64)
+                bb = step.pool.block_bytes
+                compact = step.pool.data.view(1, step.pool.num_pages, wl.hkv * bb)[0].index_select(0, pages)
+                orc16 = oracle.decode_attention(compact.contiguous().view(-1).cpu().numpy(), npg, wl.hkv, 0,
+                                                wl.rotary_dim, had, step.q[0].float().cpu().numpy(),
+                                                [wl.cached[0]], np.arange(npg, dtype=np.int32)[None], [T],
+                                                W.sm_scale(), oc, os_, v_format=1)[0]
                 res["hadamard_fp16_v"] = {
                     "rel_l2_err": round(float(np.linalg.norm(o16 - ref) / np.linalg.norm(ref)), 6),
                     "max_abs_err": float(np.abs(o16 - ref).max()),
                     "median_head_rel_l2": round(float(np.median([np.linalg.norm(o16[h] - ref[h]) /
                                                                  np.linalg.norm(ref[h]) for h in range(wl.hq)])), 6),
-                    "computed_by": "oracle (no fp16-V kernel)"}
-                log(f"outliers x{outlier_scale:g} hadamard + fp16 V (oracle): rel L2 "
-                    f"{res['hadamard_fp16_v']['rel_l2_err']:.4g}")
-            del step
-            torch.cuda.empty_cache()
+                    "gpu_vs_oracle_max_abs": float(np.abs(o16 - orc16).max()),
+                    "bytes_per_token_kv_head": 328,
+                    "computed_by": "GPU (v_format 1 pool), checked against the oracle"}
+                log(f"outliers x{outlier_scale:g} hadamard + fp16 V (GPU): rel L2 "
+                    f"{res['hadamard_fp16_v']['rel_l2_err']:.4g}, GPU vs oracle "
+                    f"{res['hadamard_fp16_v']['gpu_vs_oracle_max_abs']:.2g}")
+                del step, compact
+                torch.cuda.empty_cache()
         report[f"outliers_x{outlier_scale:g}"] = res
-        del v16
     rec = {
         "metric": "NVFP4 attention error vs unquantized fp64 attention (relative L2), per rotation",
         "value": report["outliers_x4"]["hadamard"]["rel_l2_err"], "unit": "relative L2",

@@ -56,17 +56,23 @@ typedef enum {
 typedef enum { NVFP4KV_F32 = 0, NVFP4KV_BF16 = 1 } nvfp4kv_dtype;
 
 /* Byte layout of the pool (device memory, caller-owned, 256-byte aligned).
- * One block of 9216 bytes per (layer, page, kv head), blocks ordered
- * [layer][page][kv_head].  A slot is page * 64 + t with t the token's place
- * in its page.  Code byte j of a row holds elements 2j (low nibble) and 2j+1
- * (high nibble).  Inside a block:
+ * One block per (layer, page, kv head), blocks ordered [layer][page][kv_head].
+ * A slot is page * 64 + t with t the token's place in its page.  Code byte j
+ * of a row holds elements 2j (low nibble) and 2j+1 (high nibble).
+ * v_format 0 (NVFP4 K and V, the release post's format): 9216 bytes a block,
  *   [   0, 4096) K codes, byte j of token t at (t/16)*1024 + (j/16)*256 + (t%16)*16 + j%16
  *   [4096, 8192) V codes, byte j of token t at 4096 + (t/4)*256 + (j/4)*16 + (t%4)*4 + j%4
  *   [8192, 8704) K scales, row-major: scale of block b (elements 16b..16b+15) of token t at 8192 + 8t + b
  *   [8704, 9216) V scales, row-major: at 8704 + 8t + b
- * The code tiling puts the 16 bytes that one lane of a 16x16x32 matrix
- * instruction needs next to each other; the scales stay row-major as the
- * release post specifies.  K rows are stored rotated (Hadamard domain). */
+ * v_format 1 (NVFP4 K, V in IEEE fp16: the upstream storage the release
+ * post compares against, NVFP4 section, bullet 2): 20992 bytes a block,
+ *   [    0,  4096) K codes as above
+ *   [ 4096, 20480) V, element d of token t (fp16, little-endian) at
+ *                  4096 + (t/32)*8192 + (d%8)*1024 + (((t%16)/4)*16 + d/8)*16 + ((t%4) + 4*((t%32)/16))*2
+ *   [20480, 20992) K scales, row-major: at 20480 + 8t + b
+ * The code and fp16 tilings put the 16 bytes that one lane of a 16x16x32
+ * matrix instruction needs next to each other; the scales stay row-major as
+ * the release post specifies.  K rows are stored rotated (Hadamard domain). */
 typedef struct {
     void* base;             /* device pointer to the pool */
     int64_t num_pages;      /* pages per layer; page ids index [0, num_pages) */
@@ -92,12 +98,21 @@ typedef struct {
                                over the block scales); the release post keeps
                                it at 1 */
     float v_scale;          /* the same for V */
+    int32_t v_format;       /* 0: V in NVFP4 (144 bytes per token per kv head);
+                               1: V in fp16 (328 bytes; each element times the
+                               binary32 1/v_scale, rounded to nearest even).
+                               The fp16 form is a comparison variant: decode
+                               takes it for up to 8 query heads per kv head
+                               and one query token (nvfp4kv_decode_attn,
+                               _static, _splits); multi-token decode and the
+                               read probe refuse it (NVFP4KV_ERR_UNSUPPORTED) */
 } nvfp4kv_pool;
 
 /* Bytes the pool needs: num_layers * num_pages * num_kv_heads * 64 * 144,
  * i.e. 144 bytes per token per kv head (release post, NVFP4 section, the
  * "Result" line: 2 x (64 code bytes + 8 E4M3 scale bytes) for a 128-element
- * head).  Host only.  Returns 0 if `p` is null or its sizes are invalid. */
+ * head); 328 instead of 144 with v_format 1 (64 + 8 for K, 256 for fp16 V).
+ * Host only.  Returns 0 if `p` is null or its sizes are invalid. */
 size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p);
 
 /* RoPE table on the HOST (section "YaRN context extension"): for position
@@ -283,9 +298,9 @@ int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const i
                     void* k_out, void* v_out, nvfp4kv_dtype out_dtype, int32_t unrotate,
                     hipStream_t stream);
 
-/* Bytes of one spilled page: every layer's and every kv head's 9216-byte
- * block of one page id, num_layers * num_kv_heads * 9216 (host; 0 for an
- * invalid pool). */
+/* Bytes of one spilled page: every layer's and every kv head's block of one
+ * page id, num_layers * num_kv_heads * (9216, or 20992 with v_format 1)
+ * (host; 0 for an invalid pool). */
 size_t nvfp4kv_page_bytes(const nvfp4kv_pool* p);
 
 /* Host spill and restore of whole cache pages: the pinned host arena of the
@@ -298,7 +313,7 @@ size_t nvfp4kv_page_bytes(const nvfp4kv_pool* p);
  *   page_ids    [n_pages] int32 in device memory or pinned host memory; ids
  *               outside [0, num_pages) are skipped (their arena entry is
  *               left as it was on spill)
- *   arena       [n_pages][num_layers][num_kv_heads][9216] bytes, at least
+ *   arena       [n_pages][num_layers][num_kv_heads][block bytes], at least
  *               n_pages * nvfp4kv_page_bytes(p) bytes, 16-byte aligned, in
  *               pinned host memory (hipHostMalloc) or in device memory of
  *               the current device; any other pointer is refused

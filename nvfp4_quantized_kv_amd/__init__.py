@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 HEAD_DIM, PAGE_SIZE, BLOCK_BYTES = 128, 64, 9216
+BLOCK_BYTES_F16V = 20992       # v_format 1: NVFP4 K, fp16 V
+V_NVFP4, V_FP16 = 0, 1
 
 
 class NVFP4KVError(RuntimeError):
@@ -43,6 +45,7 @@ class _PoolDesc(ctypes.Structure):
         ("hadamard_signs", ctypes.c_uint32 * 4),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("v_format", ctypes.c_int32),
     ]
 
 
@@ -154,25 +157,31 @@ class Pool:
     signs: tuple = (0, 0, 0, 0)  # hadamard 2: 128-bit element mask, 4 uint32 words
     k_scale: float = 1.0        # per-tensor global scales of K and V (stored values are x / scale)
     v_scale: float = 1.0
+    v_format: int = V_NVFP4     # V_FP16: V kept in fp16 (328 bytes per token per kv head)
 
     @classmethod
     def allocate(cls, num_pages: int, num_layers: int, num_kv_heads: int, rotary_dim: int = 0,
                  hadamard: int = 1, device="cuda", signs=(0, 0, 0, 0), k_scale: float = 1.0,
-                 v_scale: float = 1.0) -> "Pool":
+                 v_scale: float = 1.0, v_format: int = V_NVFP4) -> "Pool":
         signs = tuple(int(x) & 0xFFFFFFFF for x in signs)
         desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE,
-                         rotary_dim, int(hadamard), (ctypes.c_uint32 * 4)(*signs), k_scale, v_scale)
+                         rotary_dim, int(hadamard), (ctypes.c_uint32 * 4)(*signs), k_scale, v_scale,
+                         int(v_format))
         nbytes = _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
         if nbytes == 0:
             raise ValueError("invalid pool shape")
         data = torch.empty(nbytes, dtype=torch.uint8, device=device)
         return cls(data, num_pages, num_layers, num_kv_heads, rotary_dim, int(hadamard), signs, float(k_scale),
-                   float(v_scale))
+                   float(v_scale), int(v_format))
+
+    @property
+    def block_bytes(self) -> int:
+        return BLOCK_BYTES_F16V if self.v_format else BLOCK_BYTES
 
     def desc(self) -> _PoolDesc:
         return _PoolDesc(self.data.data_ptr(), self.num_pages, self.num_layers, self.num_kv_heads,
                          HEAD_DIM, PAGE_SIZE, self.rotary_dim, int(self.hadamard),
-                         (ctypes.c_uint32 * 4)(*self.signs), self.k_scale, self.v_scale)
+                         (ctypes.c_uint32 * 4)(*self.signs), self.k_scale, self.v_scale, int(self.v_format))
 
 
 def nvfp4kv_version() -> str:
@@ -183,8 +192,9 @@ def nvfp4kv_last_error() -> str:
     return _lib.nvfp4kv_last_error().decode()
 
 
-def nvfp4kv_pool_bytes(num_pages: int, num_layers: int, num_kv_heads: int) -> int:
-    desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE, 0, 1)
+def nvfp4kv_pool_bytes(num_pages: int, num_layers: int, num_kv_heads: int, v_format: int = V_NVFP4) -> int:
+    desc = _PoolDesc(None, num_pages, num_layers, num_kv_heads, HEAD_DIM, PAGE_SIZE, 0, 1,
+                     (ctypes.c_uint32 * 4)(0, 0, 0, 0), 0.0, 0.0, int(v_format))
     return _lib.nvfp4kv_pool_bytes(ctypes.byref(desc))
 
 
@@ -391,11 +401,12 @@ def nvfp4kv_page_bytes(pool: Pool) -> int:
 def nvfp4kv_spill_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
     """Copy whole pages (every layer and kv head) to arena [n][num_layers]
-    [num_kv_heads][9216] uint8: pinned host memory by default, or the given
-    pinned-host or device tensor.  page_ids: int32 on the device or pinned."""
+    [num_kv_heads][block bytes] uint8: pinned host memory by default, or the
+    given pinned-host or device tensor.  page_ids: int32 on the device or
+    pinned."""
     assert page_ids.dtype == torch.int32 and page_ids.is_contiguous()
     n = page_ids.numel()
-    shape = (n, pool.num_layers, pool.num_kv_heads, 9216)
+    shape = (n, pool.num_layers, pool.num_kv_heads, pool.block_bytes)
     if arena is None:
         arena = torch.empty(shape, dtype=torch.uint8, pin_memory=True)
     assert arena.dtype == torch.uint8 and arena.is_contiguous()

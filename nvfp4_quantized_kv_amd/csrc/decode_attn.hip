@@ -176,6 +176,42 @@ __device__ __forceinline__ void pv_unit(const u4& va, const u4& vb, const uint8_
   }
 }
 
+// PV of one 32-token unit with V kept in fp16 (v_format 1): `vh` holds the
+// lane's A operands of the unit's 8 dim tiles (tile j: dims 8*c16 + j of the
+// tokens of k-slots 0-7, as the pool's fp16 tiling stores them), so the
+// operands go to the matrix instructions as loaded.  Weights as in pv_unit.
+template <bool PACKED, int NT>
+__device__ __forceinline__ void pv_unit_f16(const u4 (&vh)[8], const h8 (&p0)[NT], const h8 (&p1)[NT],
+                                            f4 (&acc)[NT][8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const h8 a = __builtin_bit_cast(h8, vh[j]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p0[t], acc[t][j], 0, 0, 0);
+      if (!PACKED) acc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, p1[t], acc[t][j], 0, 0, 0);
+    }
+  }
+}
+
+// fp16 V of a page's tokens nv .. 63 set to zero in the lane's operands (both
+// units): a slot past a sequence's end may hold any bytes, Inf or NaN among
+// them, and a zero weight does not cancel those in the matrix product.
+__device__ __forceinline__ void mask_v16(u4 (&vh)[16], int nv, int g4) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // k-slots 2w and 2w+1: tokens 32u + 4*g4 + s (s < 4) or 32u + 12 + 4*g4 + s (s >= 4)
+      const int s0 = 2 * w, s1 = 2 * w + 1;
+      const int t0 = 32 * u + 4 * g4 + s0 + (s0 >= 4 ? 12 : 0);
+      const int t1 = 32 * u + 4 * g4 + s1 + (s1 >= 4 ? 12 : 0);
+      const uint32_t m = (t0 < nv ? 0x0000FFFFu : 0u) | (t1 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vh[8 * u + j][w] &= m;
+    }
+}
+
 // Pages of sequence `s`.
 __device__ inline int64_t seq_pages(const int32_t* __restrict__ seq_lens, int s) {
   return (seq_lens[s] + kPageSize - 1) / kPageSize;
@@ -339,16 +375,16 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
 
 // The current token of segment sg (token seq_lens[seq] - 1) quantized into
 // its pool slot exactly as the append kernel does it: lanes 0-15 the K row
-// (RoPE at q_positions[seq], Hadamard), lanes 16-31 the V row; lanes 32-63
-// repeat the two rows (every lane takes part in the shuffles) and store
-// nothing.
+// (RoPE at q_positions[seq], Hadamard), lanes 16-31 the V row (quantized, or
+// with `vf16` rounded to fp16); lanes 32-63 repeat the two rows (every lane
+// takes part in the shuffles) and store nothing.
 __device__ __forceinline__ void append_new_token(
     int sg, uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer,
     const void* __restrict__ k_new, const void* __restrict__ v_new, int in_dtype,
     const int32_t* __restrict__ q_positions, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, int rotary_dim, int hadamard, const SignMask& signs,
     const int32_t* __restrict__ page_table, int pt_stride, const int32_t* __restrict__ seq_lens,
-    float2 kv_inv) {
+    float2 kv_inv, bool vf16) {
   const int lane = (int)threadIdx.x;
   const int c16 = lane & 15;
   const int which = (lane >> 4) & 1;   // 0 = K, 1 = V
@@ -375,10 +411,18 @@ __device__ __forceinline__ void append_new_token(
     const int page = page_table[(size_t)seq * pt_stride + tok / kPageSize];
     const uint32_t t = (uint32_t)(tok % kPageSize);
     uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + kvh) *
-                              (size_t)kBlockBytes;
-    *reinterpret_cast<uint32_t*>(blk + (which ? v_code_word_off(t, (uint32_t)c16)
-                                              : k_code_word_off(t, (uint32_t)c16))) = codes;
-    if ((c16 & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + c16 / 2] = (uint8_t)scode;
+                              (size_t)(vf16 ? kBlockBytesF16V : kBlockBytes);
+    if (which && vf16) {
+      // (V rows get neither RoPE nor the rotation: x still holds the inputs)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        *reinterpret_cast<uint16_t*>(blk + v16_off(t, (uint32_t)(8 * c16 + k))) = (uint16_t)f16_bits(x[k]);
+    } else {
+      *reinterpret_cast<uint32_t*>(blk + (which ? v_code_word_off(t, (uint32_t)c16)
+                                                : k_code_word_off(t, (uint32_t)c16))) = codes;
+      if ((c16 & 1) == 0)
+        blk[(which ? kVScaleOff : (vf16 ? kKScaleOffF16V : kKScaleOff)) + 8 * t + c16 / 2] = (uint8_t)scode;
+    }
   }
 }
 
@@ -688,7 +732,11 @@ constexpr int kQSlots = 3;
 // dequantized once and feeds NT times the MFMAs and softmax work.  Those
 // kernels hold NT sets of scores, weights and accumulators and run one
 // wavefront per SIMD.
-template <bool PACKED, bool MQ, int NT>
+//
+// VF16 (the fp16-V pool format, page-softmax kernels only): V tiles are
+// loaded as fp16 operands, 16 KB a page, and go to the matrix instructions
+// without dequantization.
+template <bool PACKED, bool MQ, int NT, bool VF16 = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 : 2, NT > 1 ? 1 : 2))) void decode_attn_splitk_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_seq, int n_q_heads,
     QCols qc, const void* __restrict__ q, const void* __restrict__ k_new,
@@ -765,14 +813,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   };
   load_window(seq, kvh0, seq_base + (int64_t)kvh0 * pg, pg);
 
+  static_assert(!VF16 || (PACKED && NT == 1 && !MQ), "fp16 V: page-softmax kernel of one query token only");
+  constexpr int kBB = VF16 ? kBlockBytesF16V : kBlockBytes;   // block bytes
+  constexpr int kKS = VF16 ? kKScaleOffF16V : kKScaleOff;     // K scales in a block
   const uint8_t* layer_base =
-      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBlockBytes;
+      pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBB;
   // buffer resource of flat page x (empty past the range)
   auto rsrc_of = [&](int64_t x) {
     const bool ok = x < b;
     const int blk = __builtin_amdgcn_readlane(w_blk, (int)((ok ? x : b - 1) - win));
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(layer_base + (size_t)blk * kBlockBytes),
-                                             0, ok ? kBlockBytes : 0, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(layer_base + (size_t)blk * kBB),
+                                             0, ok ? kBB : 0, 0x00020000);
   };
   auto nvalid_of = [&](int64_t x) {
     return x < b ? __builtin_amdgcn_readlane(w_nv, (int)(x - win)) : 0;
@@ -821,7 +872,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
         append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
                          q_positions, rope_cos, rope_sin, rotary_dim, hadamard, signs, page_table,
-                         pt_stride, seq_lens, kv_inv);
+                         pt_stride, seq_lens, kv_inv, VF16);
         any = true;
       }
       sstart += pgl;
@@ -883,18 +934,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // loop's back edge, so the wait counts at the loop head are the same on
   // entry and on the back edge.
   u4 kA[4], vA[4], sA, kB[4], vB[4], sB;
+  u4 vH[VF16 ? 16 : 1];   // fp16 V of a page: units 0 and 1, 8 dim tiles each
   if constexpr (kPageSoftmax) {
     // one register set, loads one page ahead: page a's scales, K and V
     const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a);
-    sA = ld16(r0, voff, kKScaleOff);
+    sA = ld16(r0, voff, kKS);
     kA[0] = ld16(r0, voff, 0);
     kA[1] = ld16(r0, voff, 1024);
     kA[2] = ld16(r0, voff, 2048);
     kA[3] = ld16(r0, voff, 3072);
-    vA[0] = ld16(r0, voff, kVCodeOff);
-    vA[1] = ld16(r0, voff, kVCodeOff + 1024);
-    vA[2] = ld16(r0, voff, kVCodeOff + 2048);
-    vA[3] = ld16(r0, voff, kVCodeOff + 3072);
+    if constexpr (VF16) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) vH[j] = ld16(r0, voff, kVCodeOff + 1024 * j);
+    } else {
+      vA[0] = ld16(r0, voff, kVCodeOff);
+      vA[1] = ld16(r0, voff, kVCodeOff + 1024);
+      vA[2] = ld16(r0, voff, kVCodeOff + 2048);
+      vA[3] = ld16(r0, voff, kVCodeOff + 3072);
+    }
     __builtin_amdgcn_sched_barrier(0);
   } else {
     const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a), r1 = rsrc_of(a + 1);
@@ -938,7 +995,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     // page a+1's scales and K on their way
     const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
-    sA = ld16(r1, voff, kKScaleOff);
+    sA = ld16(r1, voff, kKS);
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
     q_of(seg0, qb, e_lo);
     qk_unit<NT>(kA[0], kA[1], sb + sk_off, qb, S);
@@ -1027,7 +1084,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     const uint8_t* sb_nxt = reinterpret_cast<const uint8_t*>(&sc_lds[cur ^ 1][0]);
     // page p+1's scales staged, page p+2's on their way
     sc_lds[cur ^ 1][lane] = sA & 0x7F7F7F7Fu;
-    sA = ld16(r2, voff, kKScaleOff);
+    sA = ld16(r2, voff, kKS);
     if (nv >= 64 + mcut)
       softmax_page<false>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group, ws_acc,
                           ws_ml, st.slot, cut[0]);
@@ -1035,12 +1092,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       softmax_page<true>(S[0], g4, c16, nv, c_log2, acc[0], m_ref[0], l_run[0], pa, pb, sw, group, ws_acc,
                          ws_ml, st.slot, cut[0]);
     if (sw) st.slot += 1;
+    if constexpr (VF16) {
+      if (nv < 64) mask_v16(vH, nv, g4);
+      pv_unit_f16<PACKED, NT>(reinterpret_cast<const u4(&)[8]>(vH[0]), reinterpret_cast<const h8(&)[NT]>(pa),
+                              pw1, acc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vH[j] = ld16(r1, voff, kVCodeOff + 1024 * j);
+      pv_unit_f16<PACKED, NT>(reinterpret_cast<const u4(&)[8]>(vH[8]), reinterpret_cast<const h8(&)[NT]>(pb),
+                              pw1, acc);
+#pragma unroll
+      for (int j = 8; j < 16; ++j) vH[j] = ld16(r1, voff, kVCodeOff + 1024 * j);
+    } else {
     pv_unit<PACKED, NT>(vA[0], vA[1], sb_cur + sv_off, reinterpret_cast<const h8(&)[NT]>(pa), pw1, acc);
     vA[0] = ld16(r1, voff, kVCodeOff);
     vA[1] = ld16(r1, voff, kVCodeOff + 1024);
     pv_unit<PACKED, NT>(vA[2], vA[3], sb_cur + sv_off + 256, reinterpret_cast<const h8(&)[NT]>(pb), pw1, acc);
     vA[2] = ld16(r1, voff, kVCodeOff + 2048);
     vA[3] = ld16(r1, voff, kVCodeOff + 3072);
+    }
     q_of(sg1, qb, e_lo);
     qk_unit<NT>(kA[0], kA[1], sb_nxt + sk_off, qb, S);
     kA[0] = ld16(r2, voff, 0);
@@ -1290,7 +1359,9 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
   const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
   const bool packed = plan.group <= 8, mq = qt.n_qtok > 1;
   const int nt = decode_column_tiles(plan.group);
-  auto kern = nt == 3   ? decode_attn_splitk_kernel<false, true, 3>
+  if (P.v_format != 0 && (!packed || mq)) return hipErrorInvalidValue;   // refused by the C ABI before
+  auto kern = P.v_format != 0 ? decode_attn_splitk_kernel<true, false, 1, true>
+              : nt == 3   ? decode_attn_splitk_kernel<false, true, 3>
               : nt == 2 ? decode_attn_splitk_kernel<false, true, 2>
               : packed  ? (mq ? decode_attn_splitk_kernel<true, true, 1> : decode_attn_splitk_kernel<true, false, 1>)
                         : (mq ? decode_attn_splitk_kernel<false, true, 1> : decode_attn_splitk_kernel<false, false, 1>);
@@ -1340,8 +1411,16 @@ hipError_t static_workspace(void** ptr) {
   return hipSuccess;
 }
 
-int decode_waves_per_cu(int nt, bool packed) {
+int decode_waves_per_cu(int nt, bool packed, bool vf16) {
   int lo = 1 << 30;
+  if (vf16) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false, 1, true>), 64, 0) !=
+        hipSuccess)
+      return 0;
+    return blocks;
+  }
   const void* one_packed[2] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, false, 1>),
                                reinterpret_cast<const void*>(decode_attn_splitk_kernel<true, true, 1>)};
   const void* one[2] = {reinterpret_cast<const void*>(decode_attn_splitk_kernel<false, false, 1>),

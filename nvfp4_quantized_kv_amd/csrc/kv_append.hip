@@ -216,11 +216,12 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     const void* __restrict__ k, const void* __restrict__ v,
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
-    int hadamard, SignMask signs, float k_inv, float v_inv) {
+    int hadamard, SignMask signs, float k_inv, float v_inv, int v_format, int block_bytes, int ks_off) {
   const int lane = (int)__lane_id();
   const int r = lane & 15;
   const int wv = (int)(threadIdx.x >> 6);
   const int which = wv >> 2;                       // 0 = K, 1 = V
+  const bool vf16 = which && v_format;             // V rows kept in fp16 (uniform per wavefront)
   const int rot = which ? 0 : rotary_dim;
   const bool had = which ? false : (hadamard != 0);
   const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
@@ -263,16 +264,25 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     raw_to_float<DT>(rw, x);
 #pragma unroll
     for (int k = 0; k < 8; ++k) x[k] *= inv;
-    uint32_t codes, scode;
-    append_row16(x, r, rot > 0, rl, had, neg, codes, scode);
-    if (active) {
-      const int64_t page = slot / kPageSize;
-      const uint32_t t = (uint32_t)(slot % kPageSize);
-      uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
-                                (size_t)kBlockBytes;
-      const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
-      *reinterpret_cast<uint32_t*>(blk + woff) = codes;
-      if ((r & 1) == 0) blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + r / 2] = (uint8_t)scode;
+    const int64_t page = slot / kPageSize;
+    const uint32_t t = (uint32_t)(slot % kPageSize);
+    uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
+                              (size_t)block_bytes;
+    if (vf16) {
+      // V kept in fp16: element 8r + k rounded to nearest even, into its tile
+      if (active) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          *reinterpret_cast<uint16_t*>(blk + v16_off(t, (uint32_t)(8 * r + k))) = (uint16_t)f16_bits(x[k]);
+      }
+    } else {
+      uint32_t codes, scode;
+      append_row16(x, r, rot > 0, rl, had, neg, codes, scode);
+      if (active) {
+        const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
+        *reinterpret_cast<uint32_t*>(blk + woff) = codes;
+        if ((r & 1) == 0) blk[(which ? kVScaleOff : ks_off) + 8 * t + r / 2] = (uint8_t)scode;
+      }
     }
     slot = slot_n;
     pos = pos_n;
@@ -285,8 +295,13 @@ __device__ inline void store8(void* dst, int dtype, size_t elem_off, const float
     uint32_t u[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      // the values are exact in bf16: truncation is exact
-      u[i] = (__float_as_uint(x[2 * i]) >> 16) | (__float_as_uint(x[2 * i + 1]) & 0xFFFF0000u);
+      // bf16 nearest with ties to even (exact for the NVFP4 block values,
+      // which have at most 6 significant bits; fp16 V values and un-rotated
+      // rows are rounded)
+      uint32_t a = __float_as_uint(x[2 * i]), b = __float_as_uint(x[2 * i + 1]);
+      a = (a + 0x7FFFu + ((a >> 16) & 1u)) >> 16;
+      b = (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+      u[i] = a | b;
     }
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + elem_off) = make_uint4(u[0], u[1], u[2], u[3]);
   } else {
@@ -299,7 +314,8 @@ __device__ inline void store8(void* dst, int dtype, size_t elem_off, const float
 __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
     const uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_rows,
     const int64_t* __restrict__ slots, void* __restrict__ k_out, void* __restrict__ v_out,
-    int dtype, int unrotate, int hadamard, SignMask signs, float k_scale, float v_scale) {
+    int dtype, int unrotate, int hadamard, SignMask signs, float k_scale, float v_scale, int v_format,
+    int block_bytes, int ks_off) {
   const int r = (int)(threadIdx.x & 15);
   const int row = (int)(blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16);
   const bool active = row < n_rows;
@@ -311,13 +327,20 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(
   const int64_t page = slot / kPageSize;
   const uint32_t t = (uint32_t)(slot % kPageSize);
   const uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
-                                  (size_t)kBlockBytes;
-  const uint32_t codes = *reinterpret_cast<const uint32_t*>(
-      blk + (which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r)));
-  const float s = e4m3_value(blk[(which ? kVScaleOff : kKScaleOff) + 8 * t + r / 2]);
+                                  (size_t)block_bytes;
   float x[8];
+  if (which && v_format) {
+    // fp16 V: the stored values, exactly
 #pragma unroll
-  for (int k = 0; k < 8; ++k) x[k] = e2m1_value((codes >> (4 * k)) & 15u) * s;
+    for (int k = 0; k < 8; ++k)
+      x[k] = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t*>(blk + v16_off(t, (uint32_t)(8 * r + k))));
+  } else {
+    const uint32_t codes = *reinterpret_cast<const uint32_t*>(
+        blk + (which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r)));
+    const float s = e4m3_value(blk[(which ? kVScaleOff : ks_off) + 8 * t + r / 2]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = e2m1_value((codes >> (4 * k)) & 15u) * s;
+  }
   // times the global scale (binary32 product of the exact block value)
   const float gs = which ? v_scale : k_scale;
 #pragma unroll
@@ -367,7 +390,7 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
   auto kern = dtype == 1 ? kv_quant_append_kernel<1> : kv_quant_append_kernel<0>;
   hipLaunchKernelGGL(kern, dim3(runs), dim3(512), 0, stream, P.base, P.num_pages, P.hkv, layer, n_tok, k,
                      v, slots, positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs, P.k_inv,
-                     P.v_inv);
+                     P.v_inv, P.v_format, P.block_bytes, P.ks_off);
   return hipGetLastError();
 }
 
@@ -377,7 +400,7 @@ hipError_t launch_dequant(const LaunchPool& P, int layer, int n_tok, const int64
   const int grid = (n_rows + 15) / 16;
   hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(grid), dim3(256), 0, stream, P.base, P.num_pages,
                      P.hkv, layer, n_rows, slots, k_out, v_out, dtype, unrotate && P.hadamard, P.hadamard,
-                     P.signs, P.k_scale, P.v_scale);
+                     P.signs, P.k_scale, P.v_scale, P.v_format, P.block_bytes, P.ks_off);
   return hipGetLastError();
 }
 

@@ -44,6 +44,8 @@ int check_pool_shape(const nvfp4kv_pool* p) {
   for (const float g : {p->k_scale, p->v_scale})
     if (g != 0.0f && !(g >= 0x1p-64f && g <= 0x1p64f))
       return fail(NVFP4KV_ERR_INVALID_ARG, "global scale %g out of range (0 = 1, else 2^-64..2^64)", (double)g);
+  if (p->v_format != 0 && p->v_format != 1)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "v_format must be 0 (NVFP4 V) or 1 (fp16 V) (got %d)", p->v_format);
   return NVFP4KV_OK;
 }
 
@@ -83,6 +85,9 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   L.base = reinterpret_cast<uint8_t*>(p->base);
   L.num_pages = p->num_pages;
   L.hkv = p->num_kv_heads;
+  L.v_format = p->v_format;
+  L.block_bytes = (int)nvfp4kv::pool_block_bytes(p->v_format);
+  L.ks_off = nvfp4kv::pool_kscale_off(p->v_format);
   L.rotary_dim = p->rotary_dim;
   L.hadamard = p->hadamard;
   for (int i = 0; i < 4; ++i) L.signs.w[i] = p->hadamard == 2 ? p->hadamard_signs[i] : 0u;
@@ -99,19 +104,19 @@ nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
 // thread computes the same value, so relaxed atomics suffice); if the device
 // cannot be queried (no GPU), 256 CUs x 8 (one tile) or 4 (several tiles) is
 // assumed so that size queries still work.
-int resident_decode_waves(int nt, bool packed) {
-  static std::atomic<int> cached[64][4][2];
+int resident_decode_waves(int nt, bool packed, bool vf16) {
+  static std::atomic<int> cached[64][4][3];
   const int fallback = nt > 1 ? 256 * 4 : 256 * 8;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
     return fallback;
   }
-  std::atomic<int>& slot = cached[dev][nt][packed ? 1 : 0];
+  std::atomic<int>& slot = cached[dev][nt][vf16 ? 2 : packed ? 1 : 0];
   int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0;
-    const int per_cu = nvfp4kv::decode_waves_per_cu(nt, packed);
+    const int per_cu = nvfp4kv::decode_waves_per_cu(nt, packed, vf16);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
       (void)hipGetLastError();
@@ -145,7 +150,7 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   const int64_t max_total = (int64_t)n_seq * p->num_kv_heads * max_pages;
   int64_t waves;
   if (pages_per_split == 0)
-    waves = resident_decode_waves(nvfp4kv::decode_column_tiles(group), group <= 8);
+    waves = resident_decode_waves(nvfp4kv::decode_column_tiles(group), group <= 8, p->v_format != 0);
   else
     waves = (max_total + pages_per_split - 1) / pages_per_split;
   waves = std::max<int64_t>(1, std::min<int64_t>(waves, std::min<int64_t>(max_total, (int64_t)1 << 24)));
@@ -167,9 +172,10 @@ extern "C" {
 
 size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p) {
   if (p == nullptr || p->num_pages <= 0 || p->num_layers <= 0 || p->num_kv_heads <= 0 ||
-      p->head_dim != 128 || p->page_size != 64)
+      p->head_dim != 128 || p->page_size != 64 || (p->v_format != 0 && p->v_format != 1))
     return 0;
-  return (size_t)p->num_layers * (size_t)p->num_pages * (size_t)p->num_kv_heads * (size_t)nvfp4kv::kPoolBlockBytes;
+  return (size_t)p->num_layers * (size_t)p->num_pages * (size_t)p->num_kv_heads *
+         nvfp4kv::pool_block_bytes(p->v_format);
 }
 
 int nvfp4kv_rope_table(double theta, int32_t rotary_dim, double pos_scale, int32_t max_pos,
@@ -247,6 +253,9 @@ static int check_decode(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
   if ((rc = check_dtype(q_dtype, "query")) != NVFP4KV_OK) return rc;
   if ((rc = make_plan(p, n_seq, n_q_heads, max_seq_len, pages_per_split, plan, max_group)) != NVFP4KV_OK) return rc;
+  if (p->v_format == 1 && plan->group > 8)
+    return fail(NVFP4KV_ERR_UNSUPPORTED, "fp16 V (v_format 1) takes up to 8 query heads per kv head (got %d)",
+                plan->group);
   if (q == nullptr || page_table == nullptr || seq_lens == nullptr)
     return fail(NVFP4KV_ERR_INVALID_ARG, "null q, page_table or seq_lens");
   if (!aligned(q, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "q must be 16-byte aligned");
@@ -412,6 +421,8 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
   g_last_error.clear();
   int rc;
   if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
+  if (p->v_format != 0)
+    return fail(NVFP4KV_ERR_UNSUPPORTED, "multi-token decode reads NVFP4 V only (v_format 0)");
   int cols = 0, per = 0;
   if ((rc = check_multi_shape(p, n_qtok, n_q_heads, &cols, &per)) != NVFP4KV_OK) return rc;
   nvfp4kv::DecodePlan full, last;
@@ -447,7 +458,7 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
 size_t nvfp4kv_page_bytes(const nvfp4kv_pool* p) {
   g_last_error.clear();
   if (check_pool_shape(p) != NVFP4KV_OK) return 0;
-  return (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::kPoolBlockBytes;
+  return (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::pool_block_bytes(p->v_format);
 }
 
 // Device address at which kernels reach `ptr`: device memory of the current
@@ -484,7 +495,7 @@ static int page_copy(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page
   if (n_pages == 0) return NVFP4KV_OK;
   if (page_ids == nullptr || arena == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null page_ids or arena");
   if (!aligned(arena, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "arena must be 16-byte aligned");
-  const size_t page = (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::kPoolBlockBytes;
+  const size_t page = (size_t)p->num_layers * (size_t)p->num_kv_heads * nvfp4kv::pool_block_bytes(p->v_format);
   if (arena_bytes / page < (size_t)n_pages)
     return fail(NVFP4KV_ERR_INVALID_ARG, "arena of %zu bytes holds fewer than %d pages of %zu bytes", arena_bytes, n_pages, page);
   uint8_t* ids_dev = nullptr;
@@ -515,6 +526,7 @@ int nvfp4kv_stream_read(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, con
   if ((rc = check_pool(p)) != NVFP4KV_OK) return rc;
   if ((rc = check_layer(p, layer)) != NVFP4KV_OK) return rc;
   if (n_seq <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq must be positive (got %d)", n_seq);
+  if (p->v_format != 0) return fail(NVFP4KV_ERR_UNSUPPORTED, "the read probe covers NVFP4 pools (v_format 0) only");
   if (n_waves <= 0 || n_waves > (1 << 24)) return fail(NVFP4KV_ERR_INVALID_ARG, "n_waves %d out of range (1..2^24)", n_waves);
   if (page_table == nullptr || seq_lens == nullptr || words == nullptr)
     return fail(NVFP4KV_ERR_INVALID_ARG, "null page_table, seq_lens or words");

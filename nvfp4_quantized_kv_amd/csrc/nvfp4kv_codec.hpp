@@ -26,6 +26,10 @@ constexpr int kKCodeOff = 0;
 constexpr int kVCodeOff = 4096;
 constexpr int kKScaleOff = 8192;
 constexpr int kVScaleOff = 8704;
+// Blocks of a pool that keeps V in fp16 (v_format 1): K codes as above, the
+// fp16 V tiles at kVCodeOff, then the K scales.
+constexpr int kBlockBytesF16V = 20992;
+constexpr int kKScaleOffF16V = 20480;
 
 // Byte offset, inside a block, of the 4-byte word holding code bytes
 // 4w .. 4w+3 of token t (w = 0..15).
@@ -34,6 +38,22 @@ __host__ __device__ inline uint32_t k_code_word_off(uint32_t t, uint32_t w) {
 }
 __host__ __device__ inline uint32_t v_code_word_off(uint32_t t, uint32_t w) {
   return kVCodeOff + (t / 4) * 256 + w * 16 + (t % 4) * 4;
+}
+
+// Byte offset, inside an fp16-V block, of V element d of token t.  Unit
+// u = t/32 of the page holds 8 tiles of 1 KB, tile j the dims d with
+// d % 8 == j; in a tile, the 16 bytes at 16 * (g4*16 + d/8) hold the eight
+// tokens 4*g4 + r and 16 + 4*g4 + r (r = 0..3) of the unit, in that order:
+// the A operand of one lane of the PV matrix instruction.
+__host__ __device__ inline uint32_t v16_off(uint32_t t, uint32_t d) {
+  return kVCodeOff + (t / 32) * 8192 + (d % 8) * 1024 + (((t % 16) / 4) * 16 + d / 8) * 16 +
+         ((t % 4) + 4 * ((t % 32) / 16)) * 2;
+}
+
+// binary16 bits of x, nearest with ties to even (the conversion instruction
+// rounds so in the default mode; overflow gives infinity).
+__device__ inline uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 // E4M3 code of the scale for a block with largest magnitude `amax`: the E4M3

@@ -6,8 +6,13 @@
 
 namespace nvfp4kv {
 
-// Bytes of one (layer, page, kv head) block: 64 tokens x (K, V) x (64 code + 8 scale bytes).
+// Bytes of one (layer, page, kv head) block: 64 tokens x (K, V) x (64 code +
+// 8 scale bytes) with NVFP4 V; 64 x (64 + 8 + 256) with fp16 V.
 constexpr size_t kPoolBlockBytes = 9216;
+constexpr size_t kPoolBlockBytesF16V = 20992;
+inline size_t pool_block_bytes(int v_format) { return v_format ? kPoolBlockBytesF16V : kPoolBlockBytes; }
+// K scales' offset inside a block (the codes and the fp16 V tiles come first)
+inline int pool_kscale_off(int v_format) { return v_format ? 20480 : 8192; }
 
 // Element mask of the randomized rotation (hadamard 2): element j of a K or
 // Q row is negated before the transform when bit j % 32 of word j / 32 is set.
@@ -28,6 +33,9 @@ struct LaunchPool {
   uint8_t* base;
   int64_t num_pages;
   int hkv;
+  int v_format;             // 0: NVFP4 V; 1: fp16 V
+  int block_bytes;          // bytes of one (layer, page, kv head) block
+  int ks_off;               // K scales' offset in a block
   int rotary_dim;
   int hadamard;
   SignMask signs;
@@ -70,8 +78,8 @@ inline int decode_column_tiles(int group) { return (group + 15) / 16; }
 
 // Resident one-wavefront decode workgroups per CU for the kernels with `nt`
 // column tiles, for one tile those of packed groups (up to 8 query columns)
-// or the others (0 if the query fails).
-int decode_waves_per_cu(int nt, bool packed);
+// or the others, or the fp16-V kernel (0 if the query fails).
+int decode_waves_per_cu(int nt, bool packed, bool vf16);
 
 hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* k, const void* v,
                          int dtype, const int64_t* slots, const int32_t* positions,

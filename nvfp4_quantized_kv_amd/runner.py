@@ -19,14 +19,14 @@ from . import workloads as W
 
 class DecodeStep:
     def __init__(self, wl: W.Workload, device="cuda", pages_per_split: int = 0,
-                 fill_chunk: int = 1 << 16, signs=(0, 0, 0, 0)):
+                 fill_chunk: int = 1 << 16, signs=(0, 0, 0, 0), v_format: int = 0):
         self.wl = wl
         self.device = device
         self.pages_per_split = pages_per_split
         table, num_pages = W.page_table(wl)
         self.table_np = table
         self.pool = Pool.allocate(num_pages, wl.layers, wl.hkv, wl.rotary_dim, int(wl.hadamard), device,
-                                  signs=signs)
+                                  signs=signs, v_format=v_format)
         self.pool.data.zero_()
         self.table = torch.from_numpy(table).to(device)
         self.seq_lens = torch.tensor(wl.seq_lens, dtype=torch.int32, device=device)

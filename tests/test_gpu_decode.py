@@ -36,13 +36,14 @@ class Case:
 
     def __init__(self, seed, lens, hkv, hq, rotary=32, hadamard=True, pos_scale=1.0,
                  dtype=torch.bfloat16, outliers=3, outlier_scale=16.0, extra_pages=3,
-                 student_t=False, hold_last=False, k_scale=1.0, v_scale=1.0):
+                 student_t=False, hold_last=False, k_scale=1.0, v_scale=1.0, v_format=0):
         import nvfp4_quantized_kv_amd as kv
         self.kv = kv
         rng = np.random.default_rng(seed)
         self.lens = list(lens)
         self.hkv, self.hq, self.rotary, self.hadamard = hkv, hq, rotary, int(hadamard)
         self.k_scale, self.v_scale = k_scale, v_scale
+        self.v_format = v_format
         # hadamard 2: the randomized rotation's element mask, drawn here
         self.signs = (rng.integers(0, 2 ** 32, 4, dtype=np.uint64).astype(np.uint32)
                       if self.hadamard == 2 else None)
@@ -69,7 +70,7 @@ class Case:
         self.max_pos = max(lens) + 1
         self.pool = kv.Pool.allocate(self.num_pages, 1, hkv, rotary, hadamard,
                                      signs=tuple(self.signs) if self.signs is not None else (0, 0, 0, 0),
-                                     k_scale=k_scale, v_scale=v_scale)
+                                     k_scale=k_scale, v_scale=v_scale, v_format=v_format)
         # stale bytes: 0x7F in every byte never written.  The decode kernels
         # clear scale sign bits, so these read as finite values (scale 1.875,
         # codes +-6): a masking mistake shows as an error, not as NaN
@@ -120,7 +121,7 @@ class Case:
         return oracle.decode_attention(pool, self.num_pages, self.hkv, 0, self.rotary, self.hadamard,
                                        self.q.float().numpy(), self.q_pos, self.table, self.lens,
                                        sm_scale, self.oc, self.os, signs=self.signs, k_scale=self.k_scale,
-                                       v_scale=self.v_scale)
+                                       v_scale=self.v_scale, v_format=self.v_format)
 
 
 def test_decode_tiny_workload():
@@ -234,7 +235,7 @@ def oracle_pool(c):
         sl = c.table[n, pos // 64].astype(np.int64) * 64 + pos % 64
         oracle.append(pool, c.num_pages, c.hkv, c.rotary, c.hadamard, 0, c.k[n].float().numpy(),
                       c.v[n].float().numpy(), sl, pos.astype(np.int32), c.oc, c.os, signs=c.signs,
-                      k_scale=c.k_scale, v_scale=c.v_scale)
+                      k_scale=c.k_scale, v_scale=c.v_scale, v_format=c.v_format)
     return pool
 
 
