@@ -428,7 +428,7 @@ __device__ __forceinline__ void append_new_token(
 
 __device__ inline float row_ror8(float x) {
   // the value of lane (c16 + 8) % 16 of the same 16-lane row
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true));
 }
 
 // Partial (m, l, acc) of the columns col0 .. col0 + 15 (those below
@@ -446,7 +446,7 @@ __device__ __forceinline__ void write_partial(const f4 (&acc)[8], float m_ref, f
       // column h += column h + 8 (high + low parts of the weights)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        o[j][i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[j][i]), 0x128, 0xF, 0xF, false));
+        o[j][i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(acc[j][i]), 0x128, 0xF, 0xF, true));
     }
   }
   float l_tot = sum4lanes(l_run);
@@ -635,8 +635,8 @@ __device__ __forceinline__ void pair_operands(const float (&P)[8], bool upper, h
     const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(fmaf(-1.0f, (float)hi[0], x),
                                                                    fmaf(-1.0f, (float)hi[1], y)));
     const uint32_t hb = __builtin_bit_cast(uint32_t, hi), lb = __builtin_bit_cast(uint32_t, lo);
-    const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hb, 0x128, 0xF, 0xF, false);
-    const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lb, 0x128, 0xF, 0xF, false);
+    const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hb, 0x128, 0xF, 0xF, true);
+    const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lb, 0x128, 0xF, 0xF, true);
     ua[s2] = upper ? lr : hb;
     ub[s2] = upper ? lb : hr;
   }
@@ -790,10 +790,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   const int kvh0 = (int)((a - seq_base) / pg);
   const int seg0 = seq * hkv + kvh0;
 
-  // ---- page window: lane i describes flat page win + i of the range
-  int64_t win = a;
+  // ---- page window: lane i describes flat page a + wo + i of the range.
+  // Pages of the range are counted from a in 32 bits (npg < 2^30, checked
+  // on the host), so the loop's bookkeeping is scalar arithmetic.
+  const int npg = (int)(b - a);
+  int wo = 0;
   int w_blk, w_nv, w_j, w_sg;
   auto load_window = [&](int wseq, int wkvh, int64_t wstart, int64_t wpg) {
+    const int64_t win = a + wo;
     int lseq = wseq, lkvh = wkvh;
     int64_t lstart = wstart, lpg = wpg;
     const int64_t x = min(win + lane, b - 1);
@@ -818,19 +822,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   constexpr int kKS = VF16 ? kKScaleOffF16V : kKScaleOff;     // K scales in a block
   const uint8_t* layer_base =
       pool + (size_t)layer * (size_t)num_pages * (size_t)hkv * (size_t)kBB;
-  // buffer resource of flat page x (empty past the range)
-  auto rsrc_of = [&](int64_t x) {
-    const bool ok = x < b;
-    const int blk = __builtin_amdgcn_readlane(w_blk, (int)((ok ? x : b - 1) - win));
+  // buffer resource of page a + i of the range (empty past the range)
+  auto rsrc_of = [&](int i) {
+    const bool ok = i < npg;
+    const int blk = __builtin_amdgcn_readlane(w_blk, (ok ? i : npg - 1) - wo);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(layer_base + (size_t)blk * kBB),
                                              0, ok ? kBB : 0, 0x00020000);
   };
-  auto nvalid_of = [&](int64_t x) {
-    return x < b ? __builtin_amdgcn_readlane(w_nv, (int)(x - win)) : 0;
+  auto nvalid_of = [&](int i) {
+    return i < npg ? __builtin_amdgcn_readlane(w_nv, i - wo) : 0;
   };
   // first page of a segment other than page a's
-  auto starts_segment = [&](int64_t x) {
-    return x < b && __builtin_amdgcn_readlane(w_j, (int)(x - win)) == 0;
+  auto starts_segment = [&](int i) {
+    return i < npg && __builtin_amdgcn_readlane(w_j, i - wo) == 0;
   };
 
   // query inputs of the range's first segment, and of the second when the
@@ -927,7 +931,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   const int e_own = PACKED ? g4 * 8 + (c16 & 7) : lane;
   const int e_lo = (kPageSoftmax && c16 >= 8) ? kQE - 1 : e_own;
   const int e_hi = c16 >= 8 ? e_own : kQE - 1;
-  auto seg_of = [&](int64_t x) { return __builtin_amdgcn_readlane(w_sg, (int)(min(x, b - 1) - win)); };
+  auto seg_of = [&](int i) { return __builtin_amdgcn_readlane(w_sg, min(i, npg - 1) - wo); };
 
   // ---- prologue: loads of the range's first two pages; unit 0's scores and
   // weights; the loads left in flight and their order are those of the
@@ -937,7 +941,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   u4 vH[VF16 ? 16 : 1];   // fp16 V of a page: units 0 and 1, 8 dim tiles each
   if constexpr (kPageSoftmax) {
     // one register set, loads one page ahead: page a's scales, K and V
-    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a);
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(0);
     sA = ld16(r0, voff, kKS);
     kA[0] = ld16(r0, voff, 0);
     kA[1] = ld16(r0, voff, 1024);
@@ -954,7 +958,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     }
     __builtin_amdgcn_sched_barrier(0);
   } else {
-    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(a), r1 = rsrc_of(a + 1);
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_of(0), r1 = rsrc_of(1);
     sA = ld16(r0, voff, kKScaleOff);
     kA[0] = ld16(r0, voff, 0);
     kA[1] = ld16(r0, voff, 1024);
@@ -993,7 +997,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   if constexpr (kPageSoftmax) {
     // page a staged and scored (both units); its scales in buffer 0, then
     // page a+1's scales and K on their way
-    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(1);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r1, voff, kKS);
     const uint8_t* sb = reinterpret_cast<const uint8_t*>(&sc_lds[0][0]);
@@ -1008,7 +1012,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     __builtin_amdgcn_sched_barrier(0);
   } else {
   {
-    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(a + 1), r2 = rsrc_of(a + 2);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(1), r2 = rsrc_of(2);
     sc_lds[0][lane] = sA & 0x7F7F7F7Fu;
     sA = ld16(r2, voff, kKScaleOff);
     q_of(seg0, qb, e_lo);
@@ -1021,7 +1025,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     // (one-tile groups of up to 8 heads take the softmax a page at a time,
     // in the loop: page a's first unit stays scored, not yet weighted)
     if (!kPageSoftmax)
-      softmax_pick<PACKED, NT>(nvalid_of(a), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
+      softmax_pick<PACKED, NT>(nvalid_of(0), 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,
                                pw0, pw1, false, group, ws_acc, ws_ml, st, cut);
   }
 
@@ -1036,8 +1040,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // lower issue rate.  Dropping the priority as the range is worked off
   // (below 50 % done: 3, then 2, 1 from 75 %, 0 from 90 %) hands the issue
   // slots to whichever wavefront is behind.
-  const int64_t t50 = a + (b - a) / 2, t75 = a + 3 * (b - a) / 4, t90 = a + 9 * (b - a) / 10;
-  int prio_level = 0;
+  const int t50 = npg / 2, t75 = (int)(3 * (int64_t)npg / 4), t90 = (int)(9 * (int64_t)npg / 10);
   if constexpr (kPageSoftmax) {
   // One-tile groups of up to 8 heads: the softmax covers a page (two units)
   // at once, and a page is one block of the software pipeline, its loads
@@ -1049,27 +1052,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   // p's V codes and page p+1's K codes and scales, in flight.  pa/pb are
   // the weight operands of page p's two units.
   h8 pa, pb;
-  for (int64_t p = a; p < b; ++p) {
-    {
-      const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
-      if (lv != prio_level) {
-        prio_level = lv;
-        if (lv == 1) __builtin_amdgcn_s_setprio(2);
-        else if (lv == 2) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-      }
+  int next_prio = t50;   // page index of the next priority step
+  for (int i = 0; i < npg; ++i) {
+    if (__builtin_expect(i >= next_prio, 0)) {
+      const int lv = i >= t90 ? 3 : i >= t75 ? 2 : 1;
+      if (lv == 1) __builtin_amdgcn_s_setprio(2);
+      else if (lv == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      next_prio = lv == 1 ? t75 : lv == 2 ? t90 : npg;
     }
-    if (min(p + 2, b - 1) - win >= 64) {   // ranges of more than 64 pages
-      const int o = (int)(p - win);
+    if (min(i + 2, npg - 1) - wo >= 64) {   // ranges of more than 64 pages
+      const int o = i - wo;
       const int sg = __builtin_amdgcn_readlane(w_sg, o);
       const int j = __builtin_amdgcn_readlane(w_j, o);
-      win = p;
-      load_window(sg / hkv, sg % hkv, p - j, seq_pages(seq_lens, sg / hkv));
+      wo = i;
+      load_window(sg / hkv, sg % hkv, a + i - j, seq_pages(seq_lens, sg / hkv));
     }
-    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(p + 1), r2 = rsrc_of(p + 2);
-    const int nv = nvalid_of(p);
-    const bool sw = p > a && starts_segment(p);
-    const int sg1 = seg_of(p + 1);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_of(i + 1), r2 = rsrc_of(i + 2);
+    const int nv = nvalid_of(i);
+    const bool sw = i > 0 && starts_segment(i);
+    const int sg1 = seg_of(i + 1);
     // query operands of a segment that starts at page p+1 (rare)
     while (q_ready < sg1) {
       ++q_ready;
@@ -1079,7 +1081,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
       make_q_operands<PACKED, kPasses, MQ, NT>(in, group, rotary_dim, rope_cos, rope_sin, hadamard, signs,
                                                qrow, q_lds[(q_ready - seg0) % kQSlots]);
     }
-    const int cur = (int)((p - a) & 1);
+    const int cur = i & 1;
     const uint8_t* sb_cur = reinterpret_cast<const uint8_t*>(&sc_lds[cur][0]);
     const uint8_t* sb_nxt = reinterpret_cast<const uint8_t*>(&sc_lds[cur ^ 1][0]);
     // page p+1's scales staged, page p+2's on their way
@@ -1124,27 +1126,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     write_partial<PACKED, kPageSoftmax>(acc[t], m_ref[t], l_run[t], c16, g4, group, ws_acc, ws_ml, st.slot, 16 * t);
   return;
   } else {
-  for (int64_t p = a; p < b; p += 2) {
-    {
-      const int lv = p >= t90 ? 3 : p >= t75 ? 2 : p >= t50 ? 1 : 0;
-      if (lv != prio_level) {
-        prio_level = lv;
-        if (lv == 1) __builtin_amdgcn_s_setprio(2);
-        else if (lv == 2) __builtin_amdgcn_s_setprio(1);
-        else __builtin_amdgcn_s_setprio(0);
-      }
+  int next_prio = t50;
+  for (int i = 0; i < npg; i += 2) {
+    if (__builtin_expect(i >= next_prio, 0)) {
+      const int lv = i >= t90 ? 3 : i >= t75 ? 2 : 1;
+      if (lv == 1) __builtin_amdgcn_s_setprio(2);
+      else if (lv == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+      next_prio = lv == 1 ? t75 : lv == 2 ? t90 : npg;
     }
-    if (min(p + 4, b - 1) - win >= 64) {   // ranges of more than 64 pages
-      const int o = (int)(p - win);
+    if (min(i + 4, npg - 1) - wo >= 64) {   // ranges of more than 64 pages
+      const int o = i - wo;
       const int sg = __builtin_amdgcn_readlane(w_sg, o);
       const int j = __builtin_amdgcn_readlane(w_j, o);
-      win = p;
-      load_window(sg / hkv, sg % hkv, p - j, seq_pages(seq_lens, sg / hkv));
+      wo = i;
+      load_window(sg / hkv, sg % hkv, a + i - j, seq_pages(seq_lens, sg / hkv));
     }
-    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(p + 2), r3 = rsrc_of(p + 3), r4 = rsrc_of(p + 4);
-    const int nv0 = nvalid_of(p), nv1 = nvalid_of(p + 1), nv2 = nvalid_of(p + 2);
-    const bool sw1 = starts_segment(p + 1), sw2 = starts_segment(p + 2);
-    const int sg0 = seg_of(p), sg1 = seg_of(p + 1), sg2 = seg_of(p + 2);
+    const __amdgpu_buffer_rsrc_t r2 = rsrc_of(i + 2), r3 = rsrc_of(i + 3), r4 = rsrc_of(i + 4);
+    const int nv0 = nvalid_of(i), nv1 = nvalid_of(i + 1), nv2 = nvalid_of(i + 2);
+    const bool sw1 = starts_segment(i + 1), sw2 = starts_segment(i + 2);
+    const int sg0 = seg_of(i), sg1 = seg_of(i + 1), sg2 = seg_of(i + 2);
     // query operands of segments that start in this trip (rare: a range
     // crosses few segment boundaries)
     while (q_ready < sg2) {
@@ -1205,7 +1206,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     // the rest of the trip to the general path below, which picks up at
     // that unit.  Either way the loads go out in the same order.
     const bool regular =
-        !sw1 && !sw2 && nv0 >= 64 + mcut && nv1 >= 64 + mcut && nv2 >= 32 + mcut && p + 1 < b;
+        !sw1 && !sw2 && nv0 >= 64 + mcut && nv1 >= 64 + mcut && nv2 >= 32 + mcut && i + 1 < npg;
     int bail = 0;
     if (__builtin_expect(regular, 1)) {
       blk1();
@@ -1227,7 +1228,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     if (bail <= 2)
       softmax_pick<PACKED, NT>(nv1, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run, pw0,
                                   pw1, sw1, group, ws_acc, ws_ml, st, cut);
-    if (p + 1 >= b) break;
+    if (i + 1 >= npg) break;
     if (bail < 3) blk3();
     if (bail <= 3)
       softmax_pick<PACKED, NT>(nv1 - 32, 32 + mcut, S, g4, c16, c_log2, lo_mask, acc, m_ref, l_run,

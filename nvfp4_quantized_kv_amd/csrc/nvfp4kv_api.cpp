@@ -154,6 +154,10 @@ int make_plan(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_q_heads, int64_t m
   else
     waves = (max_total + pages_per_split - 1) / pages_per_split;
   waves = std::max<int64_t>(1, std::min<int64_t>(waves, std::min<int64_t>(max_total, (int64_t)1 << 24)));
+  // the decode kernels count a wavefront's pages in 32 bits
+  if ((max_total + (int64_t)5 * n_seq * p->num_kv_heads) / waves + 2 >= ((int64_t)1 << 30))
+    return fail(NVFP4KV_ERR_UNSUPPORTED, "%lld pages over %lld wavefronts: too many pages per wavefront",
+                (long long)max_total, (long long)waves);
   out->n_waves = (int)waves;
   out->group = group;
   return NVFP4KV_OK;
