@@ -80,7 +80,10 @@ typedef struct {
     int32_t num_kv_heads;   /* >= 1 */
     int32_t head_dim;       /* must be 128 */
     int32_t page_size;      /* must be 64 */
-    int32_t rotary_dim;     /* RoPE dims at the head's start: 0..128, a multiple of 16 */
+    int32_t rotary_dim;     /* RoPE dims at the head's start: 0..128, even (pairs
+                               i, i + rotary_dim/2); a multiple of 16 takes
+                               the faster rotation, other even widths are
+                               exact too */
     int32_t hadamard;       /* 1: rotate K and Q before quantizing; 0: do not;
                                2: rotate after negating the elements marked in
                                hadamard_signs (a randomized rotation, a variant

@@ -89,8 +89,16 @@ struct RopeLane {
   int src;   // the lane of the row holding the partner elements
 };
 
+// Rotary widths that are not a multiple of 16: coefficients element by
+// element (rope_coeffs), the rotation by rope_rows_any.
 __device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* cos_row, const float* sin_row,
                                           RopeLane& rl) {
+  if ((rotary_dim & 15) != 0) {
+    rope_coeffs(r, rotary_dim, cos_row, sin_row, rl.cv, rl.sv);
+    rl.first = rl.in_rot = false;
+    rl.src = r;
+    return;
+  }
   const int half = rotary_dim / 2;          // a multiple of 8
   const int hl = half / 8;                  // lanes per half
   rl.first = r < hl;
@@ -111,11 +119,14 @@ __device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* co
 // read beforehand (`rl`, used when `rope`), RoPE without branches, the
 // transform's cross-lane stages through DPP and the E2M1 code by search.
 // All 16 lanes of a row must call it together.
-__device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, const RopeLane& rl,
-                                             bool hadamard, uint32_t neg, uint32_t& codes, uint32_t& scode) {
+__device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, int rotary_dim,
+                                             const RopeLane& rl, bool hadamard, uint32_t neg, uint32_t& codes,
+                                             uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
-  if (rope) {
+  if (rope && (rotary_dim & 15) != 0) {
+    rope_rows_any(x, r, rotary_dim / 2, rl.cv, rl.sv);
+  } else if (rope) {
     const int src_lane = (lane & ~15) + rl.src;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
       }
     } else {
       uint32_t codes, scode;
-      append_row16(x, r, rot > 0, rl, had, neg, codes, scode);
+      append_row16(x, r, rot > 0, rot, rl, had, neg, codes, scode);
       if (active) {
         const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
         *reinterpret_cast<uint32_t*>(blk + woff) = codes;

@@ -38,8 +38,8 @@ int check_pool_shape(const nvfp4kv_pool* p) {
   if (p->num_pages <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_pages must be positive (got %lld)", (long long)p->num_pages);
   if (p->num_layers <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_layers must be positive (got %d)", p->num_layers);
   if (p->num_kv_heads <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", p->num_kv_heads);
-  if (p->rotary_dim < 0 || p->rotary_dim > 128 || p->rotary_dim % 16 != 0)
-    return fail(NVFP4KV_ERR_UNSUPPORTED, "rotary_dim %d unsupported (0..128, multiple of 16)", p->rotary_dim);
+  if (p->rotary_dim < 0 || p->rotary_dim > 128 || p->rotary_dim % 2 != 0)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim %d invalid (even, 0..128)", p->rotary_dim);
   if (p->hadamard < 0 || p->hadamard > 2) return fail(NVFP4KV_ERR_INVALID_ARG, "hadamard must be 0, 1 or 2 (got %d)", p->hadamard);
   for (const float g : {p->k_scale, p->v_scale})
     if (g != 0.0f && !(g >= 0x1p-64f && g <= 0x1p64f))

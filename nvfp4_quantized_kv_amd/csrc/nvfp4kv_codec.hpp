@@ -124,19 +124,70 @@ __device__ inline void load8(const void* src, int dtype, size_t elem_off, float 
 }
 
 // RoPE coefficients of a lane's 8 elements for quant_row16_v: lane r of a
-// row covers elements 8r .. 8r+7; in the first half of the rotary part (i <
-// R/2) it needs cos/sin of pair i, in the second half those of pair i - R/2,
-// beyond the rotary part nothing (zeros are returned, and not used).
+// row covers elements e = 8r .. 8r+7; in the first half of the rotary part
+// (e < R/2) it needs cos/sin of pair e, in the second half those of pair
+// e - R/2, beyond the rotary part nothing (zeros are returned, and not used).
+// Any even R.
 __device__ inline void rope_coeffs(int r, int rotary_dim, const float* cos_row, const float* sin_row,
                                    float (&cv)[8], float (&sv)[8]) {
-  const int half = rotary_dim / 2;          // a multiple of 8
-  const int hl = half / 8;                  // lanes per half
-  const bool in_rot = r < 2 * hl;
-  const int base = in_rot ? (r < hl ? 8 * r : 8 * r - half) : 0;
+  const int half = rotary_dim / 2;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    cv[k] = in_rot ? cos_row[base + k] : 0.0f;
-    sv[k] = in_rot ? sin_row[base + k] : 0.0f;
+    const int e = 8 * r + k;
+    const int idx = e < half ? e : e - half;
+    cv[k] = e < rotary_dim ? cos_row[idx] : 0.0f;
+    sv[k] = e < rotary_dim ? sin_row[idx] : 0.0f;
+  }
+}
+
+// Rotate-half RoPE on a row held 8 elements per lane by a 16-lane row, for a
+// half-width R/2 = 8*hl + D that is not a multiple of 8.  Element e = 8r + k
+// pairs with e + R/2 (first half) or e - R/2 (second half): element
+// (k + D) % 8 of lane r + hl (+1 when k + D >= 8), or element (k - D) % 8 of
+// lane r - hl (-1 when k < D).  D is a template argument, so the registers
+// exchanged are fixed; both partners are fetched for every element (every
+// lane takes part in every shuffle) and the element's own half picks one.
+// Each product and each sum is rounded on its own, as in quant_row16_v.
+template <int D>
+__device__ __forceinline__ void rope_rows_general(float (&x)[8], int r, int half, const float (&cv)[8],
+                                                  const float (&sv)[8]) {
+#pragma clang fp contract(off)
+  const int base = (int)__lane_id() & ~15;
+  const int hl = half >> 3;
+  float fw[8], bw[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int lf = min(r + hl + ((k + D) >> 3), 15);       // lanes past the row are not used
+    const int lb = max(r - hl - (k < D ? 1 : 0), 0);
+    fw[k] = __shfl(x[(k + D) & 7], base + lf, 64);
+    bw[k] = __shfl(x[(k + 8 - D) & 7], base + lb, 64);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e = 8 * r + k;
+    if (e < half) {
+      const float ac = x[k] * cv[k];
+      const float bs = fw[k] * sv[k];
+      x[k] = ac - bs;
+    } else if (e < 2 * half) {
+      const float bc = x[k] * cv[k];
+      const float as = bw[k] * sv[k];
+      x[k] = bc + as;
+    }
+  }
+}
+
+// rope_rows_general for D = half % 8 in 1..7.
+__device__ __forceinline__ void rope_rows_any(float (&x)[8], int r, int half, const float (&cv)[8],
+                                              const float (&sv)[8]) {
+  switch (half & 7) {
+    case 1: rope_rows_general<1>(x, r, half, cv, sv); break;
+    case 2: rope_rows_general<2>(x, r, half, cv, sv); break;
+    case 3: rope_rows_general<3>(x, r, half, cv, sv); break;
+    case 4: rope_rows_general<4>(x, r, half, cv, sv); break;
+    case 5: rope_rows_general<5>(x, r, half, cv, sv); break;
+    case 6: rope_rows_general<6>(x, r, half, cv, sv); break;
+    default: rope_rows_general<7>(x, r, half, cv, sv); break;
   }
 }
 
@@ -155,7 +206,9 @@ __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
   // RoPE, rotate-half pairs (i, i + R/2) on the first R dims.
-  if (rotary_dim > 0) {
+  if (rotary_dim > 0 && (rotary_dim & 15) != 0) {
+    rope_rows_any(x, r, rotary_dim / 2, cv, sv);
+  } else if (rotary_dim > 0) {
     const int half = rotary_dim / 2;
     const int hl = half / 8;
     const bool first = r < hl;

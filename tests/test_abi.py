@@ -71,10 +71,12 @@ def _append(kv, d, layer=0, n_tok=4, k=4096, v=4096, dtype=1, slots=4096, pos=40
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(rotary_dim=24), -2),
-    (dict(rotary_dim=-16), -2), (dict(hadamard=3), -1), (dict(num_pages=0), -1),
+    (dict(head_dim=64), -2), (dict(page_size=32), -2), (dict(rotary_dim=23), -1),
+    (dict(rotary_dim=-16), -1), (dict(rotary_dim=130), -1), (dict(hadamard=3), -1), (dict(num_pages=0), -1),
     (dict(num_kv_heads=0), -1), (dict(base=0), -1), (dict(base=4100), -1)])
 def test_append_rejects_bad_pool(kv, over, code):
+    """Bad descriptors are refused before any launch (rotary widths: any even
+    width from 0 to 128 is accepted, an odd or out-of-range one is not)."""
     assert _append(kv, _desc(kv, **over)) == code
     assert kv.nvfp4kv_last_error() != ""
 

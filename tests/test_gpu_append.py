@@ -88,7 +88,10 @@ def test_append_layer8k_bitexact():
 
 @pytest.mark.parametrize("rotary,hadamard,dtype", [
     (0, False, np.float32), (16, True, np.float32), (32, True, "bf16"), (64, False, "bf16"),
-    (128, True, np.float32), (48, True, np.float32), (112, True, "bf16"), (32, 2, "bf16"), (0, 2, np.float32)])
+    (128, True, np.float32), (48, True, np.float32), (112, True, "bf16"), (32, 2, "bf16"), (0, 2, np.float32),
+    # even widths that are not multiples of 16 (pairs split across lanes at every in-lane offset)
+    (2, True, np.float32), (8, True, "bf16"), (14, False, np.float32), (24, True, "bf16"), (40, True, np.float32),
+    (50, 2, "bf16"), (86, True, np.float32), (126, True, "bf16"), (6, True, np.float32), (108, False, "bf16")])
 def test_append_shapes_and_flags_bitexact(rotary, hadamard, dtype):
     """hadamard 2: the randomized rotation, with a drawn element mask."""
     rng = np.random.default_rng(rotary * 7 + int(hadamard))

@@ -152,7 +152,8 @@ def test_decode_group_sizes(group):
 
 @pytest.mark.parametrize("hadamard,rotary,pos_scale", [(False, 32, 2.3), (True, 32, 2.3), (True, 0, 1.0),
                                                         (True, 128, 1.0), (False, 0, 1.0), (2, 32, 2.3),
-                                                        (2, 0, 1.0)])
+                                                        (2, 0, 1.0), (True, 24, 2.3), (True, 50, 1.0),
+                                                        (2, 10, 1.0)])
 def test_decode_flags(hadamard, rotary, pos_scale):
     c = Case(7, [3000, 1234], 4, 24, rotary=rotary, hadamard=hadamard, pos_scale=pos_scale,
              outlier_scale=32.0)
@@ -223,6 +224,8 @@ FUSED_CASES = [
     dict(lens=[700, 1500], hq=32, rotary=16),         # 16 query heads per kv head
     dict(lens=[3000, 1234], rotary=128, pos_scale=2.3),
     dict(lens=[1000, 130], hadamard=2),               # randomized rotation of the new K and of Q
+    dict(lens=[700, 65], rotary=24, pos_scale=2.3),  # a rotary width that is not a multiple of 16
+    dict(lens=[300, 64], rotary=126, hadamard=2),
 ]
 
 

@@ -54,6 +54,7 @@ MULTI_CASES = [
     ([2500, 90], 2, 2, 40, 32),        # 1 head: 40 tokens, three tiles; causal cut over a page
     ([777, 1300], 2, 8, 5, 32),        # 4 heads: 20 columns, two tiles
     ([5000, 64], 1, 1, 64, 32),        # 64 tokens: launches of 48 and 16; a 64-token sequence
+    ([1300, 90], 4, 24, 8, 24),        # RoPE width not a multiple of 16 (per-token query positions)
 ]
 
 @pytest.mark.parametrize("idx", range(len(MULTI_CASES)))
