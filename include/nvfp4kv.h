@@ -349,6 +349,35 @@ int nvfp4kv_stream_read(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, con
                         int32_t page_table_stride, const int32_t* seq_lens, int32_t n_waves, uint32_t* words,
                         hipStream_t stream);
 
+/* Range checks of the device-side tables that the entry points above trust
+ * (the header's conventions: slots, page ids, positions and sequence lengths
+ * are not checked on the device), run on HOST copies of them.  A caller may
+ * run them itself; the checked build of the library (libnvfp4kv_debug.so,
+ * compiled with NVFP4KV_DEBUG=1) runs them inside every entry point on
+ * copies it takes on the call's stream (which synchronizes that stream)
+ * before anything is launched.  Each returns NVFP4KV_OK, or
+ * NVFP4KV_ERR_INVALID_ARG with a message naming the first offending index
+ * (nvfp4kv_last_error).  The release post's section "Also included" lists a
+ * use-after-free that a missing stream synchronization caused: the checked
+ * build is the tool for catching a bad table before a kernel reads with it.
+ *   nvfp4kv_check_decode_tables: for each sequence n, n_qtok <= seq_lens[n]
+ *       <= max_seq_len and page_table[n][j] in [0, num_pages) for the
+ *       ceil(seq_lens[n] / 64) pages it uses; with rotary_dim > 0 and
+ *       q_positions given, the n_seq * n_qtok positions in [0, max_pos)
+ *   nvfp4kv_check_slots: slots in [0, num_pages * 64) and pairwise distinct
+ *       (equal slots in one append race); with rotary_dim > 0 and positions
+ *       given, positions in [0, max_pos)
+ *   nvfp4kv_check_page_ids: with `distinct` (a restore), no page id inside
+ *       the pool listed twice (ids outside the pool are skipped by contract)
+ * nvfp4kv_checked_build returns 1 in the checked build, 0 otherwise. */
+int nvfp4kv_check_decode_tables(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok, const int32_t* page_table,
+                                int32_t page_table_stride, const int32_t* seq_lens, int64_t max_seq_len,
+                                const int32_t* q_positions, int32_t max_pos);
+int nvfp4kv_check_slots(const nvfp4kv_pool* p, int32_t n_tok, const int64_t* slots, const int32_t* positions,
+                        int32_t max_pos);
+int nvfp4kv_check_page_ids(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids, int32_t distinct);
+int nvfp4kv_checked_build(void);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on the same thread.  Not a step of the method: every entry
  * point reports failure as a status code and this message instead of

@@ -17,7 +17,10 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libnvfp4kv.so")
+# NVFP4KV_DEBUG=1 loads the checked build (device-side tables range-checked
+# on the host before every launch); NVFP4KV_LIB names another build outright
+LIB_PATH = os.environ.get("NVFP4KV_LIB") or os.path.join(
+    _PKG, "libnvfp4kv_debug.so" if os.environ.get("NVFP4KV_DEBUG", "0") not in ("", "0") else "libnvfp4kv.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
@@ -49,10 +52,8 @@ class _PoolDesc(ctypes.Structure):
     ]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m nvfp4_quantized_kv_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """ctypes signatures of the C entry points on a loaded build."""
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     PD = ctypes.POINTER(_PoolDesc)
     L.nvfp4kv_pool_bytes.argtypes = [PD]
@@ -93,17 +94,33 @@ def _load():
     L.nvfp4kv_last_error.restype = ctypes.c_char_p
     L.nvfp4kv_version.argtypes = []
     L.nvfp4kv_version.restype = ctypes.c_char_p
+    L.nvfp4kv_check_decode_tables.argtypes = [PD, i32, i32, P, i32, P, i64, P, i32]
+    L.nvfp4kv_check_decode_tables.restype = ctypes.c_int
+    L.nvfp4kv_check_slots.argtypes = [PD, i32, P, P, i32]
+    L.nvfp4kv_check_slots.restype = ctypes.c_int
+    L.nvfp4kv_check_page_ids.argtypes = [PD, i32, P, i32]
+    L.nvfp4kv_check_page_ids.restype = ctypes.c_int
+    L.nvfp4kv_checked_build.argtypes = []
+    L.nvfp4kv_checked_build.restype = ctypes.c_int
     return L
 
 
-_lib = _load()
+def load_build(path: str) -> ctypes.CDLL:
+    """Load a build of the library (e.g. the checked one) with its signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m nvfp4_quantized_kv_amd.build`")
+    return _declare(ctypes.CDLL(path))
+
+
+_lib = load_build(LIB_PATH)
 
 EXPORTED = ["nvfp4kv_pool_bytes", "nvfp4kv_rope_table", "nvfp4kv_append",
             "nvfp4kv_decode_workspace_bytes", "nvfp4kv_decode_attn", "nvfp4kv_decode_attn_static",
             "nvfp4kv_decode_attn_splits",
             "nvfp4kv_decode_reduce", "nvfp4kv_decode_multi_workspace_bytes", "nvfp4kv_decode_attn_multi",
             "nvfp4kv_dequant", "nvfp4kv_page_bytes", "nvfp4kv_spill_pages", "nvfp4kv_restore_pages",
-            "nvfp4kv_stream_read", "nvfp4kv_last_error", "nvfp4kv_version"]
+            "nvfp4kv_stream_read", "nvfp4kv_last_error", "nvfp4kv_version", "nvfp4kv_check_decode_tables",
+            "nvfp4kv_check_slots", "nvfp4kv_check_page_ids", "nvfp4kv_checked_build"]
 
 
 def lib() -> ctypes.CDLL:
@@ -443,6 +460,54 @@ def nvfp4kv_restore_pages(pool: Pool, page_ids: torch.Tensor, arena: torch.Tenso
     _check("nvfp4kv_restore_pages",
            _lib.nvfp4kv_restore_pages(ctypes.byref(d), page_ids.numel(), _ptr(page_ids), _ptr(arena),
                                       arena.numel(), _stream(stream)))
+
+
+def _host_i32(t) -> torch.Tensor:
+    t = torch.as_tensor(t)
+    assert t.device.type == "cpu", "the range checks take host (CPU) tables"
+    return t.to(torch.int32).contiguous()
+
+
+def nvfp4kv_check_decode_tables(pool: Pool, page_table, seq_lens, max_seq_len: int, q_positions=None,
+                                max_pos: int = 0, n_qtok: int = 1, lib: ctypes.CDLL | None = None) -> None:
+    """Range check of a decode call's page table, lengths and query positions
+    on host copies (CPU tensors or arrays); raises NVFP4KVError naming the
+    first offending index."""
+    L = lib or _lib
+    pt = _host_i32(page_table)
+    sl = _host_i32(seq_lens)
+    qp = _host_i32(q_positions) if q_positions is not None else None
+    d = pool.desc()
+    rc = L.nvfp4kv_check_decode_tables(ctypes.byref(d), sl.numel(), int(n_qtok), pt.data_ptr(), pt.shape[-1],
+                                       sl.data_ptr(), int(max_seq_len), qp.data_ptr() if qp is not None else None,
+                                       int(max_pos))
+    if rc != OK:
+        raise NVFP4KVError("nvfp4kv_check_decode_tables", rc, L.nvfp4kv_last_error().decode())
+
+
+def nvfp4kv_check_slots(pool: Pool, slots, positions=None, max_pos: int = 0, lib: ctypes.CDLL | None = None) -> None:
+    """Range and distinctness check of an append's slots (and positions) on host copies."""
+    L = lib or _lib
+    sl = torch.as_tensor(slots).to(torch.int64).contiguous()
+    ps = _host_i32(positions) if positions is not None else None
+    d = pool.desc()
+    rc = L.nvfp4kv_check_slots(ctypes.byref(d), sl.numel(), sl.data_ptr(), ps.data_ptr() if ps is not None else None,
+                               int(max_pos))
+    if rc != OK:
+        raise NVFP4KVError("nvfp4kv_check_slots", rc, L.nvfp4kv_last_error().decode())
+
+
+def nvfp4kv_check_page_ids(pool: Pool, page_ids, distinct: bool, lib: ctypes.CDLL | None = None) -> None:
+    L = lib or _lib
+    ids = _host_i32(page_ids)
+    d = pool.desc()
+    rc = L.nvfp4kv_check_page_ids(ctypes.byref(d), ids.numel(), ids.data_ptr(), int(bool(distinct)))
+    if rc != OK:
+        raise NVFP4KVError("nvfp4kv_check_page_ids", rc, L.nvfp4kv_last_error().decode())
+
+
+def nvfp4kv_checked_build(lib: ctypes.CDLL | None = None) -> bool:
+    return bool((lib or _lib).nvfp4kv_checked_build())
 
 
 def default_sm_scale() -> float:

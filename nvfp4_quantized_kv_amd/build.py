@@ -34,9 +34,12 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", LIB + ".tmp", *srcs]
+# the checked build: every entry point range-checks the device-side tables it
+# trusts (copied back on the call's stream) before launching anything
+DEBUG_LIB = os.path.join(PKG, "libnvfp4kv_debug.so")
+
+
+def _run(cmd, verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l and l.strip())
@@ -44,14 +47,37 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out:
         print(out)
-    os.replace(LIB + ".tmp", LIB)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Build libnvfp4kv.so and, with `debug`, the checked libnvfp4kv_debug.so:
+    every source compiled to an object (in parallel), then one link per
+    library."""
+    import concurrent.futures
+    import tempfile
+    variants = [(LIB, [])] + ([(DEBUG_LIB, ["-DNVFP4KV_DEBUG=1"])] if debug else [])
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory() as tmp:
+        jobs = []
+        for li, (_, extra) in enumerate(variants):
+            for src in SOURCES:
+                obj = os.path.join(tmp, f"{li}_{src}.o")
+                jobs.append((obj, [hipcc(), *compile_flags, *extra, "-I", os.path.join(ROOT, "include"), "-c",
+                                   "-o", obj, os.path.join(CSRC, src)]))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda j: _run(j[1], verbose), jobs))
+        for li, (out_path, _) in enumerate(variants):
+            objs = [os.path.join(tmp, f"{li}_{src}.o") for src in SOURCES]
+            _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_path + ".tmp", *objs], verbose)
+            os.replace(out_path + ".tmp", out_path)
     return LIB
 
 
-def stale() -> bool:
-    if not os.path.exists(LIB):
+def stale(path: str = LIB) -> bool:
+    if not os.path.exists(path):
         return True
-    t = os.path.getmtime(LIB)
+    t = os.path.getmtime(path)
     deps = [os.path.join(CSRC, s) for s in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "nvfp4kv.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 

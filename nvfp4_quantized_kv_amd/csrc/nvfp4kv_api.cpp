@@ -1,4 +1,10 @@
 // C ABI of libnvfp4kv: argument checks, split-K planning and kernel launches.
+// Built with NVFP4KV_DEBUG=1 (libnvfp4kv_debug.so), every entry point also
+// copies the device-side tables it trusts back to the host and range-checks
+// them before launching anything.
+#ifndef NVFP4KV_DEBUG
+#define NVFP4KV_DEBUG 0
+#endif
 // Every check runs on the host before anything is queued; no exception
 // crosses the interface and no device memory is allocated here.
 #include "nvfp4kv.h"
@@ -11,6 +17,7 @@
 #include <algorithm>
 #include <atomic>
 #include <string>
+#include <vector>
 
 #include "nvfp4kv_internal.hpp"
 
@@ -170,9 +177,153 @@ int check_workspace(size_t need, const void* workspace, size_t workspace_bytes) 
   return NVFP4KV_OK;
 }
 
+// ---- range checks of the device-side tables (on host copies) ----------------
+
+int check_decode_tables_host(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok, const int32_t* page_table,
+                             int32_t page_table_stride, const int32_t* seq_lens, int64_t max_seq_len,
+                             const int32_t* q_positions, int32_t max_pos) {
+  int rc;
+  if ((rc = check_pool_shape(p)) != NVFP4KV_OK) return rc;
+  if (n_seq <= 0 || n_qtok <= 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_seq and n_qtok must be positive");
+  if (page_table == nullptr || seq_lens == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null page_table or seq_lens");
+  if (max_seq_len <= 0 || page_table_stride < (max_seq_len + 63) / 64)
+    return fail(NVFP4KV_ERR_INVALID_ARG, "page_table_stride %d smaller than the pages of max_seq_len %lld",
+                page_table_stride, (long long)max_seq_len);
+  for (int32_t n = 0; n < n_seq; ++n) {
+    const int32_t L = seq_lens[n];
+    if (L < n_qtok || (int64_t)L > max_seq_len)
+      return fail(NVFP4KV_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [%d, %lld]", n, L, n_qtok,
+                  (long long)max_seq_len);
+    for (int32_t j = 0; j < (L + 63) / 64; ++j) {
+      const int32_t pid = page_table[(size_t)n * page_table_stride + j];
+      if (pid < 0 || (int64_t)pid >= p->num_pages)
+        return fail(NVFP4KV_ERR_INVALID_ARG, "page_table[%d][%d] = %d outside [0, %lld)", n, j, pid,
+                    (long long)p->num_pages);
+    }
+  }
+  if (p->rotary_dim > 0 && q_positions != nullptr)
+    for (int64_t i = 0; i < (int64_t)n_seq * n_qtok; ++i)
+      if (q_positions[i] < 0 || q_positions[i] >= max_pos)
+        return fail(NVFP4KV_ERR_INVALID_ARG, "q_positions[%lld] = %d outside [0, %d)", (long long)i, q_positions[i],
+                    max_pos);
+  return NVFP4KV_OK;
+}
+
+int check_slots_host(const nvfp4kv_pool* p, int32_t n_tok, const int64_t* slots, const int32_t* positions,
+                     int32_t max_pos) {
+  int rc;
+  if ((rc = check_pool_shape(p)) != NVFP4KV_OK) return rc;
+  if (n_tok < 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_tok must not be negative");
+  if (n_tok > 0 && slots == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null slots");
+  const int64_t n_slots = p->num_pages * 64;
+  std::vector<std::pair<int64_t, int32_t>> order;
+  order.reserve((size_t)n_tok);
+  for (int32_t i = 0; i < n_tok; ++i) {
+    if (slots[i] < 0 || slots[i] >= n_slots)
+      return fail(NVFP4KV_ERR_INVALID_ARG, "slots[%d] = %lld outside [0, %lld)", i, (long long)slots[i],
+                  (long long)n_slots);
+    order.emplace_back(slots[i], i);
+  }
+  std::sort(order.begin(), order.end());
+  for (size_t i = 1; i < order.size(); ++i)
+    if (order[i].first == order[i - 1].first)
+      return fail(NVFP4KV_ERR_INVALID_ARG, "slots[%d] and slots[%d] both name slot %lld (the writes would race)",
+                  order[i - 1].second, order[i].second, (long long)order[i].first);
+  if (p->rotary_dim > 0 && positions != nullptr)
+    for (int32_t i = 0; i < n_tok; ++i)
+      if (positions[i] < 0 || positions[i] >= max_pos)
+        return fail(NVFP4KV_ERR_INVALID_ARG, "positions[%d] = %d outside [0, %d)", i, positions[i], max_pos);
+  return NVFP4KV_OK;
+}
+
+int check_page_ids_host(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* ids, int32_t distinct) {
+  int rc;
+  if ((rc = check_pool_shape(p)) != NVFP4KV_OK) return rc;
+  if (n_pages < 0) return fail(NVFP4KV_ERR_INVALID_ARG, "n_pages must not be negative");
+  if (n_pages > 0 && ids == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null page ids");
+  if (!distinct) return NVFP4KV_OK;   // ids outside the pool are skipped by contract
+  std::vector<std::pair<int32_t, int32_t>> order;
+  for (int32_t i = 0; i < n_pages; ++i)
+    if (ids[i] >= 0 && (int64_t)ids[i] < p->num_pages) order.emplace_back(ids[i], i);
+  std::sort(order.begin(), order.end());
+  for (size_t i = 1; i < order.size(); ++i)
+    if (order[i].first == order[i - 1].first)
+      return fail(NVFP4KV_ERR_INVALID_ARG, "page_ids[%d] and page_ids[%d] both name page %d (a restore would mix them)",
+                  order[i - 1].second, order[i].second, order[i].first);
+  return NVFP4KV_OK;
+}
+
+#if NVFP4KV_DEBUG
+// The checked build: copy the device-side tables a call trusts back to the
+// host, in order on the call's stream, and range-check them before anything
+// is launched.  This synchronizes the stream (a debugging aid only).
+template <typename T>
+int fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t stream) {
+  dst.resize(n);
+  if (n == 0) return NVFP4KV_OK;
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDefault, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "checked build: copying a table to the host");
+  return NVFP4KV_OK;
+}
+
+int debug_check_decode(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok, const int32_t* page_table,
+                       int32_t stride, const int32_t* seq_lens, int64_t max_seq_len, const int32_t* q_positions,
+                       int32_t max_pos, hipStream_t stream) {
+  std::vector<int32_t> pt, sl, qp;
+  int rc;
+  if ((rc = fetch(sl, seq_lens, (size_t)n_seq, stream)) != NVFP4KV_OK) return rc;
+  if ((rc = fetch(pt, page_table, (size_t)n_seq * stride, stream)) != NVFP4KV_OK) return rc;
+  const bool pos = p->rotary_dim > 0 && q_positions != nullptr;
+  if (pos && (rc = fetch(qp, q_positions, (size_t)n_seq * n_qtok, stream)) != NVFP4KV_OK) return rc;
+  return check_decode_tables_host(p, n_seq, n_qtok, pt.data(), stride, sl.data(), max_seq_len,
+                                  pos ? qp.data() : nullptr, max_pos);
+}
+
+int debug_check_slots(const nvfp4kv_pool* p, int32_t n_tok, const int64_t* slots, const int32_t* positions,
+                      int32_t max_pos, hipStream_t stream) {
+  std::vector<int64_t> sl;
+  std::vector<int32_t> ps;
+  int rc;
+  if ((rc = fetch(sl, slots, (size_t)n_tok, stream)) != NVFP4KV_OK) return rc;
+  const bool pos = p->rotary_dim > 0 && positions != nullptr;
+  if (pos && (rc = fetch(ps, positions, (size_t)n_tok, stream)) != NVFP4KV_OK) return rc;
+  return check_slots_host(p, n_tok, sl.data(), pos ? ps.data() : nullptr, max_pos);
+}
+
+int debug_check_page_ids(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* ids, int32_t distinct,
+                         hipStream_t stream) {
+  std::vector<int32_t> v;
+  int rc;
+  if ((rc = fetch(v, ids, (size_t)n_pages, stream)) != NVFP4KV_OK) return rc;
+  return check_page_ids_host(p, n_pages, v.data(), distinct);
+}
+#endif
+
 }  // namespace
 
 extern "C" {
+
+int nvfp4kv_check_decode_tables(const nvfp4kv_pool* p, int32_t n_seq, int32_t n_qtok, const int32_t* page_table,
+                                int32_t page_table_stride, const int32_t* seq_lens, int64_t max_seq_len,
+                                const int32_t* q_positions, int32_t max_pos) {
+  g_last_error.clear();
+  return check_decode_tables_host(p, n_seq, n_qtok, page_table, page_table_stride, seq_lens, max_seq_len,
+                                  q_positions, max_pos);
+}
+
+int nvfp4kv_check_slots(const nvfp4kv_pool* p, int32_t n_tok, const int64_t* slots, const int32_t* positions,
+                        int32_t max_pos) {
+  g_last_error.clear();
+  return check_slots_host(p, n_tok, slots, positions, max_pos);
+}
+
+int nvfp4kv_check_page_ids(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page_ids, int32_t distinct) {
+  g_last_error.clear();
+  return check_page_ids_host(p, n_pages, page_ids, distinct);
+}
+
+int nvfp4kv_checked_build(void) { return NVFP4KV_DEBUG ? 1 : 0; }
 
 size_t nvfp4kv_pool_bytes(const nvfp4kv_pool* p) {
   if (p == nullptr || p->num_pages <= 0 || p->num_layers <= 0 || p->num_kv_heads <= 0 ||
@@ -217,6 +368,9 @@ int nvfp4kv_append(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const vo
   if (!aligned(k, 16) || !aligned(v, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   if (p->rotary_dim > 0 && positions == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "rotary_dim > 0 needs positions");
   if ((rc = check_rope(p, rope_cos, rope_sin, max_pos)) != NVFP4KV_OK) return rc;
+#if NVFP4KV_DEBUG
+  if ((rc = debug_check_slots(p, n_tok, slots, positions, max_pos, stream)) != NVFP4KV_OK) return rc;
+#endif
   hipError_t e = nvfp4kv::launch_append(launch_pool(p), layer, n_tok, k, v, (int)in_dtype, slots,
                                         positions, rope_cos, rope_sin, stream);
   if (e != hipSuccess) return hip_fail(e, "kv_quant_append launch");
@@ -290,6 +444,11 @@ int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_s
                         max_pos, page_table, page_table_stride, seq_lens, max_seq_len, sm_scale,
                         workspace, workspace_bytes, pages_per_split, &plan);
   if (rc != NVFP4KV_OK) return rc;
+#if NVFP4KV_DEBUG
+  if ((rc = debug_check_decode(p, n_seq, 1, page_table, page_table_stride, seq_lens, max_seq_len, q_positions,
+                               max_pos, stream)) != NVFP4KV_OK)
+    return rc;
+#endif
   hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
@@ -332,6 +491,11 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
   if (rc != NVFP4KV_OK) return rc;
   if (out == nullptr) return fail(NVFP4KV_ERR_INVALID_ARG, "null out");
   if (!aligned(out, 16)) return fail(NVFP4KV_ERR_INVALID_ARG, "out must be 16-byte aligned");
+#if NVFP4KV_DEBUG
+  if ((rc = debug_check_decode(p, n_seq, 1, page_table, page_table_stride, seq_lens, max_seq_len, q_positions,
+                               max_pos, stream)) != NVFP4KV_OK)
+    return rc;
+#endif
   hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
@@ -442,6 +606,11 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
       NVFP4KV_OK)
     return rc;
   if ((rc = check_workspace(need, workspace, workspace_bytes)) != NVFP4KV_OK) return rc;
+#if NVFP4KV_DEBUG
+  if ((rc = debug_check_decode(p, n_seq, n_qtok, page_table, page_table_stride, seq_lens, max_seq_len, q_positions,
+                               max_pos, stream)) != NVFP4KV_OK)
+    return rc;
+#endif
   // one split + reduce pair per launch's tokens; the workspace is reused in
   // stream order
   for (int t0 = 0; t0 < n_qtok; t0 += per) {
@@ -506,6 +675,9 @@ static int page_copy(const nvfp4kv_pool* p, int32_t n_pages, const int32_t* page
   uint8_t* arena_dev = nullptr;
   if ((rc = device_view(page_ids, "page_ids", &ids_dev)) != NVFP4KV_OK) return rc;
   if ((rc = device_view(arena, "arena", &arena_dev)) != NVFP4KV_OK) return rc;
+#if NVFP4KV_DEBUG
+  if ((rc = debug_check_page_ids(p, n_pages, page_ids, to_arena ? 0 : 1, stream)) != NVFP4KV_OK) return rc;
+#endif
   hipError_t e = nvfp4kv::launch_page_copy(launch_pool(p), p->num_layers, n_pages,
                                            reinterpret_cast<const int32_t*>(ids_dev), arena_dev, to_arena, stream);
   if (e != hipSuccess) return hip_fail(e, "page copy launch");
@@ -557,6 +729,17 @@ int nvfp4kv_dequant(const nvfp4kv_pool* p, int32_t layer, int32_t n_tok, const i
   if ((k_out && !aligned(k_out, 16)) || (v_out && !aligned(v_out, 16)))
     return fail(NVFP4KV_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
   if (unrotate != 0 && unrotate != 1) return fail(NVFP4KV_ERR_INVALID_ARG, "unrotate must be 0 or 1");
+#if NVFP4KV_DEBUG
+  {
+    // reads may repeat a slot: only the range is checked
+    std::vector<int64_t> sl;
+    if ((rc = fetch(sl, slots, (size_t)n_tok, stream)) != NVFP4KV_OK) return rc;
+    for (int32_t i = 0; i < n_tok; ++i)
+      if (sl[i] < 0 || sl[i] >= p->num_pages * 64)
+        return fail(NVFP4KV_ERR_INVALID_ARG, "slots[%d] = %lld outside [0, %lld)", i, (long long)sl[i],
+                    (long long)(p->num_pages * 64));
+  }
+#endif
   hipError_t e = nvfp4kv::launch_dequant(launch_pool(p), layer, n_tok, slots, k_out, v_out,
                                          (int)out_dtype, unrotate, stream);
   if (e != hipSuccess) return hip_fail(e, "dequant launch");
