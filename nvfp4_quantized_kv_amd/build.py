@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4kv.so")
 
-SOURCES = ["kv_append.hip", "decode_attn.hip", "kv_spill.hip", "nvfp4kv_api.cpp"]
+SOURCES = ["kv_append.hip", "decode_attn.hip", "decode_attn_gr.hip", "kv_spill.hip", "nvfp4kv_api.cpp"]
 HEADERS = ["nvfp4kv_codec.hpp", "nvfp4kv_internal.hpp"]
 
 HIPCC_FLAGS = [

@@ -42,7 +42,18 @@
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
 
+// This file is compiled twice: as is, for rotary widths that are multiples
+// of 16 (the kernels the workloads run), and from decode_attn_gr.hip with
+// NVFP4KV_DECODE_GENERAL_ROPE 1, whose kernels also take every other even
+// width.  Keeping the general rotation out of the first build keeps it out
+// of those kernels' register allocation.
+#ifndef NVFP4KV_DECODE_GENERAL_ROPE
+#define NVFP4KV_DECODE_GENERAL_ROPE 0
+#endif
+
 namespace nvfp4kv {
+
+constexpr bool kGR = NVFP4KV_DECODE_GENERAL_ROPE != 0;
 
 namespace {
 
@@ -293,8 +304,8 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, co
   if (!MQ) {
     if (rotary_dim > 0) {
       const int pos = q_positions[seq];
-      rope_coeffs(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
-                  rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
+      rope_coeffs<kGR>(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
+                       rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
@@ -339,14 +350,14 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
     uint32_t codes, scode;
     if (MQ) {
       if (rotary_dim > 0)
-        rope_coeffs(c16, rotary_dim, rope_cos + (size_t)in.pos[pass] * (rotary_dim / 2),
-                    rope_sin + (size_t)in.pos[pass] * (rotary_dim / 2), in.cv, in.sv);
+        rope_coeffs<kGR>(c16, rotary_dim, rope_cos + (size_t)in.pos[pass] * (rotary_dim / 2),
+                         rope_sin + (size_t)in.pos[pass] * (rotary_dim / 2), in.cv, in.sv);
       else
 #pragma unroll
         for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
     }
-    quant_row16_v(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0, lane_signs(hadamard, signs, c16),
-                  codes, scode);
+    quant_row16_v<kGR>(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0,
+                       lane_signs(hadamard, signs, c16), codes, scode);
     const float s = e4m3_value(scode);
     h8 qv;
 #pragma unroll
@@ -404,7 +415,7 @@ __device__ __forceinline__ void append_new_token(
     srow = rope_sin + (size_t)pos * (rotary_dim / 2);
   }
   uint32_t codes, scode;
-  quant_row16(x, c16, rot, crow, srow, which ? false : (hadamard != 0),
+  quant_row16<kGR>(x, c16, rot, crow, srow, which ? false : (hadamard != 0),
               which ? 0u : lane_signs(hadamard, signs, c16), codes, scode);
   if (lane < 32) {
     const int tok = seq_lens[seq] - 1;
@@ -1243,6 +1254,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     write_partial<PACKED>(acc[t], m_ref[t], l_run[t], c16, g4, group, ws_acc, ws_ml, st.slot, 16 * t);
 }
 
+#if !NVFP4KV_DECODE_GENERAL_ROPE
 // Combine the partials of one (sequence, query head) for 32 output dims:
 // 256 threads = 32 dims x 8 groups that stride over the pieces.  The pieces
 // of segment g come from waves w_first .. w_last, found with the same flat
@@ -1343,9 +1355,17 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   }
 }
 
+#endif  // !NVFP4KV_DECODE_GENERAL_ROPE
+
 }  // namespace
 
-hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
+#if NVFP4KV_DECODE_GENERAL_ROPE
+#define NVFP4KV_SPLITS_FN launch_decode_splits_gr
+#else
+#define NVFP4KV_SPLITS_FN launch_decode_splits
+#endif
+
+hipError_t NVFP4KV_SPLITS_FN(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
                                 const void* q, const void* k_new, const void* v_new, int in_dtype,
                                 const int32_t* q_positions, const float* rope_cos,
                                 const float* rope_sin, const int32_t* page_table,
@@ -1373,6 +1393,7 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
   return hipGetLastError();
 }
 
+#if !NVFP4KV_DECODE_GENERAL_ROPE
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
                                 const QTokens& qt, float v_scale, hipStream_t stream) {
@@ -1438,5 +1459,7 @@ int decode_waves_per_cu(int nt, bool packed, bool vf16) {
   }
   return lo;
 }
+
+#endif  // !NVFP4KV_DECODE_GENERAL_ROPE
 
 }  // namespace nvfp4kv

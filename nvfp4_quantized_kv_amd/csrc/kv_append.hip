@@ -89,12 +89,14 @@ struct RopeLane {
   int src;   // the lane of the row holding the partner elements
 };
 
-// Rotary widths that are not a multiple of 16: coefficients element by
-// element (rope_coeffs), the rotation by rope_rows_any.
+// GR (rotary widths that are not a multiple of 16): coefficients element by
+// element (rope_coeffs), the rotation by rope_rows_any.  The general code is
+// only in the GR instances of the kernel.
+template <bool GR>
 __device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* cos_row, const float* sin_row,
                                           RopeLane& rl) {
-  if ((rotary_dim & 15) != 0) {
-    rope_coeffs(r, rotary_dim, cos_row, sin_row, rl.cv, rl.sv);
+  if (GR && (rotary_dim & 15) != 0) {
+    rope_coeffs<true>(r, rotary_dim, cos_row, sin_row, rl.cv, rl.sv);
     rl.first = rl.in_rot = false;
     rl.src = r;
     return;
@@ -119,12 +121,13 @@ __device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* co
 // read beforehand (`rl`, used when `rope`), RoPE without branches, the
 // transform's cross-lane stages through DPP and the E2M1 code by search.
 // All 16 lanes of a row must call it together.
+template <bool GR>
 __device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, int rotary_dim,
                                              const RopeLane& rl, bool hadamard, uint32_t neg, uint32_t& codes,
                                              uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
-  if (rope && (rotary_dim & 15) != 0) {
+  if (GR && rope && (rotary_dim & 15) != 0) {
     rope_rows_any(x, r, rotary_dim / 2, rl.cv, rl.sv);
   } else if (rope) {
     const int src_lane = (lane & ~15) + rl.src;
@@ -221,7 +224,7 @@ __device__ __forceinline__ void raw_to_float(const RawRow<DT>& rw, float (&x)[8]
 // completes those lines in its CU's L2.  Spread over workgroups (and so over
 // XCDs), each line was written back in pieces: twice the algorithmic write
 // traffic, measured.
-template <int DT>
+template <int DT, bool GR>
 __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_tok,
     const void* __restrict__ k, const void* __restrict__ v,
@@ -263,8 +266,8 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     const bool active = (int)blockIdx.x * 64 + (it / hkv) * 16 + (wv & 3) * 4 + (lane >> 4) < n_tok;
     RopeLane rl;
     if (rot > 0)
-      rope_lane(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2), rope_sin + (size_t)pos * (rotary_dim / 2),
-                rl);
+      rope_lane<GR>(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
+                    rope_sin + (size_t)pos * (rotary_dim / 2), rl);
     __builtin_amdgcn_sched_barrier(0);
     int64_t slot_n;
     int pos_n;
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
       }
     } else {
       uint32_t codes, scode;
-      append_row16(x, r, rot > 0, rot, rl, had, neg, codes, scode);
+      append_row16<GR>(x, r, rot > 0, rot, rl, had, neg, codes, scode);
       if (active) {
         const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
         *reinterpret_cast<uint32_t*>(blk + woff) = codes;
@@ -398,7 +401,10 @@ hipError_t launch_append(const LaunchPool& P, int layer, int n_tok, const void* 
                          int dtype, const int64_t* slots, const int32_t* positions,
                          const float* rope_cos, const float* rope_sin, hipStream_t stream) {
   const int runs = (n_tok + 63) / 64;            // 64 tokens, every kv head, per workgroup
-  auto kern = dtype == 1 ? kv_quant_append_kernel<1> : kv_quant_append_kernel<0>;
+  // the general rotation only in the kernels of widths that need it
+  const bool gr = (P.rotary_dim & 15) != 0;
+  auto kern = dtype == 1 ? (gr ? kv_quant_append_kernel<1, true> : kv_quant_append_kernel<1, false>)
+                         : (gr ? kv_quant_append_kernel<0, true> : kv_quant_append_kernel<0, false>);
   hipLaunchKernelGGL(kern, dim3(runs), dim3(512), 0, stream, P.base, P.num_pages, P.hkv, layer, n_tok, k,
                      v, slots, positions, rope_cos, rope_sin, P.rotary_dim, P.hadamard, P.signs, P.k_inv,
                      P.v_inv, P.v_format, P.block_bytes, P.ks_off);

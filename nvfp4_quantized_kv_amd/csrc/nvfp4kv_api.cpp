@@ -87,6 +87,12 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(NVFP4KV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The decode kernels built for the pool's rotary width: multiples of 16
+// (0 included) or the general rotation.
+decltype(&nvfp4kv::launch_decode_splits) splits_launcher(const nvfp4kv_pool* p) {
+  return (p->rotary_dim & 15) != 0 ? &nvfp4kv::launch_decode_splits_gr : &nvfp4kv::launch_decode_splits;
+}
+
 nvfp4kv::LaunchPool launch_pool(const nvfp4kv_pool* p) {
   nvfp4kv::LaunchPool L;
   L.base = reinterpret_cast<uint8_t*>(p->base);
@@ -449,7 +455,7 @@ int nvfp4kv_decode_attn_splits(const nvfp4kv_pool* p, int32_t layer, int32_t n_s
                                max_pos, stream)) != NVFP4KV_OK)
     return rc;
 #endif
-  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
+  hipError_t e = splits_launcher(p)(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
                                                workspace, plan, one_token(plan), stream);
@@ -496,7 +502,7 @@ int nvfp4kv_decode_attn(const nvfp4kv_pool* p, int32_t layer, int32_t n_seq, int
                                max_pos, stream)) != NVFP4KV_OK)
     return rc;
 #endif
-  hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
+  hipError_t e = splits_launcher(p)(launch_pool(p), layer, n_seq, n_q_heads, q, k_new,
                                                v_new, (int)q_dtype, q_positions, rope_cos, rope_sin,
                                                page_table, page_table_stride, seq_lens, sm_scale,
                                                workspace, plan, one_token(plan), stream);
@@ -616,7 +622,7 @@ int nvfp4kv_decode_attn_multi(const nvfp4kv_pool* p, int32_t layer, int32_t n_se
   for (int t0 = 0; t0 < n_qtok; t0 += per) {
     const nvfp4kv::DecodePlan& pl = t0 + per <= n_qtok ? full : last;
     const nvfp4kv::QTokens qt{n_qtok, t0, heads};
-    hipError_t e = nvfp4kv::launch_decode_splits(launch_pool(p), layer, n_seq, n_q_heads, q, nullptr, nullptr,
+    hipError_t e = splits_launcher(p)(launch_pool(p), layer, n_seq, n_q_heads, q, nullptr, nullptr,
                                                  (int)q_dtype, q_positions, rope_cos, rope_sin, page_table,
                                                  page_table_stride, seq_lens, sm_scale, workspace, pl, qt,
                                                  stream);

@@ -127,16 +127,29 @@ __device__ inline void load8(const void* src, int dtype, size_t elem_off, float 
 // row covers elements e = 8r .. 8r+7; in the first half of the rotary part
 // (e < R/2) it needs cos/sin of pair e, in the second half those of pair
 // e - R/2, beyond the rotary part nothing (zeros are returned, and not used).
-// Any even R.
+// GR (general rotary widths): any even R, element by element; otherwise R is
+// a multiple of 16 and a lane's 8 coefficients are consecutive.
+template <bool GR = false>
 __device__ inline void rope_coeffs(int r, int rotary_dim, const float* cos_row, const float* sin_row,
                                    float (&cv)[8], float (&sv)[8]) {
   const int half = rotary_dim / 2;
+  if constexpr (GR) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int e = 8 * r + k;
-    const int idx = e < half ? e : e - half;
-    cv[k] = e < rotary_dim ? cos_row[idx] : 0.0f;
-    sv[k] = e < rotary_dim ? sin_row[idx] : 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      const int e = 8 * r + k;
+      const int idx = e < half ? e : e - half;
+      cv[k] = e < rotary_dim ? cos_row[idx] : 0.0f;
+      sv[k] = e < rotary_dim ? sin_row[idx] : 0.0f;
+    }
+  } else {
+    const int hl = half / 8;                  // lanes per half
+    const bool in_rot = r < 2 * hl;
+    const int base = in_rot ? (r < hl ? 8 * r : 8 * r - half) : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      cv[k] = in_rot ? cos_row[base + k] : 0.0f;
+      sv[k] = in_rot ? sin_row[base + k] : 0.0f;
+    }
   }
 }
 
@@ -191,7 +204,9 @@ __device__ __forceinline__ void rope_rows_any(float (&x)[8], int r, int half, co
   }
 }
 
-// Quantize one 128-element row held by the 16 lanes of a lane group.  `x`
+// Quantize one 128-element row held by the 16 lanes of a lane group.  GR:
+// any even rotary width (the general rotation); otherwise the width is a
+// multiple of 16 (0 included), the only case the code then holds.  `x`
 // holds elements 8r .. 8r+7 of the row, r = lane % 16; `cv`/`sv` the lane's
 // RoPE coefficients from rope_coeffs (unused when rotary_dim is 0).  On
 // return `x` holds the rotated (RoPE'd, Hadamard'd) floats, `codes` the
@@ -200,13 +215,14 @@ __device__ __forceinline__ void rope_rows_any(float (&x)[8], int r, int half, co
 // rotation, the elements whose bit is set in `neg` (bit k: element 8r+k; the
 // randomized rotation's mask, else 0) are negated before it.  All 64 lanes of
 // the wavefront must call it together (it uses cross-lane shuffles).
+template <bool GR = false>
 __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const float (&cv)[8],
                                      const float (&sv)[8], bool hadamard, uint32_t neg,
                                      uint32_t& codes, uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
   // RoPE, rotate-half pairs (i, i + R/2) on the first R dims.
-  if (rotary_dim > 0 && (rotary_dim & 15) != 0) {
+  if (GR && rotary_dim > 0 && (rotary_dim & 15) != 0) {
     rope_rows_any(x, r, rotary_dim / 2, cv, sv);
   } else if (rotary_dim > 0) {
     const int half = rotary_dim / 2;
@@ -271,17 +287,18 @@ __device__ inline void quant_row16_v(float (&x)[8], int r, int rotary_dim, const
 }
 
 // quant_row16_v with the RoPE coefficients read from the table rows.
+template <bool GR = false>
 __device__ inline void quant_row16(float (&x)[8], int r, int rotary_dim, const float* cos_row,
                                    const float* sin_row, bool hadamard, uint32_t neg, uint32_t& codes,
                                    uint32_t& scode) {
   float cv[8], sv[8];
   if (rotary_dim > 0) {
-    rope_coeffs(r, rotary_dim, cos_row, sin_row, cv, sv);
+    rope_coeffs<GR>(r, rotary_dim, cos_row, sin_row, cv, sv);
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) cv[k] = sv[k] = 0.0f;
   }
-  quant_row16_v(x, r, rotary_dim, cv, sv, hadamard, neg, codes, scode);
+  quant_row16_v<GR>(x, r, rotary_dim, cv, sv, hadamard, neg, codes, scode);
 }
 
 }  // namespace nvfp4kv

@@ -117,6 +117,16 @@ hipError_t launch_decode_splits(const LaunchPool& P, int layer, int n_seq, int n
                                 void* workspace, const DecodePlan& plan, const QTokens& qt,
                                 hipStream_t stream);
 
+// launch_decode_splits for rotary widths that are not multiples of 16
+// (kernels compiled with the general rotation).
+hipError_t launch_decode_splits_gr(const LaunchPool& P, int layer, int n_seq, int n_q_heads,
+                                   const void* q, const void* k_new, const void* v_new, int in_dtype,
+                                   const int32_t* q_positions, const float* rope_cos,
+                                   const float* rope_sin, const int32_t* page_table,
+                                   int page_table_stride, const int32_t* seq_lens, float sm_scale,
+                                   void* workspace, const DecodePlan& plan, const QTokens& qt,
+                                   hipStream_t stream);
+
 hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t* seq_lens,
                                 float* out, const void* workspace, const DecodePlan& plan,
                                 const QTokens& qt, float v_scale, hipStream_t stream);
