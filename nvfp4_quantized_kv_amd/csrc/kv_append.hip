@@ -41,10 +41,10 @@ __device__ __forceinline__ float xor_lane(float x) {
   return __int_as_float(o);
 }
 
-// One cross-lane stage of the transform: the lower lane of a pair keeps
-// a + b, the upper one b - a (its own value subtracted from the partner's),
-// as one fused multiply-add by +-1, which rounds exactly as the addition or
-// subtraction does.
+// One cross-lane stage of the transform, exact in every case (signed zeros
+// included): the lower lane of a pair keeps a + b, the upper one a - b (its
+// partner's value minus its own), as one fused multiply-add by +-1, which
+// rounds exactly as the addition or subtraction does.
 template <int BIT>
 __device__ __forceinline__ void fwht_stage(float (&x)[8], int r) {
   const float sgn = (r & BIT) ? -1.0f : 1.0f;
@@ -64,20 +64,92 @@ __device__ __forceinline__ void fwht_stage(float (&x)[8], int r) {
   }
 }
 
-// E2M1 magnitude code of |y| for block scale s by a three-level search over
-// the same exact thresholds as e2m1_code: 1.75s (>=) splits codes 0-3 from
-// 4-7, then 0.75s or 3.5s (>=), then 0.25s, 1.25s, 2.5s or 5s (>).  The
-// thresholds increase and each test is monotone in |y|, so the result is the
-// count of thresholds passed, as in e2m1_code.
-__device__ __forceinline__ uint32_t e2m1_code_search(float y, const float (&t)[7], float s) {
-  const float a = fabsf(y);
-  const bool b2 = a >= t[3];
-  const bool b1 = a >= (b2 ? t[5] : t[1]);
-  const float t0 = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);
-  const bool b0 = a > t0;
-  uint32_t c = (b2 ? 4u : 0u) | (b1 ? 2u : 0u) | (b0 ? 1u : 0u);
-  if (s == 0.0f) c = 0;
-  return c | (signbit(y) ? 8u : 0u);
+// Cross-lane stages of the transform (strides 8, 16, 32 and 64: lane bits
+// 0-3 of the row), each a DPP instruction per element, one for bits 0, 1
+// and 3 and two for bit 2.  For bits 0, 1 and 3 every lane adds its
+// partner's value times +1 (lower lane) or -1 (upper lane) to its own in one
+// fused multiply-add, which rounds exactly as the sum or difference does, so
+// the upper lane holds the negated difference.  A lane's sign so far then
+// depends only on the lane bits of the stages before, which both lanes of a
+// later pair share, so every later stage computes the signed sum or
+// difference of the true values; the sign (-1)^(r0 + r1 + r3) is folded into
+// the closing multiply by 1/sqrt(128).  Signed zeros: the held value of a
+// zero is +0 whatever its sign so far (a cancellation rounds to +0), and so
+// is the true value as long as no -0 enters the transform (-0 only comes
+// from -0 operands); the closing fma(h, +-c, +0) then gives +0 for every
+// zero, as the plain transform does.  Rows with a -0 input take the stages
+// above instead.  For bit 2 the lower lanes (banks 0
+// and 2 of the row) take partner + own and the upper ones partner - own,
+// each under a bank mask.  Each block starts with 5 wait states: a DPP
+// source written by a VALU (or EXEC written by SALU) just before needs them.
+#define NVFP4KV_DPP8(OP, CTRL)                                                       \
+  "s_nop 4\n\t" OP " %0, %0, %8 " CTRL "\n\t" OP " %1, %1, %8 " CTRL "\n\t" OP  \
+  " %2, %2, %8 " CTRL "\n\t" OP " %3, %3, %8 " CTRL "\n\t" OP " %4, %4, %8 " CTRL \
+  "\n\t" OP " %5, %5, %8 " CTRL "\n\t" OP " %6, %6, %8 " CTRL "\n\t" OP         \
+  " %7, %7, %8 " CTRL
+#define NVFP4KV_X8(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+
+__device__ __forceinline__ void fwht_cross_lanes(float (&x)[8], int r) {
+  const float s0 = (r & 1) ? -1.0f : 1.0f, s1 = (r & 2) ? -1.0f : 1.0f, s3 = (r & 8) ? -1.0f : 1.0f;
+  asm(NVFP4KV_DPP8("v_fmac_f32_dpp", "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1")
+      : NVFP4KV_X8(x) : "v"(s0));
+  asm(NVFP4KV_DPP8("v_fmac_f32_dpp", "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1")
+      : NVFP4KV_X8(x) : "v"(s1));
+  float y[8];
+#define NVFP4KV_PM4(I, J)                                                      \
+  "v_add_f32_dpp %" I ", %" J ", %" J " row_shl:4 row_mask:0xf bank_mask:0x5\n\t" \
+  "v_sub_f32_dpp %" I ", %" J ", %" J " row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+  asm("s_nop 4\n\t" NVFP4KV_PM4("0", "8") NVFP4KV_PM4("1", "9") NVFP4KV_PM4("2", "10") NVFP4KV_PM4("3", "11")
+          NVFP4KV_PM4("4", "12") NVFP4KV_PM4("5", "13") NVFP4KV_PM4("6", "14") NVFP4KV_PM4("7", "15")
+      : "=&v"(y[0]), "=&v"(y[1]), "=&v"(y[2]), "=&v"(y[3]), "=&v"(y[4]), "=&v"(y[5]), "=&v"(y[6]), "=&v"(y[7])
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+#undef NVFP4KV_PM4
+  asm(NVFP4KV_DPP8("v_fmac_f32_dpp", "row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1")
+      : NVFP4KV_X8(y) : "v"(s3));
+  const float sg = ((r ^ (r >> 1) ^ (r >> 3)) & 1) ? -1.0f : 1.0f;
+  const float c = sg * __uint_as_float(0x3DB504F3u);   // +-(float nearest 1/sqrt(128))
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = __builtin_fmaf(y[k], c, 0.0f);
+}
+#undef NVFP4KV_DPP8
+#undef NVFP4KV_X8
+
+// E2M1 codes of a lane's 8 values for block scale s, packed (value k in bits
+// 4k..4k+3).  Magnitudes by a three-level search over the same exact
+// thresholds as e2m1_code: 1.75s (>=) splits codes 0-3 from 4-7, then 0.75s
+// or 3.5s (>=), then 0.25s, 1.25s, 2.5s or 5s (>).  The thresholds increase
+// and each test is monotone in |y|, so the result is the count of thresholds
+// passed, as in e2m1_code; with s = 0 every threshold is +infinity and every
+// magnitude code 0.  Selects only, no branches; the seven thresholds are
+// made once and kept in registers.  Sign bits are gathered with byte
+// permutes: the top byte of each even value into one word, of each odd value
+// into another, then shifted and masked into bit 3 of each nibble.
+__device__ __forceinline__ uint32_t e2m1_codes8(const float (&x)[8], float s) {
+  if (s == 0.0f) s = __builtin_inff();
+  float T[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+#pragma unroll
+  for (int i = 0; i < 7; ++i) asm volatile("" : "+v"(T[i]));
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float a = fabsf(x[k]);
+    const bool b2 = a >= T[3];
+    const float t1 = b2 ? T[5] : T[1];
+    const float lo = b2 ? T[4] : T[0], hi = b2 ? T[6] : T[2];
+    const bool b1 = a >= t1;
+    const bool b0 = a > (b1 ? hi : lo);
+    uint32_t m = (uint32_t)b2;
+    m = m + m + (uint32_t)b1;
+    m = m + m + (uint32_t)b0;
+    w |= m << (4 * k);
+  }
+  const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]), u2 = __float_as_uint(x[2]),
+                 u3 = __float_as_uint(x[3]), u4 = __float_as_uint(x[4]), u5 = __float_as_uint(x[5]),
+                 u6 = __float_as_uint(x[6]), u7 = __float_as_uint(x[7]);
+  // byte j of `ev`: the top byte of value 2j; of `od`: of value 2j + 1
+  const uint32_t ev = __builtin_amdgcn_perm(u2, u0, 0x0C0C0703u) | (__builtin_amdgcn_perm(u6, u4, 0x0C0C0703u) << 16);
+  const uint32_t od = __builtin_amdgcn_perm(u3, u1, 0x0C0C0703u) | (__builtin_amdgcn_perm(u7, u5, 0x0C0C0703u) << 16);
+  return w | ((ev >> 4) & 0x08080808u) | (od & 0x80808080u);
 }
 
 // RoPE coefficients of lane r of a row (16 lanes, 8 elements each) at one
@@ -123,8 +195,8 @@ __device__ __forceinline__ void rope_lane(int r, int rotary_dim, const float* co
 // All 16 lanes of a row must call it together.
 template <bool GR>
 __device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, int rotary_dim,
-                                             const RopeLane& rl, bool hadamard, uint32_t neg, uint32_t& codes,
-                                             uint32_t& scode) {
+                                             const RopeLane& rl, bool hadamard, uint32_t neg, bool neg_any,
+                                             uint32_t& codes, uint32_t& scode) {
 #pragma clang fp contract(off)
   const int lane = (int)__lane_id();
   if (GR && rope && (rotary_dim & 15) != 0) {
@@ -140,9 +212,17 @@ __device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, in
     }
   }
   if (hadamard) {
+    if (neg_any) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if ((neg >> k) & 1u) x[k] = -x[k];
+      for (int k = 0; k < 8; ++k)
+        if ((neg >> k) & 1u) x[k] = -x[k];
+    }
+    // a -0 among the wavefront's inputs (its bit pattern is the least int)
+    int lo = min(min(__float_as_int(x[0]), __float_as_int(x[1])), __float_as_int(x[2]));
+    lo = min(min(lo, __float_as_int(x[3])), __float_as_int(x[4]));
+    lo = min(min(lo, __float_as_int(x[5])), __float_as_int(x[6]));
+    lo = min(lo, __float_as_int(x[7]));
+    const bool neg_zero = __builtin_amdgcn_ballot_w64(lo == (int)0x80000000) != 0;
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -153,25 +233,23 @@ __device__ __forceinline__ void append_row16(float (&x)[8], int r, bool rope, in
         x[k + h] = a - b;
       }
     }
-    fwht_stage<1>(x, r);
-    fwht_stage<2>(x, r);
-    fwht_stage<4>(x, r);
-    fwht_stage<8>(x, r);
-    const float inv_sqrt128 = __uint_as_float(0x3DB504F3u);
+    if (__builtin_expect(neg_zero, 0)) {
+      fwht_stage<1>(x, r);
+      fwht_stage<2>(x, r);
+      fwht_stage<4>(x, r);
+      fwht_stage<8>(x, r);
+      const float inv_sqrt128 = __uint_as_float(0x3DB504F3u);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = x[k] * inv_sqrt128;
+      for (int k = 0; k < 8; ++k) x[k] = x[k] * inv_sqrt128;
+    } else {
+      fwht_cross_lanes(x, r);
+    }
   }
   float am = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(x[k]));
   am = fmaxf(am, xor_lane<1>(am));
-  scode = e4m3_scale_code(am);
-  const float s = e4m3_value(scode);
-  const float t[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) w |= e2m1_code_search(x[k], t, s) << (4 * k);
-  codes = w;
+  codes = e2m1_codes8(x, e4m3_scale_fast(am, scode));
 }
 
 // A lane's 8 inputs of a row as raw words: bf16 (DT 1) takes 4 words, f32
@@ -180,19 +258,6 @@ template <int DT>
 struct RawRow {
   uint32_t w[DT == 1 ? 4 : 8];
 };
-
-template <int DT>
-__device__ __forceinline__ void load_raw(const void* src, size_t elem_off, RawRow<DT>& rw) {
-  if (DT == 1) {
-    const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + elem_off);
-    rw.w[0] = q.x; rw.w[1] = q.y; rw.w[2] = q.z; rw.w[3] = q.w;
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + elem_off);
-    const uint4 a = p[0], b = p[1];
-    rw.w[0] = a.x; rw.w[1] = a.y; rw.w[2] = a.z; rw.w[3] = a.w;
-    rw.w[4] = b.x; rw.w[5] = b.y; rw.w[6] = b.z; rw.w[7] = b.w;
-  }
-}
 
 template <int DT>
 __device__ __forceinline__ void raw_to_float(const RawRow<DT>& rw, float (&x)[8]) {
@@ -207,23 +272,26 @@ __device__ __forceinline__ void raw_to_float(const RawRow<DT>& rw, float (&x)[8]
   }
 }
 
-// One workgroup (8 wavefronts) per run of 64 consecutive tokens, every kv
-// head in turn, in passes of 16 tokens: wavefronts 0-3 take the 16 tokens' K
-// rows, 4-7 their V rows (4 rows of 16 lanes each), so every wavefront's rows
-// are all K or all V and only K rows run RoPE and the rotation.  The kv heads
-// of a token share its RoPE table rows, read once into the CU's L2.
-// Software pipeline over a wavefront's rows: an iteration first issues the
-// loads of its own RoPE coefficients, then those of the next row (its
-// token's slot and position and the row itself, unconditionally, with the
-// indices clamped), then quantizes its row; so a row's chain of dependent
-// loads (position, then table) overlaps the quantization of the row before
-// (one row per chain and nothing in flight meanwhile made the kernel bound
-// by load latency).  Consecutive tokens of a prefill sit in consecutive
-// slots, whose code bytes share 128-byte lines (16 bytes per token in the K
-// tiles, 4 in the V tiles) and whose scale bytes do too: one workgroup
-// completes those lines in its CU's L2.  Spread over workgroups (and so over
-// XCDs), each line was written back in pieces: twice the algorithmic write
-// traffic, measured.
+// Kv heads whose blocks a workgroup assembles in LDS at a time (36 KB).
+constexpr int kStageHeads = 4;
+
+// One workgroup (8 wavefronts) per run of 64 consecutive tokens, in passes
+// of 16 tokens: wavefronts 0-3 take the K rows of a pass (4 tokens each, one
+// row of 16 lanes per token), 4-7 its V rows, so every wavefront's rows are
+// all K or all V and only K rows run RoPE and the rotation.  A wavefront
+// goes through the kv heads of its 4 tokens before the next pass: the
+// tokens' slots, positions and RoPE coefficients are read once per pass,
+// and a row's input address differs from the one before by a constant.
+// The inputs of the next row are loaded before the current row is
+// quantized, so their latency overlaps its arithmetic.
+//
+// Stores.  When the run's 64 tokens sit in the 64 consecutive slots of one
+// page (the common case in prefill), the workgroup assembles the blocks of
+// up to 4 kv heads in LDS and writes them out as whole 16-byte words, every
+// 128-byte line at once; a line written in pieces is written back to HBM
+// in pieces, which cost a sixth more write traffic than the bytes.  Other
+// runs (a partial page, scattered slots, a pool with fp16 V) store each
+// row's code word and scale byte in place.
 template <int DT, bool GR>
 __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_tok,
@@ -231,6 +299,7 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, SignMask signs, float k_inv, float v_inv, int v_format, int block_bytes, int ks_off) {
+  __shared__ __attribute__((aligned(16))) uint8_t img[kStageHeads * kBlockBytes];
   const int lane = (int)__lane_id();
   const int r = lane & 15;
   const int wv = (int)(threadIdx.x >> 6);
@@ -239,68 +308,118 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
   const int rot = which ? 0 : rotary_dim;
   const bool had = which ? false : (hadamard != 0);
   const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
-  const void* src = which ? v : k;
-  const float inv = which ? v_inv : k_inv;   // 1 / the global scale
-  const int n_it = 4 * hkv;
-  // token of iteration `it` (kv head it % hkv, pass it / hkv); lanes past
-  // the last token take a copy of the last token's row of their kind (they
-  // still take part in the shuffles) and store nothing
-  auto token = [&](int it) {
-    return min((int)blockIdx.x * 64 + (it / hkv) * 16 + (wv & 3) * 4 + (lane >> 4), n_tok - 1);
+  const bool neg_any = !which && hadamard == 2;    // the randomized rotation's negations
+  const float inv = which ? v_inv : k_inv;         // 1 / the global scale
+  const int tok0 = (int)blockIdx.x * 64;
+
+  // the run fills one page: 64 tokens, consecutive slots from a page start
+  bool fills = false;
+  if (threadIdx.x < 64) {
+    const int64_t s0 = slots[min(tok0, n_tok - 1)];
+    fills = tok0 + 63 < n_tok && s0 % kPageSize == 0 && slots[tok0 + threadIdx.x] == s0 + (int64_t)threadIdx.x;
+  } else {
+    fills = true;
+  }
+  const bool staged = v_format == 0 && __syncthreads_and(fills);
+  const int64_t run_page = staged ? slots[tok0] / kPageSize : 0;
+
+  // row of this lane in pass p: token tok0 + 16p + 4(wv % 4) + lane / 16;
+  // lanes past the last token take the last token's rows (they still take
+  // part in the cross-lane steps) and store nothing
+  const int lt0 = (wv & 3) * 4 + (lane >> 4);
+  const size_t row_elems = (size_t)hkv * kHeadDim;
+  const char* src = reinterpret_cast<const char*>(which ? v : k);
+  constexpr int kEs = DT == 1 ? 2 : 4;             // input element bytes
+  auto row_ptr = [&](int p) {
+    const int tok = min(tok0 + 16 * p + lt0, n_tok - 1);
+    return src + ((size_t)tok * row_elems + 8 * r) * kEs;
   };
-  // the next row's inputs, loaded one iteration ahead
-  auto fetch = [&](int it, int64_t& slot, int& pos, RawRow<DT>& rw) {
-    it = min(it, n_it - 1);
-    const int tok = token(it);
-    slot = slots[tok];
-    pos = rot > 0 ? positions[tok] : 0;
-    load_raw<DT>(src, ((size_t)tok * hkv + it % hkv) * kHeadDim + 8 * r, rw);
-  };
-  int64_t slot;
-  int pos;
-  RawRow<DT> rw;
-  fetch(0, slot, pos, rw);
-#pragma unroll 1
-  for (int it = 0; it < n_it; ++it) {
-    const int g = it % hkv;
-    const bool active = (int)blockIdx.x * 64 + (it / hkv) * 16 + (wv & 3) * 4 + (lane >> 4) < n_tok;
-    RopeLane rl;
-    if (rot > 0)
-      rope_lane<GR>(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
-                    rope_sin + (size_t)pos * (rotary_dim / 2), rl);
-    __builtin_amdgcn_sched_barrier(0);
-    int64_t slot_n;
-    int pos_n;
-    RawRow<DT> rw_n;
-    fetch(it + 1, slot_n, pos_n, rw_n);
-    __builtin_amdgcn_sched_barrier(0);
-    float x[8];
-    raw_to_float<DT>(rw, x);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] *= inv;
-    const int64_t page = slot / kPageSize;
-    const uint32_t t = (uint32_t)(slot % kPageSize);
-    uint8_t* blk = pool + (((size_t)layer * (size_t)num_pages + (size_t)page) * (size_t)hkv + g) *
-                              (size_t)block_bytes;
-    if (vf16) {
-      // V kept in fp16: element 8r + k rounded to nearest even, into its tile
-      if (active) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          *reinterpret_cast<uint16_t*>(blk + v16_off(t, (uint32_t)(8 * r + k))) = (uint16_t)f16_bits(x[k]);
-      }
+  auto load_row = [&](const char* ptr, RawRow<DT>& rw) {
+    if (DT == 1) {
+      const uint4 q = *reinterpret_cast<const uint4*>(ptr);
+      rw.w[0] = q.x; rw.w[1] = q.y; rw.w[2] = q.z; rw.w[3] = q.w;
     } else {
-      uint32_t codes, scode;
-      append_row16<GR>(x, r, rot > 0, rot, rl, had, neg, codes, scode);
-      if (active) {
-        const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
-        *reinterpret_cast<uint32_t*>(blk + woff) = codes;
-        if ((r & 1) == 0) blk[(which ? kVScaleOff : ks_off) + 8 * t + r / 2] = (uint8_t)scode;
-      }
+      const uint4 a = reinterpret_cast<const uint4*>(ptr)[0], b = reinterpret_cast<const uint4*>(ptr)[1];
+      rw.w[0] = a.x; rw.w[1] = a.y; rw.w[2] = a.z; rw.w[3] = a.w;
+      rw.w[4] = b.x; rw.w[5] = b.y; rw.w[6] = b.z; rw.w[7] = b.w;
     }
-    slot = slot_n;
-    pos = pos_n;
-    rw = rw_n;
+  };
+  auto tok_of = [&](int p) { return min(tok0 + 16 * p + lt0, n_tok - 1); };
+
+#pragma unroll 1
+  for (int g0 = 0; g0 < hkv; g0 += kStageHeads) {
+    const int G = min(kStageHeads, hkv - g0);
+    int64_t slot = slots[tok_of(0)];
+    int pos = rot > 0 ? positions[tok_of(0)] : 0;
+    const char* rp = row_ptr(0) + (size_t)g0 * kHeadDim * kEs;
+    RawRow<DT> rw;
+    load_row(rp, rw);
+#pragma unroll 1
+    for (int p = 0; p < 4; ++p) {
+      const bool active = tok0 + 16 * p + lt0 < n_tok;
+      RopeLane rl;
+      if (rot > 0)
+        rope_lane<GR>(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
+                      rope_sin + (size_t)pos * (rotary_dim / 2), rl);
+      // the next pass's token
+      const int pn = min(p + 1, 3);
+      const int64_t slot_n = slots[tok_of(pn)];
+      const int pos_n = rot > 0 ? positions[tok_of(pn)] : 0;
+      const char* rp_n = row_ptr(pn) + (size_t)g0 * kHeadDim * kEs;
+      const uint32_t t = staged ? (uint32_t)(16 * p + lt0) : (uint32_t)(slot % kPageSize);
+      const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
+      const uint32_t soff = (which ? kVScaleOff : ks_off) + 8 * t + r / 2;
+      uint8_t* blk0 = pool + (((size_t)layer * (size_t)num_pages + (size_t)(slot / kPageSize)) * (size_t)hkv + g0) *
+                                 (size_t)block_bytes;
+#pragma unroll 1
+      for (int gl = 0; gl < G; ++gl) {
+        __builtin_amdgcn_sched_barrier(0);
+        RawRow<DT> rw_n;
+        load_row(gl + 1 < G ? rp + (size_t)(gl + 1) * kHeadDim * kEs : rp_n, rw_n);
+        __builtin_amdgcn_sched_barrier(0);
+        float x[8];
+        raw_to_float<DT>(rw, x);
+        if (inv != 1.0f) {   // (x * 1 is x: the common case skips it)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= inv;
+        }
+        uint8_t* blk = blk0 + (size_t)gl * (size_t)block_bytes;
+        if (vf16) {
+          // V kept in fp16: element 8r + e rounded to nearest even, into its tile
+          // (element 8r + e sits at the lane's offset plus 1024 e)
+          if (active) {
+            uint16_t* vb = reinterpret_cast<uint16_t*>(blk + v16_off(t, (uint32_t)(8 * r)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vb[512 * e] = (uint16_t)f16_bits(x[e]);
+          }
+        } else {
+          uint32_t codes, scode;
+          append_row16<GR>(x, r, rot > 0, rot, rl, had, neg, neg_any, codes, scode);
+          if (staged) {
+            uint8_t* b = img + gl * kBlockBytes;
+            *reinterpret_cast<uint32_t*>(b + woff) = codes;
+            if ((r & 1) == 0) b[soff] = (uint8_t)scode;
+          } else if (active) {
+            *reinterpret_cast<uint32_t*>(blk + woff) = codes;
+            if ((r & 1) == 0) blk[soff] = (uint8_t)scode;
+          }
+        }
+        rw = rw_n;
+      }
+      slot = slot_n;
+      pos = pos_n;
+      rp = rp_n;
+    }
+    if (staged) {
+      // the blocks of kv heads g0 .. g0+G-1 of the run's page are contiguous
+      __syncthreads();
+      uint4* dst = reinterpret_cast<uint4*>(
+          pool + (((size_t)layer * (size_t)num_pages + (size_t)run_page) * (size_t)hkv + g0) * (size_t)kBlockBytes);
+      const uint4* from = reinterpret_cast<const uint4*>(img);
+      const int n16 = G * (kBlockBytes / 16);
+      for (int c = (int)threadIdx.x; c < n16; c += 512) dst[c] = from[c];
+      __syncthreads();
+    }
   }
 }
 

@@ -78,6 +78,32 @@ __host__ __device__ inline uint32_t e4m3_scale_code(float amax) {
   return ((e - 120u) << 3) | m;              // E4M3 bias 7 = 127 - 120
 }
 
+// The same block scale (code and value, equal to e4m3_scale_code and
+// e4m3_value of it for every non-negative binary32 amax, +infinity
+// included) in a few operations and no branch.  amax/6: q0 = amax * fl(1/6)
+// corrected once with the exact remainder amax - 6 q0 (two fused
+// multiply-adds); this is the correctly rounded quotient except where it is
+// subnormal, far below the smallest scale.  Rounding to the E4M3 grid (3
+// mantissa bits, spacing 2^-9 below 2^-6) by adding and subtracting
+// M = 1.5 * 2^(e + 20), e the quotient's exponent clamped to [-6, 8]: the sum
+// lands in M's binade, whose spacing is the grid's, so the addition rounds to
+// the grid (nearest, ties to even) and the subtraction is exact.  Values
+// from 464 up round to 480 or more and saturate to 448.  The code follows
+// from the value's bits (normal) or value * 2^9 (subnormal).
+__host__ __device__ inline float e4m3_scale_fast(float amax, uint32_t& code) {
+#pragma clang fp contract(off)
+  const float c6 = 0x1.555556p-3f;           // the float nearest 1/6
+  const float q0 = amax * c6;
+  const float x = fmaf(fmaf(-q0, 6.0f, amax), c6, q0);
+  uint32_t eb = __builtin_bit_cast(uint32_t, x) >> 23;
+  eb = eb < 121u ? 121u : eb > 135u ? 135u : eb;
+  const float m = __builtin_bit_cast(float, ((eb + 20u) << 23) | 0x400000u);
+  float s = (x + m) - m;
+  s = fminf(s, 448.0f);
+  code = s >= 0.015625f ? (__builtin_bit_cast(uint32_t, s) >> 20) - 960u : (uint32_t)(s * 512.0f);
+  return s;
+}
+
 // E4M3 code -> float (exact).  Codes are never NaN here.
 __host__ __device__ inline float e4m3_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
