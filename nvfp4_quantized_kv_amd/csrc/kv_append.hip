@@ -272,26 +272,29 @@ __device__ __forceinline__ void raw_to_float(const RawRow<DT>& rw, float (&x)[8]
   }
 }
 
-// Kv heads whose blocks a workgroup assembles in LDS at a time (36 KB).
-constexpr int kStageHeads = 4;
-
-// One workgroup (8 wavefronts) per run of 64 consecutive tokens, in passes
-// of 16 tokens: wavefronts 0-3 take the K rows of a pass (4 tokens each, one
-// row of 16 lanes per token), 4-7 its V rows, so every wavefront's rows are
-// all K or all V and only K rows run RoPE and the rotation.  A wavefront
-// goes through the kv heads of its 4 tokens before the next pass: the
-// tokens' slots, positions and RoPE coefficients are read once per pass,
-// and a row's input address differs from the one before by a constant.
-// The inputs of the next row are loaded before the current row is
-// quantized, so their latency overlaps its arithmetic.
+// One workgroup (8 wavefronts) per range of tokens, in passes of 16 tokens:
+// wavefronts 0-3 take the K rows of a pass (4 tokens each, one row of 16
+// lanes per token), 4-7 its V rows, so every wavefront's rows are all K or
+// all V and only K rows run RoPE and the rotation.  A wavefront goes through
+// the kv heads of its 4 tokens before the next pass: RoPE coefficients are
+// read once per pass, and a row's input address differs from the one before
+// by a constant.  The inputs of the next row are loaded before the current
+// row is quantized, so their latency overlaps its arithmetic.
 //
-// Stores.  When the run's 64 tokens sit in the 64 consecutive slots of one
-// page (the common case in prefill), the workgroup assembles the blocks of
-// up to 4 kv heads in LDS and writes them out as whole 16-byte words, every
-// 128-byte line at once; a line written in pieces is written back to HBM
-// in pieces, which cost a sixth more write traffic than the bytes.  Other
-// runs (a partial page, scattered slots, a pool with fp16 V) store each
-// row's code word and scale byte in place.
+// Ranges follow the pool's line groups.  A line group is 16 slots of a page
+// from a multiple of 16; per (page, kv head) block it owns whole 128-byte
+// lines (1024 bytes of K codes, 1024 of V codes, 128 of each scale) that no
+// other slot touches.  Workgroup w takes tokens [a_w, a_{w+1}), a_w the first
+// token from 64w on that starts a line group (its slot a multiple of 16, or
+// not the slot after the previous token's), which lies within 16 tokens of
+// 64w; its passes start at a_w, so the 16 tokens of a group are quantized
+// in one pass and their lines filled at once.  No line is then written by
+// two workgroups (unless the slots jump inside a group) nor in two pieces
+// far apart in time; either way a line goes back to HBM in pieces, and
+// 64-token ranges that ignored the groups cost a seventh more write traffic
+// than the bytes.  The slots and positions of the 80 tokens from 64w are
+// read once, in the same round trip as the range's bounds, and each pass
+// takes its tokens' from the lanes that hold them.
 template <int DT, bool GR>
 __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     uint8_t* __restrict__ pool, int64_t num_pages, int hkv, int layer, int n_tok,
@@ -299,41 +302,61 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
     const int64_t* __restrict__ slots, const int32_t* __restrict__ positions,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin, int rotary_dim,
     int hadamard, SignMask signs, float k_inv, float v_inv, int v_format, int block_bytes, int ks_off) {
-  __shared__ __attribute__((aligned(16))) uint8_t img[kStageHeads * kBlockBytes];
   const int lane = (int)__lane_id();
   const int r = lane & 15;
-  const int wv = (int)(threadIdx.x >> 6);
+  // the wavefront's index, made wave-uniform for the compiler: every choice
+  // derived from it (K or V rows, the transform, the fp16 V store) is then a
+  // scalar branch rather than masked lanes
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int which = wv >> 2;                       // 0 = K, 1 = V
-  const bool vf16 = which && v_format;             // V rows kept in fp16 (uniform per wavefront)
+  const bool vf16 = which && v_format;             // V rows kept in fp16
   const int rot = which ? 0 : rotary_dim;
   const bool had = which ? false : (hadamard != 0);
   const uint32_t neg = which ? 0u : lane_signs(hadamard, signs, r);
   const bool neg_any = !which && hadamard == 2;    // the randomized rotation's negations
   const float inv = which ? v_inv : k_inv;         // 1 / the global scale
-  const int tok0 = (int)blockIdx.x * 64;
+  const int lt0 = (wv & 3) * 4 + (lane >> 4);      // the lane's token within a pass
 
-  // the run fills one page: 64 tokens, consecutive slots from a page start
-  bool fills = false;
-  if (threadIdx.x < 64) {
-    const int64_t s0 = slots[min(tok0, n_tok - 1)];
-    fills = tok0 + 63 < n_tok && s0 % kPageSize == 0 && slots[tok0 + threadIdx.x] == s0 + (int64_t)threadIdx.x;
-  } else {
-    fills = true;
-  }
-  const bool staged = v_format == 0 && __syncthreads_and(fills);
-  const int64_t run_page = staged ? slots[tok0] / kPageSize : 0;
-
-  // row of this lane in pass p: token tok0 + 16p + 4(wv % 4) + lane / 16;
-  // lanes past the last token take the last token's rows (they still take
-  // part in the cross-lane steps) and store nothing
-  const int lt0 = (wv & 3) * 4 + (lane >> 4);
-  const size_t row_elems = (size_t)hkv * kHeadDim;
-  const char* src = reinterpret_cast<const char*>(which ? v : k);
-  constexpr int kEs = DT == 1 ? 2 : 4;             // input element bytes
-  auto row_ptr = [&](int p) {
-    const int tok = min(tok0 + 16 * p + lt0, n_tok - 1);
-    return src + ((size_t)tok * row_elems + 8 * r) * kEs;
+  // the window: tokens 64w + lane (wa) and 64w + 64 + lane (wb, lanes 0-15),
+  // with the slot of the token before each
+  const int w64 = (int)blockIdx.x * 64;
+  const int ia = min(w64 + lane, n_tok - 1), ib = min(w64 + 64 + (lane & 15), n_tok - 1);
+  const int64_t sa = slots[ia], sb = slots[ib];
+  const int64_t pa = slots[max(ia - 1, 0)], pb = slots[max(ib - 1, 0)];
+  const int qa = rot > 0 ? positions[ia] : 0, qb = rot > 0 ? positions[ib] : 0;
+  // a line-group start before token i (slot s, previous slot sp)
+  auto starts = [&](int i, int64_t s, int64_t sp) { return i <= 0 || i >= n_tok || s % 16 == 0 || s != sp + 1; };
+  const uint64_t sm = __builtin_amdgcn_ballot_w64(lane < 16 ? starts(w64 + lane, sa, pa)
+                                                  : lane < 32 ? starts(w64 + 64 + (lane & 15), sb, pb) : false);
+  const int ra = min(w64 + (int)__builtin_ctzll((sm & 0xFFFFull) | 0x10000ull), n_tok);
+  const int rb = min(w64 + 64 + (int)__builtin_ctzll(((sm >> 16) & 0xFFFFull) | 0x10000ull), n_tok);
+  const int n_pass = (rb - ra + 15) / 16;          // at most 5: a range holds at most 79 tokens
+  // the lane's token in pass p (lanes past the range take its last token's
+  // rows: they still take part in the cross-lane steps, and store nothing),
+  // with its slot and position from the window
+  auto token = [&](int p, bool& valid, int64_t& slot, int& pos) {
+    const int t = ra + 16 * p + lt0;
+    valid = t < rb;
+    const int tc = valid ? t : rb - 1;
+    const int j = tc - w64;                        // 0 .. 78
+    const int src = (j & 63) << 2;
+    const int lo = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)sa);
+    const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(sa >> 32));
+    const int lo2 = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)sb);
+    const int hi2 = __builtin_amdgcn_ds_bpermute(src, (int)(uint32_t)(sb >> 32));
+    slot = j < 64 ? (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo)
+                  : (int64_t)(((uint64_t)(uint32_t)hi2 << 32) | (uint32_t)lo2);
+    pos = 0;
+    if (rot > 0) {
+      const int p1 = __builtin_amdgcn_ds_bpermute(src, qa), p2 = __builtin_amdgcn_ds_bpermute(src, qb);
+      pos = j < 64 ? p1 : p2;
+    }
+    return tc;
   };
+
+  const size_t row_elems = (size_t)hkv * kHeadDim;
+  constexpr int kEs = DT == 1 ? 2 : 4;             // input element bytes
+  const char* src = reinterpret_cast<const char*>(which ? v : k);
   auto load_row = [&](const char* ptr, RawRow<DT>& rw) {
     if (DT == 1) {
       const uint4 q = *reinterpret_cast<const uint4*>(ptr);
@@ -344,29 +367,31 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
       rw.w[4] = b.x; rw.w[5] = b.y; rw.w[6] = b.z; rw.w[7] = b.w;
     }
   };
-  auto tok_of = [&](int p) { return min(tok0 + 16 * p + lt0, n_tok - 1); };
+  // the lane's 8 inputs of kv head g of token t
+  auto row_ptr = [&](int t, int g) { return src + ((size_t)t * row_elems + (size_t)g * kHeadDim + 8 * r) * kEs; };
 
 #pragma unroll 1
-  for (int g0 = 0; g0 < hkv; g0 += kStageHeads) {
-    const int G = min(kStageHeads, hkv - g0);
-    int64_t slot = slots[tok_of(0)];
-    int pos = rot > 0 ? positions[tok_of(0)] : 0;
-    const char* rp = row_ptr(0) + (size_t)g0 * kHeadDim * kEs;
+  for (int g0 = 0; g0 < hkv; g0 += 4) {
+    const int G = min(4, hkv - g0);
+    bool valid;
+    int64_t slot;
+    int pos;
+    const char* rp = row_ptr(token(0, valid, slot, pos), g0);
     RawRow<DT> rw;
     load_row(rp, rw);
 #pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-      const bool active = tok0 + 16 * p + lt0 < n_tok;
+    for (int p = 0; p < n_pass; ++p) {
+      const bool active = valid;
       RopeLane rl;
       if (rot > 0)
         rope_lane<GR>(r, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
                       rope_sin + (size_t)pos * (rotary_dim / 2), rl);
       // the next pass's token
-      const int pn = min(p + 1, 3);
-      const int64_t slot_n = slots[tok_of(pn)];
-      const int pos_n = rot > 0 ? positions[tok_of(pn)] : 0;
-      const char* rp_n = row_ptr(pn) + (size_t)g0 * kHeadDim * kEs;
-      const uint32_t t = staged ? (uint32_t)(16 * p + lt0) : (uint32_t)(slot % kPageSize);
+      bool valid_n;
+      int64_t slot_n;
+      int pos_n;
+      const char* rp_n = row_ptr(token(min(p + 1, n_pass - 1), valid_n, slot_n, pos_n), g0);
+      const uint32_t t = (uint32_t)(slot % kPageSize);
       const uint32_t woff = which ? v_code_word_off(t, (uint32_t)r) : k_code_word_off(t, (uint32_t)r);
       const uint32_t soff = (which ? kVScaleOff : ks_off) + 8 * t + r / 2;
       uint8_t* blk0 = pool + (((size_t)layer * (size_t)num_pages + (size_t)(slot / kPageSize)) * (size_t)hkv + g0) *
@@ -395,30 +420,17 @@ __global__ __launch_bounds__(512) void kv_quant_append_kernel(
         } else {
           uint32_t codes, scode;
           append_row16<GR>(x, r, rot > 0, rot, rl, had, neg, neg_any, codes, scode);
-          if (staged) {
-            uint8_t* b = img + gl * kBlockBytes;
-            *reinterpret_cast<uint32_t*>(b + woff) = codes;
-            if ((r & 1) == 0) b[soff] = (uint8_t)scode;
-          } else if (active) {
+          if (active) {
             *reinterpret_cast<uint32_t*>(blk + woff) = codes;
             if ((r & 1) == 0) blk[soff] = (uint8_t)scode;
           }
         }
         rw = rw_n;
       }
+      valid = valid_n;
       slot = slot_n;
       pos = pos_n;
       rp = rp_n;
-    }
-    if (staged) {
-      // the blocks of kv heads g0 .. g0+G-1 of the run's page are contiguous
-      __syncthreads();
-      uint4* dst = reinterpret_cast<uint4*>(
-          pool + (((size_t)layer * (size_t)num_pages + (size_t)run_page) * (size_t)hkv + g0) * (size_t)kBlockBytes);
-      const uint4* from = reinterpret_cast<const uint4*>(img);
-      const int n16 = G * (kBlockBytes / 16);
-      for (int c = (int)threadIdx.x; c < n16; c += 512) dst[c] = from[c];
-      __syncthreads();
     }
   }
 }
