@@ -102,17 +102,20 @@ def stream_read_ceiling_gbps(step, wl, torch, kv) -> float:
 
 def traffic_from_profiles(kernel_tag: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source (same hash); else None."""
+    taken on the current kernel source and headers (same hashes); else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_{workload}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "nvfp4_quantized_kv_amd", "csrc", rec.get("source", "decode_attn.hip"))
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if h != rec.get("source_sha256"):
-        return None
+    csrc = os.path.join(ROOT, "nvfp4_quantized_kv_amd", "csrc")
+    want = dict(rec.get("header_sha256", {}))
+    want[rec.get("source", "decode_attn.hip")] = rec.get("source_sha256")
+    for name, digest in want.items():
+        # the kernel's source and the headers it includes, as when counted
+        if hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest() != digest:
+            return None
     return rec.get("hbm_bytes_per_launch")
 
 
