@@ -273,12 +273,60 @@ struct QCols {
 // (MQ) the rows' positions instead, their coefficients being loaded per pass
 // when the operands are made (one set per pass would hold 16 more registers
 // per pass through the page loads).
+// A lane's query inputs as loaded: the 8 elements of each pass as raw
+// words (bf16: w[.][0]; f32: both), unpacked only where the operands are
+// made, so no instruction waits for these loads before the first page loads
+// are issued (the wait counter is in order: a load read early would be
+// waited for with everything issued before it).
 template <int kPasses, bool MQ>
 struct QIn {
-  float x[kPasses][8];
-  float cv[8], sv[8];
+  u4 w[kPasses][2];
+  u4 rc[2], rs[2];   // RoPE cos / sin of the lane's 8 elements, as loaded
   int pos[MQ ? kPasses : 1];
+  int dtype;
 };
+
+__device__ __forceinline__ void q_unpack(const u4 (&w)[2], int dtype, float (&x)[8]) {
+  if (dtype == 1) {   // bf16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[0][i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[0][i] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = __uint_as_float(w[0][i]);
+      x[4 + i] = __uint_as_float(w[1][i]);
+    }
+  }
+}
+
+// RoPE coefficients of a lane's 8 query elements (those of rope_coeffs), as
+// loaded: lanes past the rotary part read the row's first 8 pairs, which the
+// rotation does not use, instead of taking zeros, so nothing selects on (and
+// waits for) these loads before the rotation itself.  Rows of R/2 floats,
+// R a multiple of 16, start on 32-byte boundaries.
+template <bool GR>
+__device__ __forceinline__ void rope_coeffs_q(int r, int rotary_dim, const float* __restrict__ cos_row,
+                                              const float* __restrict__ sin_row, u4 (&rc)[2], u4 (&rs)[2]) {
+  if constexpr (GR) {
+    float cv[8], sv[8];
+    rope_coeffs<true>(r, rotary_dim, cos_row, sin_row, cv, sv);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rc[k / 4][k % 4] = __float_as_uint(cv[k]);
+      rs[k / 4][k % 4] = __float_as_uint(sv[k]);
+    }
+  } else {
+    const int half = rotary_dim / 2, hl = half / 8;
+    const int base = r < hl ? 8 * r : r < 2 * hl ? 8 * r - half : 0;
+    rc[0] = *reinterpret_cast<const u4*>(cos_row + base);
+    rc[1] = *reinterpret_cast<const u4*>(cos_row + base + 4);
+    rs[0] = *reinterpret_cast<const u4*>(sin_row + base);
+    rs[1] = *reinterpret_cast<const u4*>(sin_row + base + 4);
+  }
+}
 
 template <int kPasses, bool MQ>
 __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, const QCols& qc,
@@ -290,26 +338,30 @@ __device__ __forceinline__ void load_q_inputs(int sg, int hkv, int n_q_heads, co
   const int lane = (int)threadIdx.x;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int seq = sg / hkv, kvh = sg % hkv;
+  in.dtype = q_dtype;
+  const bool bf16 = q_dtype == 1;
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int col = min(pass * 4 + g4, qc.group - 1);
     const int tok = MQ ? qc.qtok0 + col / qc.heads : 0;
     const int h = MQ ? col % qc.heads : col;
-    load8(q, q_dtype,
-          (((size_t)seq * (MQ ? qc.n_qtok : 1) + tok) * n_q_heads + (size_t)kvh * qc.heads + h) * kHeadDim +
-              8 * c16,
-          in.x[pass]);
+    const size_t e0 =
+        (((size_t)seq * (MQ ? qc.n_qtok : 1) + tok) * n_q_heads + (size_t)kvh * qc.heads + h) * kHeadDim +
+        8 * c16;
+    // the lane's 16 (bf16) or 32 (f32) bytes; bf16 reads its 16 twice
+    const uint8_t* p0 = static_cast<const uint8_t*>(q) + e0 * (bf16 ? 2 : 4);
+    in.w[pass][0] = *reinterpret_cast<const u4*>(p0);
+    in.w[pass][1] = *reinterpret_cast<const u4*>(bf16 ? p0 : p0 + 16);
     if (MQ) in.pos[pass] = rotary_dim > 0 ? q_positions[(size_t)seq * qc.n_qtok + tok] : 0;
   }
   if (!MQ) {
-    if (rotary_dim > 0) {
-      const int pos = q_positions[seq];
-      rope_coeffs<kGR>(c16, rotary_dim, rope_cos + (size_t)pos * (rotary_dim / 2),
-                       rope_sin + (size_t)pos * (rotary_dim / 2), in.cv, in.sv);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
-    }
+    // loaded on both sides of the rotary test (no join to copy them across,
+    // which would wait for them): without RoPE the query rows stand in for
+    // the table, read and not used
+    const int pos = rotary_dim > 0 ? q_positions[seq] : 0;
+    const float* qf = static_cast<const float*>(q);
+    rope_coeffs_q<kGR>(c16, rotary_dim, rotary_dim > 0 ? rope_cos + (size_t)pos * (rotary_dim / 2) : qf,
+                       rotary_dim > 0 ? rope_sin + (size_t)pos * (rotary_dim / 2) : qf, in.rc, in.rs);
   }
 }
 
@@ -350,13 +402,19 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
     uint32_t codes, scode;
     if (MQ) {
       if (rotary_dim > 0)
-        rope_coeffs<kGR>(c16, rotary_dim, rope_cos + (size_t)in.pos[pass] * (rotary_dim / 2),
-                         rope_sin + (size_t)in.pos[pass] * (rotary_dim / 2), in.cv, in.sv);
+        rope_coeffs_q<kGR>(c16, rotary_dim, rope_cos + (size_t)in.pos[pass] * (rotary_dim / 2),
+                           rope_sin + (size_t)in.pos[pass] * (rotary_dim / 2), in.rc, in.rs);
       else
-#pragma unroll
-        for (int k = 0; k < 8; ++k) in.cv[k] = in.sv[k] = 0.0f;
+        in.rc[0] = in.rc[1] = in.rs[0] = in.rs[1] = u4{0u, 0u, 0u, 0u};
     }
-    quant_row16_v<kGR>(in.x[pass], c16, rotary_dim, in.cv, in.sv, hadamard != 0,
+    float x[8], cv[8], sv[8];
+    q_unpack(in.w[pass], in.dtype, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      cv[k] = __uint_as_float(in.rc[k / 4][k % 4]);
+      sv[k] = __uint_as_float(in.rs[k / 4][k % 4]);
+    }
+    quant_row16_v<kGR>(x, c16, rotary_dim, cv, sv, hadamard != 0,
                        lane_signs(hadamard, signs, c16), codes, scode);
     const float s = e4m3_value(scode);
     h8 qv;
@@ -822,7 +880,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     }
     const int j = (int)(x - lstart);
     w_blk = page_table[(size_t)lseq * pt_stride + j] * hkv + lkvh;
-    w_nv = (win + lane < b) ? seq_lens[lseq] - j * kPageSize : 0;
+    // the sequence's length as loaded: the page's valid tokens are taken
+    // where they are read (lanes past the range are never read)
+    w_nv = seq_lens[lseq];
     w_j = j;
     w_sg = lseq * hkv + lkvh;
   };
@@ -841,7 +901,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
                                              0, ok ? kBB : 0, 0x00020000);
   };
   auto nvalid_of = [&](int i) {
-    return i < npg ? __builtin_amdgcn_readlane(w_nv, i - wo) : 0;
+    return i < npg ? __builtin_amdgcn_readlane(w_nv, i - wo) - kPageSize * __builtin_amdgcn_readlane(w_j, i - wo)
+                   : 0;
   };
   // first page of a segment other than page a's
   auto starts_segment = [&](int i) {
