@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4kv.so")
 
 SOURCES = ["kv_append.hip", "decode_attn.hip", "decode_attn_gr.hip", "kv_spill.hip", "nvfp4kv_api.cpp"]
-HEADERS = ["nvfp4kv_codec.hpp", "nvfp4kv_internal.hpp"]
+HEADERS = ["nvfp4kv_codec.hpp", "nvfp4kv_internal.hpp", "nvfp4kv_rowq.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

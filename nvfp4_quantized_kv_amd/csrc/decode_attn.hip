@@ -41,6 +41,7 @@
 
 #include "nvfp4kv_codec.hpp"
 #include "nvfp4kv_internal.hpp"
+#include "nvfp4kv_rowq.hpp"
 
 // This file is compiled twice: as is, for rotary widths that are multiples
 // of 16 (the kernels the workloads run), and from decode_attn_gr.hip with
@@ -407,19 +408,31 @@ __device__ __forceinline__ void make_q_operands(QIn<kPasses, MQ>& in, int group,
       else
         in.rc[0] = in.rc[1] = in.rs[0] = in.rs[1] = u4{0u, 0u, 0u, 0u};
     }
-    float x[8], cv[8], sv[8];
+    // the append kernel's row quantizer (the NVFP4 round trip of K rows)
+    float x[8];
     q_unpack(in.w[pass], in.dtype, x);
+    rowq::RopeLane rl;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      cv[k] = __uint_as_float(in.rc[k / 4][k % 4]);
-      sv[k] = __uint_as_float(in.rs[k / 4][k % 4]);
+      rl.cv[k] = __uint_as_float(in.rc[k / 4][k % 4]);
+      rl.sv[k] = __uint_as_float(in.rs[k / 4][k % 4]);
     }
-    quant_row16_v<kGR>(x, c16, rotary_dim, cv, sv, hadamard != 0,
-                       lane_signs(hadamard, signs, c16), codes, scode);
-    const float s = e4m3_value(scode);
+    const int hl = rotary_dim / 16;   // lanes per rotary half
+    rl.first = c16 < hl;
+    rl.in_rot = c16 < 2 * hl;
+    rl.src = rl.in_rot ? (rl.first ? c16 + hl : c16 - hl) : c16;
+    rowq::append_row16<kGR>(x, c16, rotary_dim > 0, rotary_dim, rl, hadamard != 0,
+                            lane_signs(hadamard, signs, c16), hadamard == 2, codes, scode);
+    // exact fp16 operands: E2M1 values times 2^8, then the E4M3 scale times
+    // 2^-8 (the scale byte shifted left by 7 is its fp16 encoding)
+    const h2 sc = bits_h2((scode << 7) | (scode << 23));
     h8 qv;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) qv[k] = (_Float16)(e2m1_value((codes >> (4 * k)) & 15u) * s);
+    for (int b = 0; b < 4; ++b) {
+      const h2 v = fp4x2(codes, b) * sc;
+      qv[2 * b] = v[0];
+      qv[2 * b + 1] = v[1];
+    }
     if (h < group) *reinterpret_cast<h8*>(&rows[(h - 16 * t) * kHeadDim + 8 * c16]) = qv;
   }
   __syncthreads();
