@@ -258,6 +258,166 @@ __device__ inline int64_t page_of_unit(int64_t u, const int32_t* __restrict__ se
   return P;
 }
 
+// The sequences' page counts and the flat unit and page offsets of their
+// first segments, held across the wavefront: lane l of chunk c stands for
+// sequence 64c + l.  The lengths are read 8 per round trip and the offsets
+// are prefix sums by lane shuffles, so the lookups below are ballots and
+// register reads, where a walk over the sequences took one dependent load
+// per step (with 64 sequences, 40-110 us of a wavefront's start).  From
+// kWalkSeqs + 1 up to kScanSeqs sequences; otherwise the walks.
+// (vector types, not arrays: an array indexed in a loop before unrolling is
+// moved to LDS, one LDS round trip per access)
+constexpr int kScanChunks = 4;
+constexpr int kScanSeqs = 64 * kScanChunks;
+// Up to this many sequences the walks are cheaper (measured: three
+// sequences, 2.0 us to a wavefront's range against 2.5 us for the scan).
+constexpr int kWalkSeqs = 4;
+typedef int scan_i4 __attribute__((ext_vector_type(4)));
+typedef int64_t scan_l4 __attribute__((ext_vector_type(4)));
+struct SeqScan {
+  scan_i4 pg;   // per chunk: pages of the lane's sequence (0 past n_seq)
+  scan_l4 u0;   // flat unit index of its first segment
+  scan_l4 p0;   // flat page index of its first page
+  int64_t TU, TP;   // units and pages of all segments
+};
+
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)x >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ void seq_scan(const int32_t* __restrict__ seq_lens, int n_seq, int hkv, SeqScan& sc) {
+  const int lane = (int)__lane_id();
+  // the lengths through the scalar cache, 8 independent loads per wait,
+  // set into the lanes: every wavefront reads the same words at its start,
+  // and as one vector load per wavefront that hot line took 3-13 us
+  scan_i4 len;
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c) {
+    len[c] = 0;
+    if (64 * c < n_seq) {
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int base = 64 * c + 8 * g;
+        if (base < n_seq) {
+          int v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = seq_lens[min(base + i, n_seq - 1)];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) len[c] = lane == 8 * g + i ? v[i] : len[c];
+        }
+      }
+    }
+  }
+  int64_t uc = 0, pc = 0;
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c) {
+    const int sq = 64 * c + lane;
+    const int pg = sq < n_seq ? (len[c] + kPageSize - 1) / kPageSize : 0;
+    const int64_t u = sq < n_seq ? (int64_t)hkv * (pg + kSegExtra) : 0;
+    const int64_t p = (int64_t)hkv * pg;
+    int64_t ui = u, pi = p;
+    // (only the steps the chunk's sequences need; lanes past them keep
+    // partial sums, which are never read)
+    const int nc = min(n_seq - 64 * c, 64);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      if (d >= nc) break;
+      const int64_t ut = __shfl_up(ui, d, 64), pt = __shfl_up(pi, d, 64);
+      if (lane >= d) {
+        ui += ut;
+        pi += pt;
+      }
+    }
+    sc.pg[c] = pg;
+    sc.u0[c] = uc + ui - u;
+    sc.p0[c] = pc + pi - p;
+    if (nc > 0) {   // the chunk's totals: its last sequence's inclusive sums
+      uc += readlane64(ui, nc - 1);
+      pc += readlane64(pi, nc - 1);
+    }
+  }
+  sc.TU = uc;
+  sc.TP = pc;
+}
+
+// Chunk c (wave-uniform or per lane) of a scanned array.
+template <typename V>
+__device__ __forceinline__ auto scan_chunk(const V& v, int c) {
+  auto r = v[0];
+#pragma unroll
+  for (int k = 1; k < kScanChunks; ++k) r = c == k ? v[k] : r;
+  return r;
+}
+
+// Entry `src` (a lane index) of chunk c of a scanned array, c chosen per
+// lane: every chunk in use is shuffled and the reading lane picks its own
+// (a shuffle of an array chosen per lane would return the chunk the source
+// lane chose).
+template <typename V>
+__device__ __forceinline__ auto scan_shfl(const V& v, int c, int src, int n_seq) {
+  auto r = __shfl(v[0], src, 64);
+#pragma unroll
+  for (int k = 1; k < kScanChunks; ++k)
+    if (64 * k < n_seq) {
+      const auto t = __shfl(v[k], src, 64);
+      r = c == k ? t : r;
+    }
+  return r;
+}
+
+// Sequence s's page count and first unit / page (s wave-uniform, < n_seq).
+__device__ __forceinline__ int scan_pages(const SeqScan& sc, int s) {
+  return __builtin_amdgcn_readlane(scan_chunk(sc.pg, s >> 6), s & 63);
+}
+
+// The last sequence whose offset `off` (its first unit or page) is at or
+// before x; sequences with no pages share the offset of the next one, so
+// for a page x this is the sequence holding it.
+__device__ __forceinline__ int scan_seq_at(const scan_l4& off, int64_t x, int n_seq) {
+  const int lane = (int)__lane_id();
+  int n = 0;
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c)
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 * c + lane < n_seq && off[c] <= x));
+  return n - 1;
+}
+
+// page_of_unit from the scan.
+__device__ __forceinline__ int64_t scan_page_of_unit(const SeqScan& sc, int64_t u, int n_seq) {
+  if (u >= sc.TU) return sc.TP;
+  const int sq = scan_seq_at(sc.u0, u, n_seq);
+  const int64_t U = readlane64(scan_chunk(sc.u0, sq >> 6), sq & 63);
+  const int64_t P = readlane64(scan_chunk(sc.p0, sq >> 6), sq & 63);
+  const int64_t pg = scan_pages(sc, sq);
+  const int64_t k = (u - U) / (pg + kSegExtra);
+  const int64_t off = (u - U) - k * (pg + kSegExtra);
+  return P + k * pg + min(off, pg);
+}
+
+// Per lane: the sequence holding flat page x (x < TP), by a binary search
+// over the scanned first pages (every lane runs the same shuffle steps).
+__device__ __forceinline__ int scan_seq_of_page_lane(const SeqScan& sc, int64_t x, int n_seq) {
+  // chunk: the last one whose first sequence starts at or before x
+  int c = 0;
+#pragma unroll
+  for (int k = 1; k < kScanChunks; ++k)
+    if (64 * k < n_seq && readlane64(sc.p0[k], 0) <= x) c = k;
+  const int nv = min(n_seq - 64 * c, 64);   // valid lanes of the chunk
+  // (steps below the largest chunk in use: the others probe past its end)
+  const int span = min(n_seq, 64);
+  int lo = 0;
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1) {
+    if (step >= span) continue;
+    const int probe = lo + step;
+    const int64_t v = scan_shfl(sc.p0, c, probe & 63, n_seq);
+    if (probe < nv && v <= x) lo = probe;
+  }
+  return 64 * c + lo;
+}
+
 // Query columns.  A kernel pass works on `group` columns per kv head: the
 // query heads of the kv head (`heads` of them) for `group / heads`
 // consecutive query tokens starting at token qtok0 of the n_qtok new tokens
@@ -851,23 +1011,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   const int mcut = MQ ? qc.n_qtok - 1 - qc.qtok0 : 0;
   __builtin_amdgcn_s_setprio(3);
   const int64_t W = gridDim.x, w = blockIdx.x;
-  int64_t TP = 0;
-  for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
-  TP *= hkv;
-  const int64_t TU = TP + (int64_t)kSegExtra * n_seq * hkv;
+  // the sequences' offsets across the wavefront (kWalkSeqs + 1 up to
+  // kScanSeqs of them), else walks over the lengths
+  const bool scan = n_seq > kWalkSeqs && n_seq <= kScanSeqs;
+  SeqScan sc;
+  if (scan) seq_scan(seq_lens, n_seq, hkv, sc);
+  int64_t TU;
+  if (scan) {
+    TU = sc.TU;
+  } else {
+    int64_t TP = 0;
+    for (int s = 0; s < n_seq; ++s) TP += seq_pages(seq_lens, s);
+    TU = TP * hkv + (int64_t)kSegExtra * n_seq * hkv;
+  }
   // this wave's pages: those of its work units [w*TU/W, (w+1)*TU/W)
-  const int64_t a = page_of_unit((w * TU) / W, seq_lens, n_seq, hkv);
-  const int64_t b = page_of_unit(((w + 1) * TU) / W, seq_lens, n_seq, hkv);
+  const int64_t u_a = (w * TU) / W, u_b = ((w + 1) * TU) / W;
+  const int64_t a = scan ? scan_page_of_unit(sc, u_a, n_seq) : page_of_unit(u_a, seq_lens, n_seq, hkv);
+  const int64_t b = scan ? scan_page_of_unit(sc, u_b, n_seq) : page_of_unit(u_b, seq_lens, n_seq, hkv);
   if (a >= b) return;
 
   // segment holding page a: sequence, kv head, flat index of its first page
   int seq = 0;
   int64_t seq_base = 0;
-  int64_t pg = seq_pages(seq_lens, 0);
-  while (a >= seq_base + hkv * pg) {
-    seq_base += hkv * pg;
-    ++seq;
-    pg = seq_pages(seq_lens, seq);
+  int64_t pg;
+  if (scan) {
+    seq = scan_seq_at(sc.p0, a, n_seq);
+    seq_base = readlane64(scan_chunk(sc.p0, seq >> 6), seq & 63);
+    pg = scan_pages(sc, seq);
+  } else {
+    pg = seq_pages(seq_lens, 0);
+    while (a >= seq_base + hkv * pg) {
+      seq_base += hkv * pg;
+      ++seq;
+      pg = seq_pages(seq_lens, seq);
+    }
   }
   const int kvh0 = (int)((a - seq_base) / pg);
   const int seg0 = seq * hkv + kvh0;
@@ -878,19 +1055,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   const int npg = (int)(b - a);
   int wo = 0;
   int w_blk, w_nv, w_j, w_sg;
-  auto load_window = [&](int wseq, int wkvh, int64_t wstart, int64_t wpg) {
-    const int64_t win = a + wo;
-    int lseq = wseq, lkvh = wkvh;
-    int64_t lstart = wstart, lpg = wpg;
-    const int64_t x = min(win + lane, b - 1);
-    while (x >= lstart + lpg) {
-      lstart += lpg;
-      if (++lkvh == hkv) {
-        lkvh = 0;
-        ++lseq;
-        lpg = seq_pages(seq_lens, lseq);
-      }
-    }
+  // the window's entries for lanes whose page x lies in sequence lseq, kv
+  // head lkvh, whose segment starts at flat page lstart
+  auto set_window = [&](int lseq, int lkvh, int64_t lstart, int64_t x) {
     const int j = (int)(x - lstart);
     w_blk = page_table[(size_t)lseq * pt_stride + j] * hkv + lkvh;
     // the sequence's length as loaded: the page's valid tokens are taken
@@ -899,7 +1066,70 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
     w_j = j;
     w_sg = lseq * hkv + lkvh;
   };
-  load_window(seq, kvh0, seq_base + (int64_t)kvh0 * pg, pg);
+  // the window at wo by a walk from the segment holding page a + wo (the
+  // loop's reloads, and the first window past kScanSeqs sequences)
+  auto load_window = [&](int wseq, int wkvh, int64_t wstart, int64_t wpg) {
+    int lseq = wseq, lkvh = wkvh;
+    int64_t lstart = wstart, lpg = wpg;
+    const int64_t x = min(a + wo + lane, b - 1);
+    while (x >= lstart + lpg) {
+      lstart += lpg;
+      if (++lkvh == hkv) {
+        lkvh = 0;
+        ++lseq;
+        lpg = seq_pages(seq_lens, lseq);
+      }
+    }
+    set_window(lseq, lkvh, lstart, x);
+  };
+  if (scan) {
+    // the first window from the scan: each lane's sequence by search, its kv
+    // head and page by division (kept out of the lambdas, so the scan's
+    // registers are not addressed and die here)
+    const int64_t x = min(a + lane, b - 1);
+    const int lseq = scan_seq_of_page_lane(sc, x, n_seq);
+    const int c = lseq >> 6;
+    const int lpg = scan_shfl(sc.pg, c, lseq & 63, n_seq);
+    const int64_t sb = scan_shfl(sc.p0, c, lseq & 63, n_seq);
+    const uint32_t r = (uint32_t)(x - sb);   // < hkv * pages of one sequence
+    const int lkvh = (int)(r / (uint32_t)lpg);
+    set_window(lseq, lkvh, sb + (int64_t)lkvh * lpg, x);
+  } else {
+    load_window(seq, kvh0, seq_base + (int64_t)kvh0 * pg, pg);
+  }
+
+  // ---- the current token of every segment whose last page is in the range
+  // goes into the cache here (only this wavefront reads that page), and its
+  // stores land before that page's loads are issued.  A token whose page is
+  // among the range's first two pages is written before any page load;
+  // the others after the first two pages' loads are on their way, so the
+  // wavefront does not start late.
+  auto append_tokens = [&](bool first_pages) {
+    bool any = false;
+    int sq = seq, kv = kvh0;
+    int64_t sstart = seq_base + (int64_t)kvh0 * pg, pgl = pg;
+    while (sstart < b) {
+      const int64_t last = sstart + pgl - 1;
+      if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
+        append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
+                         q_positions, rope_cos, rope_sin, rotary_dim, hadamard, signs, page_table,
+                         pt_stride, seq_lens, kv_inv, VF16);
+        any = true;
+      }
+      sstart += pgl;
+      if (++kv == hkv) {
+        kv = 0;
+        if (++sq >= n_seq) break;
+        pgl = seq_pages(seq_lens, sq);
+      }
+    }
+    return any;
+  };
+  if (k_new != nullptr && append_tokens(true)) {
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+  }
+
 
   static_assert(!VF16 || (PACKED && NT == 1 && !MQ), "fp16 V: page-softmax kernel of one query token only");
   constexpr int kBB = VF16 ? kBlockBytesF16V : kBlockBytes;   // block bytes
@@ -944,38 +1174,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
   } else if (two_segs) {
     load_q_inputs<kPasses, MQ>(seg0 + 1, hkv, n_q_heads, qc, q, in_dtype, q_positions, rope_cos,
                            rope_sin, rotary_dim, qin2);
-  }
-
-  // ---- the current token of every segment whose last page is in the range
-  // goes into the cache here (only this wavefront reads that page), and its
-  // stores land before that page's loads are issued.  A token whose page is
-  // among the range's first two pages is written before any page load;
-  // the others after the first two pages' loads are on their way, so the
-  // wavefront does not start late.
-  auto append_tokens = [&](bool first_pages) {
-    bool any = false;
-    int sq = seq, kv = kvh0;
-    int64_t sstart = seq_base + (int64_t)kvh0 * pg, pgl = pg;
-    while (sstart < b) {
-      const int64_t last = sstart + pgl - 1;
-      if (pgl > 0 && last >= a && last < b && (last <= a + 1) == first_pages) {
-        append_new_token(sq * hkv + kv, pool, num_pages, hkv, layer, k_new, v_new, in_dtype,
-                         q_positions, rope_cos, rope_sin, rotary_dim, hadamard, signs, page_table,
-                         pt_stride, seq_lens, kv_inv, VF16);
-        any = true;
-      }
-      sstart += pgl;
-      if (++kv == hkv) {
-        kv = 0;
-        if (++sq >= n_seq) break;
-        pgl = seq_pages(seq_lens, sq);
-      }
-    }
-    return any;
-  };
-  if (k_new != nullptr && append_tokens(true)) {
-    __builtin_amdgcn_s_waitcnt(0);
-    asm volatile("" ::: "memory");
   }
 
   const int voff = 16 * lane;
@@ -1346,12 +1544,35 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int dd = tid & 31, j = tid >> 5;  // dim within the chunk, piece group
   const int kvh = hq_idx / group, h = hq_idx % group;
   // work units (pages plus kSegExtra per segment, as the decode kernel
-  // splits them) before this segment and in all
+  // splits them) before this segment and in all: a few sequences summed in
+  // order; more read by the block's threads side by side and summed (one
+  // load per sequence per step took most of the kernel at 64 sequences)
+  __shared__ int64_t red_u[2][8];
   int64_t TU = 0, seq_base = 0;
-  for (int s = 0; s < n_seq; ++s) {
-    const int64_t pg = seq_pages(seq_lens, s) + kSegExtra;
-    if (s == seq) seq_base = TU;
-    TU += pg;
+  if (n_seq <= 16) {
+    for (int s = 0; s < n_seq; ++s) {
+      const int64_t u = seq_pages(seq_lens, s) + kSegExtra;
+      if (s == seq) seq_base = TU;
+      TU += u;
+    }
+  } else {
+    int64_t tu = 0, before = 0;
+    for (int s = tid; s < n_seq; s += 256) {
+      const int64_t u = seq_pages(seq_lens, s) + kSegExtra;
+      tu += u;
+      before += s < seq ? u : 0;
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      tu += __shfl_xor(tu, o, 64);
+      before += __shfl_xor(before, o, 64);
+    }
+    if ((tid & 63) == 0) {
+      red_u[0][tid >> 6] = tu;
+      red_u[1][tid >> 6] = before;
+    }
+    __syncthreads();
+    TU = red_u[0][0] + red_u[0][1] + red_u[0][2] + red_u[0][3];
+    seq_base = red_u[1][0] + red_u[1][1] + red_u[1][2] + red_u[1][3];
   }
   TU *= hkv;
   seq_base *= hkv;

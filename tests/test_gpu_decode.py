@@ -279,3 +279,36 @@ def test_decode_quantizes_current_token_many_segments_one_wave():
     assert torch.equal(held.pool.data, full.pool.data)
     assert np.array_equal(out_fused, out_full)
     assert_attention_close(out_fused, held.oracle(), "many segments")
+
+
+def _many_lens(n_seq):
+    return [int(t) for t in np.random.default_rng(n_seq).integers(1, 300, n_seq)]
+
+
+@pytest.mark.parametrize("n_seq", [64, 65, 200, 256, 257, 300])
+@pytest.mark.parametrize("pages_per_split", [0, 16])
+def test_decode_many_sequences(n_seq, pages_per_split):
+    """More sequences than a wavefront has lanes.  The kernels scan the
+    sequences' page offsets across the wavefront in chunks of 64 sequences,
+    up to 256 (past that they walk the lengths): 64 and 65 sit on the first
+    chunk boundary, 200 spans four chunks, 256 fills them, 257 and 300 take
+    the walk.  Ragged lengths of 1-299 tokens; at 16 units per wavefront a
+    range spans several segments."""
+    c = Case(600 + n_seq, _many_lens(n_seq), 2, 8)
+    assert_attention_close(c.gpu(pages_per_split=pages_per_split), c.oracle(),
+                           f"{n_seq} sequences, pages_per_split {pages_per_split}")
+
+
+@pytest.mark.parametrize("n_seq", [65, 300])
+def test_decode_many_sequences_fused(n_seq):
+    """The same with each sequence's current token quantized by the decode
+    launch: the pool bytes equal the oracle's append of every token, the
+    output equals append + decode."""
+    lens = _many_lens(n_seq)
+    full = Case(700 + n_seq, lens, 2, 8)
+    held = Case(700 + n_seq, lens, 2, 8, hold_last=True)
+    out_full = full.gpu()
+    out_fused = held.gpu(fused=True)
+    assert np.array_equal(held.pool.data.cpu().numpy(), oracle_pool(held)), "pool bytes differ from the oracle"
+    assert np.array_equal(out_fused, out_full), "output differs from append + decode"
+    assert_attention_close(out_fused, held.oracle(), f"fused, {n_seq} sequences")
