@@ -1586,6 +1586,40 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   __shared__ float red_o[8][32];
   __shared__ float red_l[8];
   __shared__ float wts[kChunk];
+  float L = 0.0f, acc = 0.0f;
+  const int64_t np = w1 - w0 + 1;          // pieces of the segment
+  if (np <= 256) {
+    // up to 256 pieces: the thread's accumulator entries (pieces j, j + 8,
+    // ...) are requested first, the pieces' (m, l) once, and the weights
+    // made from those registers: two rounds of loads in flight together
+    float a[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int i = j + 8 * u;
+      a[u] = i < np ? ws_acc[((g + w0 + i) * group + h) * kHeadDim + d0 + dd] : 0.0f;
+    }
+    const int64_t w = w0 + tid;
+    const bool written = tid < np && (w * TU) / W != ((w + 1) * TU) / W;
+    const float2 ml = written ? ws_ml[(g + w) * group + h] : make_float2(-INFINITY, 0.0f);
+    float M = ml.x;
+    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+    if ((tid & 31) == 0) red_m[tid >> 5] = M;
+    __syncthreads();
+    M = red_m[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
+    const float wt = written ? exp2f(ml.x - M) : 0.0f;
+    L = wt * ml.y;
+    if (tid < np) wts[tid] = wt;
+    __syncthreads();
+    // a piece of weight 0 adds nothing; its slot may never have been
+    // written (a wavefront with an empty range), so it is not multiplied
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int i = j + 8 * u;
+      if (i < np && wts[i] != 0.0f) acc += wts[i] * a[u];
+    }
+  } else {
   // ---- running max over all pieces
   float M = -INFINITY;
   for (int64_t w = w0 + tid; w <= w1; w += 256) {
@@ -1602,7 +1636,6 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   // ---- weighted sums, a chunk of pieces at a time: weights 2^(m - M) go to
   // LDS once, then 8 groups stride over the pieces with 16 independent loads
   // in flight per thread
-  float L = 0.0f, acc = 0.0f;
   for (int64_t c0 = w0; c0 <= w1; c0 += kChunk) {
     const int n = (int)((w1 - c0 + 1) < kChunk ? (w1 - c0 + 1) : kChunk);
     __syncthreads();
@@ -1630,6 +1663,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
       for (int u = 0; u < 16; ++u)
         if (i + 8 * u < n && wts[i + 8 * u] != 0.0f) acc += wts[i + 8 * u] * a[u];
     }
+  }
   }
   // L was summed per thread over its pieces; combine across the block
   for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o, 32);
