@@ -1532,6 +1532,73 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
 // of segment g come from waves w_first .. w_last, found with the same flat
 // indexing as the decode kernel; waves with an empty range (more waves than
 // pages) wrote nothing and are skipped.
+// Combine of a segment's pieces, at most 8 * NU of them, by a block of 256
+// threads (thread: column `col` of pieces j, j + 8, ..., j + 8 (NU - 1),
+// j = tid / 32).  Each piece's (m, l) is requested first, then the
+// accumulator entries, so the maximum and the weights are made while those
+// are in flight.  Loads use indices clamped into the segment and the values
+// past it get weight 0 (conditional loads became branches with waits
+// between them).  Adds the thread's share to `acc` and `L`.
+template <int NU>
+__device__ __forceinline__ void reduce_few(const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
+                                           size_t g, int64_t w0, int np, int group, int h, int col, int tid,
+                                           int64_t TU, int64_t W, float* red_m, float* wts, float& acc,
+                                           float& L) {
+  constexpr int NP = 8 * NU;               // pieces covered
+  constexpr int MLP = (NP + 255) / 256;    // (m, l) pairs per thread: pieces tid + 256k
+  const int j = tid >> 5;
+  float2 mlr[MLP];
+  bool written[MLP];
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const int p = tid + 256 * k;
+    const int64_t w = w0 + p;
+    // with at least as many units as wavefronts no range is empty
+    written[k] = p < np && (TU >= W || (w * TU) / W != ((w + 1) * TU) / W);
+    mlr[k] = ws_ml[(g + w0 + min(p, np - 1)) * group + h];
+  }
+  float a[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    a[u] = ws_acc[((g + w0 + min(j + 8 * u, np - 1)) * group + h) * kHeadDim + col];
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) M = written[k] ? fmaxf(M, mlr[k].x) : M;
+  for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+  if ((tid & 31) == 0) red_m[tid >> 5] = M;
+  __syncthreads();
+  M = red_m[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
+  // weights by piece group: piece j + 8u at NU j + u, read back as vectors
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const int p = tid + 256 * k;
+    // (an unwritten slot's l may be anything: it is not multiplied either)
+    const float wt = written[k] ? exp2f(mlr[k].x - M) : 0.0f;
+    L += written[k] ? wt * mlr[k].y : 0.0f;
+    if (p < NP) wts[NU * (p & 7) + (p >> 3)] = wt;
+  }
+  __syncthreads();
+  // a piece of weight 0 adds nothing; its slot may never have been written
+  // (a wavefront with an empty range), so it is not multiplied
+  if constexpr (NU % 4 == 0) {
+    const f4* wj = reinterpret_cast<const f4*>(wts + NU * j);
+#pragma unroll
+    for (int q = 0; q < NU / 4; ++q) {
+      const f4 x = wj[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += x[e] != 0.0f ? x[e] * a[4 * q + e] : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const float x = wts[NU * j + u];
+      acc += x != 0.0f ? x * a[u] : 0.0f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
     const int32_t* __restrict__ seq_lens, int n_seq, int hkv, QCols qc, int n_q_heads, int64_t W,
@@ -1544,17 +1611,37 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int dd = tid & 31, j = tid >> 5;  // dim within the chunk, piece group
   const int kvh = hq_idx / group, h = hq_idx % group;
   // work units (pages plus kSegExtra per segment, as the decode kernel
-  // splits them) before this segment and in all: a few sequences summed in
-  // order; more read by the block's threads side by side and summed (one
-  // load per sequence per step took most of the kernel at 64 sequences)
+  // splits them) before this segment and in all.  Up to 16 sequences: the
+  // lengths through the scalar cache, 8 independent loads per wait (a
+  // dependent load per sequence took a round trip each); more are read by
+  // the block's threads side by side and summed across the block (with
+  // thousands of blocks, scalar loads of every length from every wavefront
+  // queued: 64 sequences, 6.3 against 1.7 us)
   __shared__ int64_t red_u[2][8];
-  int64_t TU = 0, seq_base = 0;
+  int64_t TU = 0, seq_base = 0, pg = 0;
   if (n_seq <= 16) {
-    for (int s = 0; s < n_seq; ++s) {
-      const int64_t u = seq_pages(seq_lens, s) + kSegExtra;
-      if (s == seq) seq_base = TU;
-      TU += u;
+    // at most 16 x (2^25 + 5) units: the sums fit in 32 unsigned bits
+    uint32_t tu = 0, before = 0;
+#pragma unroll
+    for (int g8 = 0; g8 < 2; ++g8) {
+      const int base = 8 * g8;
+      if (base < n_seq) {
+        int v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = seq_lens[min(base + i, n_seq - 1)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int sq = base + i;
+          const int pgi = (v[i] + kPageSize - 1) / kPageSize;
+          const uint32_t u = sq < n_seq ? (uint32_t)(pgi + kSegExtra) : 0u;
+          tu += u;
+          before += sq < seq ? u : 0u;
+          pg = sq == seq ? pgi : pg;
+        }
+      }
     }
+    TU = tu;
+    seq_base = before;
   } else {
     int64_t tu = 0, before = 0;
     for (int s = tid; s < n_seq; s += 256) {
@@ -1573,10 +1660,10 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     __syncthreads();
     TU = red_u[0][0] + red_u[0][1] + red_u[0][2] + red_u[0][3];
     seq_base = red_u[1][0] + red_u[1][1] + red_u[1][2] + red_u[1][3];
+    pg = seq_pages(seq_lens, seq);
   }
   TU *= hkv;
   seq_base *= hkv;
-  const int64_t pg = seq_pages(seq_lens, seq);
   const int64_t S = seq_base + kvh * (pg + kSegExtra), E = S + pg;   // the segment's page units
   const int64_t w0 = wave_of(S, TU, W), w1 = wave_of(E - 1, TU, W);
   const size_t g = (size_t)seq * hkv + kvh;
@@ -1585,45 +1672,21 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   __shared__ float red_m[8];
   __shared__ float red_o[8][32];
   __shared__ float red_l[8];
-  __shared__ float wts[kChunk];
+  __shared__ __attribute__((aligned(16))) float wts[kChunk];
   float L = 0.0f, acc = 0.0f;
   const int64_t np = w1 - w0 + 1;          // pieces of the segment
-  if (np <= 256) {
-    // up to 256 pieces: the thread's accumulator entries (pieces j, j + 8,
-    // ...) are requested first, the pieces' (m, l) once, and the weights
-    // made from those registers: two rounds of loads in flight together
-    float a[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int i = j + 8 * u;
-      a[u] = i < np ? ws_acc[((g + w0 + i) * group + h) * kHeadDim + d0 + dd] : 0.0f;
-    }
-    const int64_t w = w0 + tid;
-    const bool written = tid < np && (w * TU) / W != ((w + 1) * TU) / W;
-    const float2 ml = written ? ws_ml[(g + w) * group + h] : make_float2(-INFINITY, 0.0f);
-    float M = ml.x;
-    for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
-    if ((tid & 31) == 0) red_m[tid >> 5] = M;
-    __syncthreads();
-    M = red_m[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) M = fmaxf(M, red_m[i]);
-    const float wt = written ? exp2f(ml.x - M) : 0.0f;
-    L = wt * ml.y;
-    if (tid < np) wts[tid] = wt;
-    __syncthreads();
-    // a piece of weight 0 adds nothing; its slot may never have been
-    // written (a wavefront with an empty range), so it is not multiplied
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int i = j + 8 * u;
-      if (i < np && wts[i] != 0.0f) acc += wts[i] * a[u];
-    }
+  if (np <= 512) {
+    const int n = (int)np;
+    if (n <= 8) reduce_few<1>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
+    else if (n <= 32) reduce_few<4>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
+    else if (n <= 64) reduce_few<8>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
+    else if (n <= 256) reduce_few<32>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
+    else reduce_few<64>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
   } else {
   // ---- running max over all pieces
   float M = -INFINITY;
   for (int64_t w = w0 + tid; w <= w1; w += 256) {
-    if ((w * TU) / W == ((w + 1) * TU) / W) continue;
+    if (TU < W && (w * TU) / W == ((w + 1) * TU) / W) continue;
     M = fmaxf(M, ws_ml[(g + w) * group + h].x);
   }
   for (int o = 16; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
@@ -1642,7 +1705,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     for (int i = tid; i < n; i += 256) {
       const int64_t w = c0 + i;
       float wt = 0.0f;
-      if ((w * TU) / W != ((w + 1) * TU) / W) {
+      if (TU >= W || (w * TU) / W != ((w + 1) * TU) / W) {
         const float2 ml = ws_ml[(g + w) * group + h];
         wt = exp2f(ml.x - M);
         L += wt * ml.y;
