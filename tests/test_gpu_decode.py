@@ -174,6 +174,22 @@ def test_decode_split_count_invariance():
         assert np.abs(o - outs[0]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
 
 
+def test_decode_reduce_piece_counts():
+    """One 64K-token segment split over 1 to 1024 wavefronts, so its partials
+    take every combine path of the reduce (up to 8, 32, 64, 256 and 512
+    pieces, and the staged one past 512): all match the oracle and each
+    other."""
+    c = Case(21, [65536], 1, 6)
+    ref = c.oracle()
+    outs = []
+    for p in (4096, 128, 40, 20, 8, 3, 2, 1):
+        o = c.gpu(pages_per_split=p)
+        assert_attention_close(o, ref, f"pages_per_split {p}")
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-4 * max(1.0, np.abs(outs[0]).max())
+
+
 def test_decode_ignores_unwritten_workspace():
     """More wavefronts than pages leaves wavefronts with empty ranges inside a
     segment's span; their partial slots are never written.  With the
