@@ -65,6 +65,20 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 __device__ inline h2 bits_h2(uint32_t b) { return __builtin_bit_cast(h2, b); }
 
+// a - (float)h for the f16 h in the low (HI false) or high half of a pair,
+// in one mixed-precision fused multiply-add: the f16 operand converts
+// exactly, so this rounds once, as the conversion and subtraction do
+// (the compiler emits those two instructions for the plain expression)
+template <bool HI>
+__device__ __forceinline__ float sub_f16(float a, h2 h) {
+  float d;
+  if (HI)
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(a));
+  else
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(a));
+  return d;
+}
+
 // 16 bytes at block byte offset voff + soff (voff per lane, soff uniform).
 __device__ __forceinline__ u4 ld16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
@@ -770,7 +784,7 @@ __device__ __forceinline__ void softmax_sw(const f4 (&S)[2], int g4, int c16, in
       p0[2 * s2] = lo[0];
       p0[2 * s2 + 1] = lo[1];
     } else {
-      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
+      lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(sub_f16<false>(pa, hi), sub_f16<true>(pb, hi)));
       p0[2 * s2] = hi[0];
       p0[2 * s2 + 1] = hi[1];
       p1[2 * s2] = lo[0];
@@ -821,7 +835,7 @@ __device__ __forceinline__ bool softmax_fast(const f4 (&S)[NT][2], float c_log2,
         p0[t][2 * s2] = lo[0];
         p0[t][2 * s2 + 1] = lo[1];
       } else {
-        lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(pa - (float)hi[0], pb - (float)hi[1]));
+        lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(sub_f16<false>(pa, hi), sub_f16<true>(pb, hi)));
         p0[t][2 * s2] = hi[0];
         p0[t][2 * s2 + 1] = hi[1];
         p1[t][2 * s2] = lo[0];
