@@ -1689,7 +1689,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   __shared__ __attribute__((aligned(16))) float wts[kChunk];
   float L = 0.0f, acc = 0.0f;
   const int64_t np = w1 - w0 + 1;          // pieces of the segment
-  if (np <= 512) {
+  // (a segment has at least one piece for every length of at least one
+  // token, which the interface requires; the clamped loads need one)
+  if (np >= 1 && np <= 512) {
     const int n = (int)np;
     if (n <= 8) reduce_few<1>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
     else if (n <= 32) reduce_few<4>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
