@@ -207,6 +207,27 @@ def test_decode_ignores_unwritten_workspace():
     assert_attention_close(out.cpu().numpy(), c.oracle(), "NaN-filled workspace")
 
 
+@pytest.mark.parametrize("pages_per_split", [1, 2, 4, 8, 32, 64, 512])
+def test_decode_unwritten_slots_every_combine_path(pages_per_split):
+    """max_seq_len far past the actual lengths gives far more wavefronts than
+    work units, so most partial slots inside every segment's span are never
+    written.  With the workspace filled with NaN bytes, every combine path of
+    the reduce (chosen by the pieces per segment: from 2 to about 1200 here,
+    the staged path past 512 included) must give those slots no weight."""
+    c = Case(22, [700, 3, 200], 2, 12)
+    max_len = 70000
+    table = np.zeros((len(c.lens), (max_len + 63) // 64), np.int32)
+    table[:, :c.table.shape[1]] = c.table
+    need = c.kv.nvfp4kv_decode_workspace_bytes(c.pool, len(c.lens), c.hq, max_len, pages_per_split)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = c.kv.nvfp4kv_decode_attn(
+        c.pool, 0, c.q.cuda(), torch.from_numpy(c.q_pos).cuda(), torch.from_numpy(table).cuda(),
+        torch.tensor(c.lens, dtype=torch.int32).cuda(), max_len, 1 / np.sqrt(128), workspace=ws,
+        rope_cos=c.rc, rope_sin=c.rs, pages_per_split=pages_per_split)
+    torch.cuda.synchronize()
+    assert_attention_close(out.cpu().numpy(), c.oracle(), f"NaN-filled workspace, pages_per_split {pages_per_split}")
+
+
 def test_decode_sm_scale_zero_and_large():
     c = Case(10, [900], 2, 4)
     assert_attention_close(c.gpu(sm_scale=0.0), c.oracle(sm_scale=0.0), "sm_scale 0")
