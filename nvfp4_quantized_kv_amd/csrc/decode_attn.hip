@@ -1546,17 +1546,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT > 1 ? 1 :
 // of segment g come from waves w_first .. w_last, found with the same flat
 // indexing as the decode kernel; waves with an empty range (more waves than
 // pages) wrote nothing and are skipped.
+// DPT consecutive output dims of a piece's accumulator row (16-byte loads
+// for 4).
+template <int DPT>
+__device__ __forceinline__ void load_dims(const float* __restrict__ p, float (&x)[DPT]) {
+  if constexpr (DPT == 4) {
+    const f4 v = *reinterpret_cast<const f4*>(p);
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+  } else {
+    x[0] = *p;
+  }
+}
+
 // Combine of a segment's pieces, at most 8 * NU of them, by a block of 256
-// threads (thread: column `col` of pieces j, j + 8, ..., j + 8 (NU - 1),
-// j = tid / 32).  Each piece's (m, l) is requested first, then the
-// accumulator entries, so the maximum and the weights are made while those
-// are in flight.  Loads use indices clamped into the segment and the values
-// past it get weight 0 (conditional loads became branches with waits
-// between them).  Adds the thread's share to `acc` and `L`.
-template <int NU>
+// threads (thread: output dims col .. col + DPT - 1 of pieces j, j + 8, ...,
+// j + 8 (NU - 1), j = tid / 32).  Each piece's (m, l) is requested first,
+// then the accumulator entries, so the maximum and the weights are made
+// while those are in flight.  Loads use indices clamped into the segment and
+// the values past it get weight 0 (conditional loads became branches with
+// waits between them).  Adds the thread's share to `acc` and `L`.
+template <int NU, int DPT>
 __device__ __forceinline__ void reduce_few(const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
                                            size_t g, int64_t w0, int np, int group, int h, int col, int tid,
-                                           int64_t TU, int64_t W, float* red_m, float* wts, float& acc,
+                                           int64_t TU, int64_t W, float* red_m, float* wts, float (&acc)[DPT],
                                            float& L) {
   constexpr int NP = 8 * NU;               // pieces covered
   constexpr int MLP = (NP + 255) / 256;    // (m, l) pairs per thread: pieces tid + 256k
@@ -1571,10 +1583,10 @@ __device__ __forceinline__ void reduce_few(const float* __restrict__ ws_acc, con
     written[k] = p < np && (TU >= W || (w * TU) / W != ((w + 1) * TU) / W);
     mlr[k] = ws_ml[(g + w0 + min(p, np - 1)) * group + h];
   }
-  float a[NU];
+  float a[NU][DPT];
 #pragma unroll
   for (int u = 0; u < NU; ++u)
-    a[u] = ws_acc[((g + w0 + min(j + 8 * u, np - 1)) * group + h) * kHeadDim + col];
+    load_dims<DPT>(ws_acc + ((g + w0 + min(j + 8 * u, np - 1)) * group + h) * kHeadDim + col, a[u]);
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < MLP; ++k) M = written[k] ? fmaxf(M, mlr[k].x) : M;
@@ -1602,17 +1614,24 @@ __device__ __forceinline__ void reduce_few(const float* __restrict__ ws_acc, con
     for (int q = 0; q < NU / 4; ++q) {
       const f4 x = wj[q];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc += x[e] != 0.0f ? x[e] * a[4 * q + e] : 0.0f;
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int d = 0; d < DPT; ++d) acc[d] += x[e] != 0.0f ? x[e] * a[4 * q + e][d] : 0.0f;
     }
   } else {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const float x = wts[NU * j + u];
-      acc += x != 0.0f ? x * a[u] : 0.0f;
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) acc[d] += x != 0.0f ? x * a[u][d] : 0.0f;
     }
   }
 }
 
+// DPT output dims per thread: 1 (blocks of 32 dims, four per column) or 4
+// (one block per column, 16-byte loads: a quarter of the blocks and of the
+// load instructions, for launches with many columns).
+template <int DPT>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float* __restrict__ ws_acc, const float2* __restrict__ ws_ml,
     const int32_t* __restrict__ seq_lens, int n_seq, int hkv, QCols qc, int n_q_heads, int64_t W,
@@ -1620,7 +1639,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int group = qc.group;
   const int hq_idx = (int)blockIdx.x;     // column over all kv heads: kvh * group + c
   const int seq = (int)blockIdx.y;
-  const int d0 = 32 * (int)blockIdx.z;    // first output dim of this block
+  const int d0 = 32 * DPT * (int)blockIdx.z;   // first output dim of this block
   const int tid = (int)threadIdx.x;
   const int dd = tid & 31, j = tid >> 5;  // dim within the chunk, piece group
   const int kvh = hq_idx / group, h = hq_idx % group;
@@ -1684,20 +1703,25 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 
   constexpr int kChunk = 1024;             // pieces whose weights are staged at once
   __shared__ float red_m[8];
-  __shared__ float red_o[8][32];
+  __shared__ __attribute__((aligned(16))) float red_o[8][32 * DPT];
   __shared__ float red_l[8];
   __shared__ __attribute__((aligned(16))) float wts[kChunk];
-  float L = 0.0f, acc = 0.0f;
+  float L = 0.0f, acc[DPT];
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) acc[d] = 0.0f;
+  const int col = d0 + DPT * dd;           // the thread's first output dim
   const int64_t np = w1 - w0 + 1;          // pieces of the segment
   // (a segment has at least one piece for every length of at least one
   // token, which the interface requires; the clamped loads need one)
-  if (np >= 1 && np <= 512) {
+  // (up to 512 pieces with one dim per thread, 256 with four: the
+  // accumulator entries held at once)
+  if (np >= 1 && np <= (DPT == 1 ? 512 : 256)) {
     const int n = (int)np;
-    if (n <= 8) reduce_few<1>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
-    else if (n <= 32) reduce_few<4>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
-    else if (n <= 64) reduce_few<8>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
-    else if (n <= 256) reduce_few<32>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
-    else reduce_few<64>(ws_acc, ws_ml, g, w0, n, group, h, d0 + dd, tid, TU, W, red_m, wts, acc, L);
+    if (n <= 8) reduce_few<1, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    else if (n <= 32) reduce_few<4, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    else if (n <= 64) reduce_few<8, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    else if (DPT == 4 || n <= 256) reduce_few<32, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    else reduce_few<DPT == 1 ? 64 : 32, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
   } else {
   // ---- running max over all pieces
   float M = -INFINITY;
@@ -1730,36 +1754,45 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     }
     __syncthreads();
     for (int i = j; i < n; i += 128) {
-      float a[16];
+      float a[16][DPT];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int iu = i + 8 * u < n ? i + 8 * u : i;
-        a[u] = ws_acc[((g + c0 + iu) * group + h) * kHeadDim + d0 + dd];
+        load_dims<DPT>(ws_acc + ((g + c0 + iu) * group + h) * kHeadDim + col, a[u]);
       }
       // a piece of weight 0 adds nothing; its slot may never have been
       // written (a wavefront with an empty range), so it is not multiplied
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (i + 8 * u < n && wts[i + 8 * u] != 0.0f) acc += wts[i + 8 * u] * a[u];
+        if (i + 8 * u < n && wts[i + 8 * u] != 0.0f)
+#pragma unroll
+          for (int d = 0; d < DPT; ++d) acc[d] += wts[i + 8 * u] * a[u][d];
     }
   }
   }
   // L was summed per thread over its pieces; combine across the block
   for (int o = 16; o > 0; o >>= 1) L += __shfl_xor(L, o, 32);
-  red_o[j][dd] = acc;
+#pragma unroll
+  for (int d = 0; d < DPT; ++d) red_o[j][DPT * dd + d] = acc[d];
   if (dd == 0) red_l[j] = L;
   __syncthreads();
   if (j == 0) {
-    float o = 0.0f, l = 0.0f;
+    float o[DPT], l = 0.0f;
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) o[d] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      o += red_o[i][dd];
+#pragma unroll
+      for (int d = 0; d < DPT; ++d) o[d] += red_o[i][DPT * dd + d];
       l += red_l[i];
     }
     // column h of kv head kvh: head h % heads of query token qtok0 + h / heads
     const int tok = qc.qtok0 + h / qc.heads;
-    out[(((size_t)seq * qc.n_qtok + tok) * n_q_heads + (size_t)kvh * qc.heads + h % qc.heads) * kHeadDim +
-        d0 + dd] = o * v_scale / l;   // V's global scale: stored V values are V / v_scale
+    float* dst = out + (((size_t)seq * qc.n_qtok + tok) * n_q_heads + (size_t)kvh * qc.heads + h % qc.heads) *
+                           kHeadDim + col;
+    // V's global scale: stored V values are V / v_scale
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) dst[d] = o[d] * v_scale / l;
   }
 }
 
@@ -1809,9 +1842,17 @@ hipError_t launch_decode_reduce(int hkv, int n_seq, int n_q_heads, const int32_t
   const float2* ws_ml = reinterpret_cast<const float2*>(reinterpret_cast<const uint8_t*>(workspace) +
                                                         ws_ml_offset(n_seq, hkv, plan));
   const QCols qc{plan.group, qt.heads, qt.n_qtok, qt.qtok0};
-  hipLaunchKernelGGL(decode_reduce_kernel, dim3(hkv * plan.group, n_seq, kHeadDim / 32), dim3(256), 0,
-                     stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
-                     (int64_t)plan.n_waves, v_scale, out);
+  // four blocks of 32 dims per column; with 1024 such blocks or more, one
+  // block of 4 dims per thread per column instead
+  const int64_t blocks = (int64_t)hkv * plan.group * n_seq * (kHeadDim / 32);
+  if (blocks >= 1024)
+    hipLaunchKernelGGL(decode_reduce_kernel<4>, dim3(hkv * plan.group, n_seq, kHeadDim / 128), dim3(256), 0,
+                       stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
+                       (int64_t)plan.n_waves, v_scale, out);
+  else
+    hipLaunchKernelGGL(decode_reduce_kernel<1>, dim3(hkv * plan.group, n_seq, kHeadDim / 32), dim3(256), 0,
+                       stream, ws_acc, ws_ml, seq_lens, n_seq, hkv, qc, n_q_heads,
+                       (int64_t)plan.n_waves, v_scale, out);
   return hipGetLastError();
 }
 

@@ -207,14 +207,17 @@ def test_decode_ignores_unwritten_workspace():
     assert_attention_close(out.cpu().numpy(), c.oracle(), "NaN-filled workspace")
 
 
+@pytest.mark.parametrize("reps", [1, 8])
 @pytest.mark.parametrize("pages_per_split", [1, 2, 4, 8, 32, 64, 512])
-def test_decode_unwritten_slots_every_combine_path(pages_per_split):
+def test_decode_unwritten_slots_every_combine_path(pages_per_split, reps):
     """max_seq_len far past the actual lengths gives far more wavefronts than
     work units, so most partial slots inside every segment's span are never
     written.  With the workspace filled with NaN bytes, every combine path of
-    the reduce (chosen by the pieces per segment: from 2 to about 1200 here,
-    the staged path past 512 included) must give those slots no weight."""
-    c = Case(22, [700, 3, 200], 2, 12)
+    the reduce (chosen by the pieces per segment: from 2 to about 1060 here,
+    the staged path included) must give those slots no weight: with 3
+    sequences in its one-dim-per-thread form, with 24 in its four-dim form
+    (a launch of 1152 column blocks of 32 dims)."""
+    c = Case(22, [700, 3, 200] * reps, 2, 12)
     max_len = 70000
     table = np.zeros((len(c.lens), (max_len + 63) // 64), np.int32)
     table[:, :c.table.shape[1]] = c.table
