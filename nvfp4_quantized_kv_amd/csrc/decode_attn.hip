@@ -1711,17 +1711,23 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   for (int d = 0; d < DPT; ++d) acc[d] = 0.0f;
   const int col = d0 + DPT * dd;           // the thread's first output dim
   const int64_t np = w1 - w0 + 1;          // pieces of the segment
-  // (a segment has at least one piece for every length of at least one
-  // token, which the interface requires; the clamped loads need one)
-  // (up to 512 pieces with one dim per thread, 256 with four: the
-  // accumulator entries held at once)
+  // One round of loads up to 512 pieces with one dim per thread, 256 with
+  // four (the accumulator entries held at once); past that, or for an empty
+  // segment (no length of at least one token, which the interface requires,
+  // gives one; the clamped loads need a piece), the staged path.
   if (np >= 1 && np <= (DPT == 1 ? 512 : 256)) {
     const int n = (int)np;
-    if (n <= 8) reduce_few<1, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
-    else if (n <= 32) reduce_few<4, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
-    else if (n <= 64) reduce_few<8, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
-    else if (DPT == 4 || n <= 256) reduce_few<32, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
-    else reduce_few<DPT == 1 ? 64 : 32, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    if (n <= 8) {
+      reduce_few<1, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    } else if (n <= 32) {
+      reduce_few<4, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    } else if (n <= 64) {
+      reduce_few<8, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    } else if (n <= 256) {
+      reduce_few<32, DPT>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    } else {
+      if constexpr (DPT == 1) reduce_few<64, 1>(ws_acc, ws_ml, g, w0, n, group, h, col, tid, TU, W, red_m, wts, acc, L);
+    }
   } else {
   // ---- running max over all pieces
   float M = -INFINITY;
