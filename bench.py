@@ -25,7 +25,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
-ALGO_BYTES_PER_TOKEN_HEAD = 144
 
 
 def log(msg: str) -> None:
@@ -54,6 +53,9 @@ def parse():
                     help="time host spill and restore of the longest sequence's pages instead")
     ap.add_argument("--multi", type=int, default=0,
                     help="time multi-query decode instead: this many new query tokens per sequence")
+    ap.add_argument("--v-format", type=int, default=0, choices=[0, 1],
+                    help="1: time the decode step on a pool that keeps V in fp16 (the upstream "
+                         "storage, 328 B per token per kv head) instead of NVFP4")
     return ap.parse_args()
 
 
@@ -140,7 +142,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(step, wl, torch):
+def cpu_baseline(step, wl, torch, v_format=0):
     """Time the CPU oracle on a bounded sample of the same step: layer 0 of
     the workload, i.e. the append of every sequence's new token and decode
     attention of every sequence and query head over the layer's cache."""
@@ -161,11 +163,12 @@ def cpu_baseline(step, wl, torch):
     slots = step.new_slots.cpu().numpy()
     pos = np.array(wl.cached, np.int32)
     t0 = time.perf_counter()
-    oracle.append(pool0, step.pool.num_pages, wl.hkv, wl.rotary_dim, wl.hadamard, 0, k, v, slots, pos, oc, os_)
+    oracle.append(pool0, step.pool.num_pages, wl.hkv, wl.rotary_dim, wl.hadamard, 0, k, v, slots, pos, oc, os_,
+                  v_format=v_format)
     ref = oracle.decode_attention(pool0, step.pool.num_pages, wl.hkv, 0, wl.rotary_dim, wl.hadamard, q,
-                                  pos, step.table_np, wl.seq_lens, W.sm_scale(), oc, os_)
+                                  pos, step.table_np, wl.seq_lens, W.sm_scale(), oc, os_, v_format=v_format)
     sec = time.perf_counter() - t0
-    nbytes = ALGO_BYTES_PER_TOKEN_HEAD * wl.hkv * sum(wl.seq_lens)
+    nbytes = wl.decode_bytes_per_layer(v_format)
     # the same layer on the GPU (new token quantized by the decode kernel), for a parity figure
     out = step.decode(0, fused=True).clone()
     torch.cuda.synchronize()
@@ -197,6 +200,9 @@ def main():
         sys.exit(1)
     if args.quality:
         return bench_quality(args, torch, kv, W, DecodeStep)
+    if args.v_format and (args.multi or args.spill or args.append):
+        log("--v-format applies to the decode step only")
+        sys.exit(2)
     wl = W.config(args.workload)
     if args.layers:
         wl.layers = min(args.layers, wl.layers)
@@ -205,7 +211,7 @@ def main():
     ceiling = None if args.no_ceiling else copy_ceiling_gbps(torch)
     if ceiling:
         log(f"plain copy ceiling {ceiling:.0f} GB/s")
-    step = DecodeStep(wl, pages_per_split=args.pages_per_split)
+    step = DecodeStep(wl, pages_per_split=args.pages_per_split, v_format=args.v_format)
     t0 = time.perf_counter()
     for layer in range(wl.layers):
         step.fill([layer])
@@ -250,13 +256,15 @@ def main():
     avg_kernel_ms = sum(kern_ms) / len(kern_ms)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, decode kernel avg {avg_kernel_ms * 1e3:.1f} us")
 
-    bytes_per_layer = wl.decode_bytes_per_layer()
+    bytes_per_layer = wl.decode_bytes_per_layer(args.v_format)
     bytes_per_step = bytes_per_layer * wl.layers
     value = bytes_per_step / (ms_per_step * 1e-3) / 1e9
     tok_heads = sum(wl.seq_lens) * wl.hkv * wl.layers
     achieved = bytes_per_layer / (avg_kernel_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles("decode_attn_splitk", wl.name)
-    read_ceiling = None if args.no_ceiling else stream_read_ceiling_gbps(step, wl, torch, kv)
+    # (the counters and the read probe cover the NVFP4 pool)
+    traffic = traffic_from_profiles("decode_attn_splitk", wl.name) if args.v_format == 0 else None
+    read_ceiling = (None if args.no_ceiling or args.v_format
+                    else stream_read_ceiling_gbps(step, wl, torch, kv))
     if read_ceiling:
         log(f"stream-read ceiling of the same blocks {read_ceiling:.0f} GB/s")
 
@@ -264,7 +272,7 @@ def main():
     parity_err = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on layer 0")
-        cpu, parity_err = cpu_baseline(step, wl, torch)
+        cpu, parity_err = cpu_baseline(step, wl, torch, args.v_format)
         cpu.pop("seconds", None)
         log(f"oracle {cpu['value']:.3f} GB/s on {cpu['cores']} threads; max |gpu - oracle| = {parity_err:.2e}")
 
@@ -284,18 +292,20 @@ def main():
         "config": {
             "workload": f"{wl.name}: {wl.n_seq} sequences at {'/'.join(str(t) for t in wl.cached)} cached "
                         f"tokens + 1 appended, {wl.layers} layers, {wl.hq} query / {wl.hkv} KV heads, "
-                        f"head_dim 128, 64-token pages, randomly permuted page table",
+                        f"head_dim 128, 64-token pages, randomly permuted page table"
+                        + (", V kept in fp16 (328 B per token per kv head)" if args.v_format else ""),
             "n_seq": wl.n_seq, "layers": wl.layers, "q_heads": wl.hq, "kv_heads": wl.hkv,
             "rotary_dim": wl.rotary_dim, "hadamard": wl.hadamard, "input_dtype": wl.dtype,
             "step": "per layer: decode_attn_splitk (new token quantized in place) + decode_reduce",
             "pages_per_split": args.pages_per_split or "auto",
+            "v_format": args.v_format,
         },
         "pct_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "kv_token_heads_per_s": round(tok_heads / (ms_per_step * 1e-3), 1),
         "bytes_per_step": bytes_per_step,
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_attn_splitk_kernel",
+            "kernel": "decode_attn_splitk_kernel" + (" (fp16 V)" if args.v_format else ""),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -70,9 +70,11 @@ class Workload:
     def torch_dtype(self):
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
 
-    def decode_bytes_per_layer(self) -> int:
-        """Algorithmic bytes one decode pass reads per layer: 144 per token per kv head."""
-        return 144 * self.hkv * sum(self.seq_lens)
+    def decode_bytes_per_layer(self, v_format: int = 0) -> int:
+        """Algorithmic bytes one decode pass reads per layer: 144 per token per
+        kv head, or 328 when the pool keeps V in fp16 (72 B of NVFP4 K and
+        256 B of V)."""
+        return (144 if v_format == 0 else 328) * self.hkv * sum(self.seq_lens)
 
 
 def _c4_lengths(seed: int) -> list:
